@@ -1,0 +1,201 @@
+/*
+ * moebal.h — C ABI of libmoebal: per-invocation hot-expert replication and
+ * token dispatch/combine for expert-parallel MoE layers on AMD MI355X
+ * (gfx950).
+ *
+ * One MoE layer call goes through three asynchronous steps on one HIP stream:
+ *
+ *   mb_plan      count routed pairs, replicate the heaviest experts of the
+ *                busiest ranks into free replica slots until every rank is at
+ *                or below the water level T, assign pairs to replicas
+ *                local-first, and lay out fixed-shape per-rank regions
+ *                (cu_seqlens, a dispatch row per pair, the token of each row);
+ *   mb_dispatch  copy every token row to its K dispatch rows;
+ *   mb_combine   weighted gather-reduce of the K expert-output rows of each
+ *                token back into token order.
+ *
+ * The P logical ranks of the expert-parallel group are partitions of one
+ * GPU's memory: rank r owns rows [r*cap, (r+1)*cap) of every [P*cap, ...]
+ * buffer.
+ *
+ * Sources (pages, by title and section):
+ *  [ISER]   "ISER-MoE: Dynamic In-Switch Replication of Hot Experts for Load
+ *           Balancing in Expert-Parallel", Methodology, HALO-Q Scheduler
+ *           (Objectives 1-2, stages 1-3 and 5); Background (imbalance ratio).
+ *  [Zepp]   Zepp summary (picx.dev/p/sh48ti), §4.1 (R replica slots per GPU;
+ *           eq. (1) locality-preferred routing).
+ *  [MoonEP] "MoonEP: Planner-Enforced S×K Token Balance and Zero-Copy Buffers
+ *           to Fix MoE Skew", "What MoonEP enforces and how" (S*K per rank,
+ *           planner-made cu_seqlens, fixed-shape expert-grouped buffers,
+ *           no host synchronisation) and "Implementation details"
+ *           (home experts then prefetch slots in one numbering).
+ *
+ * Conventions
+ *  - Every buffer is owned by the caller and lives in device memory unless
+ *    stated otherwise. The library never allocates or frees memory and keeps
+ *    no state between calls; all calls except mb_plan_status only enqueue
+ *    work on `stream` and return without waiting. Calls on different streams
+ *    with disjoint buffers may run concurrently.
+ *  - All integers are int32, all arrays row-major and densely packed.
+ *  - Host-detectable errors (bad sizes, null pointers, misaligned rows, a
+ *    workspace that is too small) return a negative MB_ERR_* code and enqueue
+ *    nothing. MB_ERR_HIP means a HIP launch failed.
+ *  - Data-dependent problems are reported by mb_plan in status[0] on the
+ *    device (MB_ST_* bits). mb_dispatch and mb_combine read that word on the
+ *    device and do nothing when a fatal bit (MB_ST_FATAL) is set, so a bad
+ *    plan never writes out of bounds. When a fatal bit is set, the plan's
+ *    pos and row_src contents are unspecified.
+ *
+ * Limits: 1 <= P <= 64, E % P == 0, E <= 2048, 1 <= K <= min(E, 32),
+ * 0 <= R <= 64, N % P == 0, N*K < 2^31, P*cap < 2^31, row bytes a multiple
+ * of 16; fp8 rows need H % 128 == 0.
+ */
+#ifndef MOEBAL_H
+#define MOEBAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MB_VERSION 1
+
+/* Element types of rows. */
+enum mb_dtype {
+  MB_F32 = 0,       /* IEEE binary32 */
+  MB_BF16 = 1,      /* bfloat16 */
+  MB_FP8_E4M3 = 2   /* OCP fp8 e4m3fn, one fp32 scale per 128 elements */
+};
+
+/* Return codes. */
+enum mb_error {
+  MB_OK = 0,
+  MB_ERR_INVALID_ARG = -1, /* sizes outside the limits, null pointer, ... */
+  MB_ERR_WORKSPACE = -2,   /* ws_bytes < mb_plan_workspace_bytes(dims) */
+  MB_ERR_HIP = -3          /* a HIP runtime call failed */
+};
+
+/* status[0] bits written by mb_plan. */
+enum mb_status_flag {
+  MB_ST_BAD_ID = 1,     /* an id outside [0, E) (fatal) */
+  MB_ST_DUP_ID = 2,     /* a token lists one expert twice (fatal) */
+  MB_ST_UNBALANCED = 4, /* placement stopped with a rank above T (not fatal) */
+  MB_ST_CAPACITY = 8    /* a rank needs more than cap rows (fatal) */
+};
+#define MB_ST_FATAL (MB_ST_BAD_ID | MB_ST_DUP_ID | MB_ST_CAPACITY)
+
+/* Problem sizes of one MoE layer call. */
+typedef struct mb_dims {
+  int32_t n_tokens;       /* N tokens; token t originates on rank t / (N/P) */
+  int32_t top_k;          /* K experts per token, distinct within a token */
+  int32_t n_experts;      /* E experts; expert e is homed on rank e / (E/P) */
+  int32_t n_ranks;        /* P logical ranks */
+  int32_t slots_per_rank; /* R replica slots per rank */
+  int32_t hidden;         /* H elements per row */
+  int32_t cap;            /* rows per rank region; S*K = the water level T */
+  int32_t dtype_in;       /* token rows x and dispatch buffer (mb_dtype) */
+  int32_t dtype_out;      /* expert outputs and combined rows: F32 or BF16 */
+} mb_dims;
+
+/*
+ * Caller-owned device outputs of mb_plan (Eh = E/P, NS = Eh + R):
+ *   counts[P*E]         d[s][e] = pairs from source rank s to expert e
+ *   load_pre[P]         L_r = pairs whose expert is homed on r
+ *   load_post[P]        rows rank r serves after planning
+ *   rep_expert[P*R]     expert held by replica slot j of rank r, -1 if empty
+ *   slot_quota[P*NS]    rows of local slot i of rank r: i < Eh is home expert
+ *                       r*Eh + i, i >= Eh is replica slot i - Eh
+ *   cu_seqlens[P*(NS+1)] per-rank running row offsets of the local slots,
+ *                       relative to the rank's region (cu[r][0] = 0)
+ *   pos[N*K]            dispatch row of pair (t, k), in [0, P*cap)
+ *   row_src[P*cap]      token of each dispatch row, -1 for padding rows
+ *   status[4]           {flags (mb_status_flag), T, max_r load_post, moves}
+ */
+typedef struct mb_plan_bufs {
+  int32_t* counts;
+  int32_t* load_pre;
+  int32_t* load_post;
+  int32_t* rep_expert;
+  int32_t* slot_quota;
+  int32_t* cu_seqlens;
+  int32_t* pos;
+  int32_t* row_src;
+  int32_t* status;
+} mb_plan_bufs;
+
+/* Library version (MB_VERSION). */
+int mb_version(void);
+
+/* Short description of an mb_error code or of one mb_status_flag bit
+ * (pass the flag as a positive value). Never NULL; static storage. */
+const char* mb_strerror(int code);
+
+/* Bytes of device workspace mb_plan needs for these sizes; 0 for sizes
+ * outside the limits. Pure host function. */
+size_t mb_plan_workspace_bytes(const mb_dims* dims);
+
+/*
+ * Plan one MoE layer call [ISER HALO-Q stages 1-3, 5; Zepp §4.1; MoonEP].
+ *  ids_dev   [N*K] int32 expert ids, device.
+ *  ws_dev    device workspace of at least mb_plan_workspace_bytes(dims)
+ *            bytes, 16-byte aligned; contents need no initialisation and are
+ *            scratch after the call.
+ *  out       device pointers of the outputs (struct itself is host memory,
+ *            read during the call only).
+ * The greedy: while the busiest rank (lowest index on ties) is above
+ * T = ceil(N*K/P), take its home expert with the largest remaining home
+ * quota (lowest id on ties) that has an eligible destination: a rank with a
+ * free replica slot, load below T, not yet holding that expert; the least
+ * loaded such rank (lowest index on ties) gets a replica in its lowest free
+ * slot and min(T - its load, remaining home quota) pairs. Placement stops
+ * when every rank is at or below T, or with MB_ST_UNBALANCED when the
+ * busiest rank has no expert with a destination. Pairs are then assigned in
+ * (t, k) order: to the source rank when it holds the expert and has quota
+ * left, otherwise to the lowest-index holder with quota left; rows of a
+ * slot are in ascending token order.
+ * Returns MB_OK once the work is enqueued.
+ */
+int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws_bytes,
+            const mb_plan_bufs* out, hipStream_t stream);
+
+/*
+ * Dispatch [MoonEP, "What MoonEP enforces and how": tokens written into
+ * fixed-shape expert-grouped buffers]: buf[pos[t][k]] = x[t] for every pair.
+ *  x_dev          [N, H] rows of dtype_in.
+ *  x_scale_dev    [N, H/128] fp32 scales for MB_FP8_E4M3 rows, else NULL.
+ *  buf_dev        [P*cap, H] rows of dtype_in; padding rows are not written.
+ *  buf_scale_dev  [P*cap, H/128] fp32 for MB_FP8_E4M3, else NULL.
+ * Reads plan->pos and plan->status. Row pointers must be 16-byte aligned.
+ */
+int mb_dispatch(const mb_dims* dims, const mb_plan_bufs* plan, const void* x_dev,
+                const float* x_scale_dev, void* buf_dev, float* buf_scale_dev,
+                hipStream_t stream);
+
+/*
+ * Combine [Zepp §4.2 merge, combine side; MoonEP fixed buffers]:
+ *   y[t][i] = sum_{k=0..K-1} w[t][k] * y_exp[pos[t][k]][i]
+ * accumulated in fp32 in k order, stored as dtype_out (bf16: round to
+ * nearest even).
+ *  y_exp_dev  [P*cap, H] expert outputs of dtype_out (the dispatch layout).
+ *  w_dev      [N*K] fp32 gate weights.
+ *  y_dev      [N, H] of dtype_out.
+ * Reads plan->pos and plan->status. Row pointers must be 16-byte aligned.
+ */
+int mb_combine(const mb_dims* dims, const mb_plan_bufs* plan, const void* y_exp_dev,
+               const float* w_dev, void* y_dev, hipStream_t stream);
+
+/*
+ * Copy status[4] to host_status (host memory) after the work enqueued on
+ * `stream` so far has finished. The only call that synchronises.
+ */
+int mb_plan_status(const mb_plan_bufs* plan, hipStream_t stream, int32_t host_status[4]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEBAL_H */

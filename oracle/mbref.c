@@ -1,0 +1,381 @@
+/*
+ * mbref.c — CPU oracle for per-invocation hot-expert replication and token
+ * dispatch/combine.
+ *
+ * TEST INFRASTRUCTURE: the reference the GPU library is checked against.
+ * Single threaded, plain loops, no blocking or fusion; built with
+ * -ffp-contract=off. It shares no code with the GPU path.
+ *
+ * Sources (pages, by title and section):
+ *  [ISER]   "ISER-MoE: Dynamic In-Switch Replication of Hot Experts for Load
+ *           Balancing in Expert-Parallel" — Methodology, HALO-Q Scheduler:
+ *           Objective 1 (water level T), Objective 2 (locality), stage 1
+ *           (count exchange), stage 2 (busiest rank's heaviest home expert
+ *           placed where a slot is free), stage 3 (smallest free helper
+ *           index), stage 5 (local-first rewrite of surplus routes onto the
+ *           hosts' spare quotas); Background (rank imbalance ratio); E1 table
+ *           (excess load removed).
+ *  [Zepp]   Zepp summary (picx.dev/p/sh48ti) — §4.1: R replica slots per
+ *           GPU given greedily to the experts of highest demand; eq. (1):
+ *           locality-preferred routing with demand d_i^e per source GPU.
+ *  [MoonEP] "MoonEP: Planner-Enforced S×K Token Balance and Zero-Copy
+ *           Buffers to Fix MoE Skew" — "What MoonEP enforces and how": every
+ *           rank receives S*K tokens into fixed-shape expert-grouped buffers
+ *           indexed by planner-made cu_seqlens; "Variables and core terms":
+ *           maxvio; "Implementation details": home experts, then prefetch
+ *           rows, in one [E+B, H, H'] numbering.
+ *
+ * Readings taken where the pages leave a step open (each one is also listed
+ * with its reason in the design notes of the repository):
+ *  - token t originates on rank t / S; expert e is homed on rank e / Eh;
+ *  - L_r counts (token, expert) pairs whose expert is homed on r, so
+ *    T = ceil(N*K / P) = S*K;
+ *  - ties: busiest rank -> lowest index; heaviest expert -> largest remaining
+ *    home quota, then lowest id; destination -> least loaded, then lowest
+ *    index; replica slot -> lowest free index;
+ *  - a move gives the destination min(T - load[dst], remaining home quota)
+ *    pairs (it fills the host's spare quota); MBREF_MOVE_EXCESS_ONLY also
+ *    caps it at the busiest rank's excess, for comparison only;
+ *  - if the busiest rank's heaviest expert has no eligible destination its
+ *    next heaviest is tried; if none has one, placement stops UNBALANCED;
+ *  - surplus pairs go to hosts in ascending rank order; rows inside a slot
+ *    are in ascending token order; local slots are numbered home experts
+ *    first (by id), then replica slots;
+ *  - a rank needing more than cap rows sets CAPACITY and nothing is laid out.
+ */
+#include "mbref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+int mbref_version(void) { return 1; }
+
+static int64_t elt_bytes(int32_t dtype) {
+  switch (dtype) {
+    case MBREF_F32: return 4;
+    case MBREF_BF16: return 2;
+    case MBREF_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+/* O0 — sizes the method is defined for. */
+static int valid_dims(const mbref_dims* d) {
+  if (d->n_ranks < 1 || d->n_tokens < 0 || d->n_tokens % d->n_ranks) return 0;
+  if (d->n_experts < 1 || d->n_experts % d->n_ranks) return 0;
+  if (d->top_k < 1 || d->top_k > d->n_experts) return 0;
+  if (d->slots_per_rank < 0 || d->cap < 1 || d->hidden < 1) return 0;
+  if (!elt_bytes(d->dtype_in)) return 0;
+  if (d->dtype_out != MBREF_F32 && d->dtype_out != MBREF_BF16) return 0;
+  if (d->dtype_in == MBREF_FP8_E4M3 && d->hidden % 128) return 0;
+  if ((int64_t)d->n_tokens * d->top_k > 2147483647LL) return 0;
+  if ((int64_t)d->n_ranks * d->cap > 2147483647LL) return 0;
+  return 1;
+}
+
+int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
+               mbref_plan_out* o, mbref_report* rep) {
+  if (!dm || !o || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
+  if (move_rule != MBREF_MOVE_FILL_HOST && move_rule != MBREF_MOVE_EXCESS_ONLY)
+    return MBREF_ERR_INVALID_ARG;
+  const int64_t N = dm->n_tokens, K = dm->top_k, E = dm->n_experts;
+  const int64_t P = dm->n_ranks, R = dm->slots_per_rank, cap = dm->cap;
+  const int64_t S = N / P, Eh = E / P, NS = Eh + R;
+  /* [ISER] Objective 1: T = ceil(sum_r L_r / P); sum_r L_r = N*K. */
+  const int64_t T = (N * K + P - 1) / P;
+
+  memset(o->counts, 0, sizeof(int32_t) * P * E);
+  memset(o->load_pre, 0, sizeof(int32_t) * P);
+  memset(o->load_post, 0, sizeof(int32_t) * P);
+  for (int64_t i = 0; i < P * R; ++i) o->rep_expert[i] = -1;
+  memset(o->slot_quota, 0, sizeof(int32_t) * P * NS);
+  memset(o->cu_seqlens, 0, sizeof(int32_t) * P * (NS + 1));
+  for (int64_t i = 0; i < N * K; ++i) o->pos[i] = -1;
+  for (int64_t i = 0; i < N * K; ++i) o->host[i] = -1;
+  for (int64_t i = 0; i < P * cap; ++i) o->row_src[i] = -1;
+  o->status[0] = 0;
+  o->status[1] = (int32_t)T;
+  o->status[2] = 0;
+  o->status[3] = 0;
+  if (rep) memset(rep, 0, sizeof(*rep));
+
+  /* O0 — every id names an expert, and no token names one twice. */
+  int32_t flags = 0;
+  for (int64_t t = 0; t < N; ++t)
+    for (int64_t k = 0; k < K; ++k) {
+      int32_t e = ids[t * K + k];
+      if (e < 0 || e >= E) flags |= MBREF_ST_BAD_ID;
+      for (int64_t k2 = 0; k2 < k; ++k2)
+        if (ids[t * K + k2] == e) flags |= MBREF_ST_DUP_ID;
+    }
+  if (flags) {
+    o->status[0] = flags;
+    return MBREF_OK;
+  }
+
+  int64_t* c = calloc((size_t)E, sizeof(int64_t));     /* c_e */
+  int64_t* L = calloc((size_t)P, sizeof(int64_t));     /* L_r */
+  int64_t* load = calloc((size_t)P, sizeof(int64_t));  /* running load */
+  int64_t* qh = calloc((size_t)E, sizeof(int64_t));    /* home quota */
+  int64_t* rq = calloc((size_t)(P * R + 1), sizeof(int64_t)); /* replica quota */
+  char* is_host = calloc((size_t)(E * P), 1);          /* [e][r] */
+  char* tried = calloc((size_t)(Eh + 1), 1);
+  int64_t* Q = calloc((size_t)(E * P), sizeof(int64_t));    /* quota [e][h] */
+  int64_t* used = calloc((size_t)(E * P), sizeof(int64_t)); /* [e][h] */
+  int64_t* slot_of = calloc((size_t)(E * P), sizeof(int64_t)); /* [h][e] */
+  int64_t* rows = calloc((size_t)(P * NS), sizeof(int64_t));
+  int64_t* cu = calloc((size_t)(P * (NS + 1)), sizeof(int64_t));
+  int64_t* fill = calloc((size_t)(P * NS), sizeof(int64_t));
+  int rc = MBREF_OK;
+  if (!c || !L || !load || !qh || !rq || !is_host || !tried || !Q || !used ||
+      !slot_of || !rows || !cu || !fill) {
+    rc = MBREF_ERR_NOMEM;
+    goto done;
+  }
+
+  /* O1 — count. [ISER] stage 1: routed pairs per (source rank, expert),
+   * d_i^e of [Zepp] eq. (1); c_e = sum_s d[s][e]; L_r = sum of c_e over
+   * r's home experts. */
+  for (int64_t t = 0; t < N; ++t) {
+    const int64_t s = t / S;
+    for (int64_t k = 0; k < K; ++k) o->counts[s * E + ids[t * K + k]] += 1;
+  }
+  for (int64_t s = 0; s < P; ++s)
+    for (int64_t e = 0; e < E; ++e) c[e] += o->counts[s * E + e];
+  for (int64_t e = 0; e < E; ++e) L[e / Eh] += c[e];
+  for (int64_t r = 0; r < P; ++r) o->load_pre[r] = (int32_t)L[r];
+
+  /* O2 — greedy placement. [ISER] stage 2 picks the busiest rank's heaviest
+   * home expert and places a replica where a slot is free; stage 3 takes the
+   * smallest free helper index; [Zepp] §4.1 provides R slots per rank. */
+  for (int64_t r = 0; r < P; ++r) load[r] = L[r];
+  for (int64_t e = 0; e < E; ++e) {
+    qh[e] = c[e];
+    is_host[e * P + e / Eh] = 1;
+  }
+  int64_t moves = 0;
+  int unbalanced = 0;
+  for (;;) {
+    int64_t rs = 0; /* busiest rank, lowest index on ties */
+    for (int64_t r = 1; r < P; ++r)
+      if (load[r] > load[rs]) rs = r;
+    if (load[rs] <= T) break;
+    memset(tried, 0, (size_t)Eh);
+    int moved = 0;
+    for (;;) {
+      int64_t best = -1; /* heaviest untried home expert of rs */
+      for (int64_t i = 0; i < Eh; ++i) {
+        const int64_t e = rs * Eh + i;
+        if (tried[i] || qh[e] == 0) continue;
+        if (best < 0 || qh[e] > qh[best]) best = e;
+      }
+      if (best < 0) break;
+      tried[best - rs * Eh] = 1;
+      int64_t dst = -1; /* least loaded eligible rank, lowest index on ties */
+      for (int64_t r = 0; r < P; ++r) {
+        int64_t nfree = 0;
+        for (int64_t j = 0; j < R; ++j)
+          if (o->rep_expert[r * R + j] < 0) ++nfree;
+        if (nfree == 0 || load[r] >= T || is_host[best * P + r]) continue;
+        if (dst < 0 || load[r] < load[dst]) dst = r;
+      }
+      if (dst < 0) continue;
+      int64_t m = T - load[dst];
+      if (qh[best] < m) m = qh[best];
+      if (move_rule == MBREF_MOVE_EXCESS_ONLY && load[rs] - T < m) m = load[rs] - T;
+      int64_t j = 0; /* smallest free slot index */
+      while (o->rep_expert[dst * R + j] >= 0) ++j;
+      o->rep_expert[dst * R + j] = (int32_t)best;
+      rq[dst * R + j] = m;
+      is_host[best * P + dst] = 1;
+      qh[best] -= m;
+      load[rs] -= m;
+      load[dst] += m;
+      ++moves;
+      moved = 1;
+      break;
+    }
+    if (!moved) {
+      unbalanced = 1;
+      break;
+    }
+  }
+
+  /* Quotas per (expert, host) and the local slot of each (host, expert):
+   * home experts first by id, then replica slots ([MoonEP] [E+B,H,H']). */
+  for (int64_t i = 0; i < E * P; ++i) slot_of[i] = -1;
+  for (int64_t e = 0; e < E; ++e) {
+    const int64_t h = e / Eh;
+    Q[e * P + h] = qh[e];
+    slot_of[h * E + e] = e - h * Eh;
+    o->slot_quota[h * NS + (e - h * Eh)] = (int32_t)qh[e];
+  }
+  for (int64_t r = 0; r < P; ++r)
+    for (int64_t j = 0; j < R; ++j) {
+      const int32_t e = o->rep_expert[r * R + j];
+      if (e < 0) continue;
+      Q[e * P + r] = rq[r * R + j];
+      slot_of[r * E + e] = Eh + j;
+      o->slot_quota[r * NS + Eh + j] = (int32_t)rq[r * R + j];
+    }
+
+  /* O3 — assignment. [ISER] Objective 2 and stage 5; [Zepp] eq. (1).
+   * Pass 1, in (t, k) order: a pair stays on its source rank when that rank
+   * hosts the expert and still has quota. */
+  for (int64_t t = 0; t < N; ++t) {
+    const int64_t s = t / S;
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t e = ids[t * K + k];
+      if (is_host[e * P + s] && used[e * P + s] < Q[e * P + s]) {
+        o->host[t * K + k] = (int32_t)s;
+        used[e * P + s] += 1;
+      }
+    }
+  }
+  /* Pass 2, same order: every other pair goes to the lowest-index host of
+   * its expert that still has spare quota. */
+  for (int64_t t = 0; t < N; ++t)
+    for (int64_t k = 0; k < K; ++k) {
+      if (o->host[t * K + k] >= 0) continue;
+      const int64_t e = ids[t * K + k];
+      int64_t h = 0;
+      while (h < P && !(is_host[e * P + h] && used[e * P + h] < Q[e * P + h])) ++h;
+      if (h == P) {
+        rc = MBREF_ERR_INTERNAL; /* sum of quotas < c_e: cannot happen */
+        goto done;
+      }
+      o->host[t * K + k] = (int32_t)h;
+      used[e * P + h] += 1;
+    }
+
+  /* O4 — layout. [MoonEP] fixed [P*cap, H] buffer, rank r's region starting
+   * at row r*cap, slots contiguous in local slot order (cu_seqlens), rows of
+   * a slot in ascending token order. */
+  for (int64_t t = 0; t < N; ++t)
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t h = o->host[t * K + k];
+      rows[h * NS + slot_of[h * E + ids[t * K + k]]] += 1;
+    }
+  int64_t max_load = 0;
+  int cap_exceeded = 0;
+  for (int64_t h = 0; h < P; ++h) {
+    for (int64_t i = 0; i < NS; ++i) cu[h * (NS + 1) + i + 1] = cu[h * (NS + 1) + i] + rows[h * NS + i];
+    for (int64_t i = 0; i <= NS; ++i) o->cu_seqlens[h * (NS + 1) + i] = (int32_t)cu[h * (NS + 1) + i];
+    const int64_t lp = cu[h * (NS + 1) + NS];
+    o->load_post[h] = (int32_t)lp;
+    if (lp > max_load) max_load = lp;
+    if (lp > cap) cap_exceeded = 1;
+  }
+  if (!cap_exceeded) {
+    for (int64_t t = 0; t < N; ++t)
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t h = o->host[t * K + k];
+        const int64_t sl = slot_of[h * E + ids[t * K + k]];
+        const int64_t p = h * cap + cu[h * (NS + 1) + sl] + fill[h * NS + sl];
+        fill[h * NS + sl] += 1;
+        o->pos[t * K + k] = (int32_t)p;
+        o->row_src[p] = (int32_t)t;
+      }
+  }
+  o->status[0] = (unbalanced ? MBREF_ST_UNBALANCED : 0) | (cap_exceeded ? MBREF_ST_CAPACITY : 0);
+  o->status[2] = (int32_t)max_load;
+  o->status[3] = (int32_t)moves;
+
+  /* O7 — report. IR as in [ISER] Background; maxvio as in [MoonEP]
+   * "Variables and core terms"; excess removed as in [ISER] E1. */
+  if (rep) {
+    const double mean_l = (double)(N * K) / (double)P;
+    const double mean_c = (double)(N * K) / (double)E;
+    int64_t maxL = 0, maxc = 0;
+    for (int64_t r = 0; r < P; ++r) {
+      if (L[r] > maxL) maxL = L[r];
+      if (L[r] > T) rep->excess_before += L[r] - T;
+    }
+    for (int64_t e = 0; e < E; ++e)
+      if (c[e] > maxc) maxc = c[e];
+    rep->ir_before = mean_l > 0 ? (double)maxL / mean_l : 1.0;
+    rep->ir_after = mean_l > 0 ? (double)max_load / mean_l : 1.0;
+    rep->maxvio = mean_c > 0 ? (double)maxc / mean_c - 1.0 : 0.0;
+    rep->excess_removed = rep->ir_before > 1.0
+                              ? (rep->ir_before - rep->ir_after) / (rep->ir_before - 1.0)
+                              : 1.0;
+    rep->water_level = T;
+    rep->n_moves = moves;
+    rep->slots_used = moves;
+    for (int64_t t = 0; t < N; ++t)
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t h = o->host[t * K + k];
+        if (h != ids[t * K + k] / Eh) rep->offhome_pairs += 1;
+        if (h != t / S) rep->nonlocal_pairs += 1;
+      }
+  }
+
+done:
+  free(c); free(L); free(load); free(qh); free(rq); free(is_host); free(tried);
+  free(Q); free(used); free(slot_of); free(rows); free(cu); free(fill);
+  return rc;
+}
+
+/* O5 — dispatch: the row of token t is copied to every row pos[t][k]
+ * ([MoonEP] "What MoonEP enforces and how": tokens written straight into the
+ * fixed-shape expert-grouped buffers). */
+int mbref_dispatch_window(const mbref_dims* dm, const int32_t* pos,
+                          const int32_t* status, const void* x,
+                          const float* x_scale, int64_t row0, int64_t row1,
+                          void* buf_win, float* buf_scale_win) {
+  if (!dm || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
+  if (status[0] & MBREF_ST_FATAL) return 1;
+  const int64_t N = dm->n_tokens, K = dm->top_k;
+  const int64_t rb = (int64_t)dm->hidden * elt_bytes(dm->dtype_in);
+  const int64_t nsc = dm->dtype_in == MBREF_FP8_E4M3 ? dm->hidden / 128 : 0;
+  for (int64_t t = 0; t < N; ++t)
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t p = pos[t * K + k];
+      if (p < row0 || p >= row1) continue;
+      memcpy((char*)buf_win + (p - row0) * rb, (const char*)x + t * rb, (size_t)rb);
+      if (nsc && buf_scale_win && x_scale)
+        memcpy(buf_scale_win + (p - row0) * nsc, x_scale + t * nsc, sizeof(float) * (size_t)nsc);
+    }
+  return 0;
+}
+
+int mbref_dispatch(const mbref_dims* dm, const int32_t* pos,
+                   const int32_t* status, const void* x, const float* x_scale,
+                   void* buf, float* buf_scale) {
+  if (!dm || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
+  return mbref_dispatch_window(dm, pos, status, x, x_scale, 0,
+                               (int64_t)dm->n_ranks * dm->cap, buf, buf_scale);
+}
+
+static double out_elem(int32_t dtype, const void* base, int64_t idx) {
+  if (dtype == MBREF_F32) return (double)((const float*)base)[idx];
+  uint32_t b = (uint32_t)((const uint16_t*)base)[idx] << 16; /* bf16 */
+  float f;
+  memcpy(&f, &b, 4);
+  return (double)f;
+}
+
+/* O6 — combine: the weighted gather-reduce of the K expert-output rows of
+ * each token, in double precision. */
+int mbref_combine(const mbref_dims* dm, const int32_t* pos,
+                  const int32_t* status, const float* w, const void* y_exp,
+                  int32_t t0, int32_t t1, double* y, double* mag) {
+  if (!dm || !valid_dims(dm) || t0 < 0 || t1 < t0 || t1 > dm->n_tokens)
+    return MBREF_ERR_INVALID_ARG;
+  if (status[0] & MBREF_ST_FATAL) return 1;
+  const int64_t K = dm->top_k, H = dm->hidden;
+  for (int64_t t = t0; t < t1; ++t)
+    for (int64_t i = 0; i < H; ++i) {
+      double acc = 0.0, a = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double v = out_elem(dm->dtype_out, y_exp, (int64_t)pos[t * K + k] * H + i);
+        const double term = (double)w[t * K + k] * v;
+        acc += term;
+        a += fabs(term);
+      }
+      y[(t - t0) * H + i] = acc;
+      if (mag) mag[(t - t0) * H + i] = a;
+    }
+  return 0;
+}

@@ -1,0 +1,127 @@
+/*
+ * mbref.h — CPU oracle for per-invocation hot-expert replication and token
+ * dispatch/combine.
+ *
+ * TEST INFRASTRUCTURE. This library defines the expected results that the
+ * GPU library is compared against. Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it; the GPU path never calls it
+ * and shares no code, header or table with it.
+ *
+ * Plain, slow and single threaded on purpose: every step is a loop over the
+ * definition, in the order the pages state it. See mbref.c for the steps and
+ * their citations.
+ *
+ * Layouts (all row-major, all int32 unless noted):
+ *   ids[N][K], w[N][K] (float)            routing decisions per token
+ *   counts[P][E]                          d[s][e], pairs from source rank s to e
+ *   load_pre[P], load_post[P]             rank loads before / after planning
+ *   rep_expert[P][R]                      expert held by replica slot, -1 empty
+ *   slot_quota[P][Eh+R]                   rows planned per local slot
+ *   cu_seqlens[P][Eh+R+1]                 per-rank row offsets of the slots
+ *   pos[N][K]                             dispatch row of each pair
+ *   row_src[P*cap]                        token of each row, -1 for padding
+ *   host[N][K]                            rank serving each pair
+ *   status[4]                             {flags, T, max load_post, moves}
+ */
+#ifndef MBREF_H
+#define MBREF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MBREF_F32 = 0, MBREF_BF16 = 1, MBREF_FP8_E4M3 = 2 };
+
+enum {
+  MBREF_OK = 0,
+  MBREF_ERR_INVALID_ARG = -1,
+  MBREF_ERR_INTERNAL = -2,
+  MBREF_ERR_NOMEM = -3
+};
+
+/* status[0] bit flags */
+enum {
+  MBREF_ST_BAD_ID = 1,     /* an id outside [0, E) */
+  MBREF_ST_DUP_ID = 2,     /* an expert listed twice for one token */
+  MBREF_ST_UNBALANCED = 4, /* placement stopped with a rank above T */
+  MBREF_ST_CAPACITY = 8    /* a rank needs more than cap rows */
+};
+#define MBREF_ST_FATAL (MBREF_ST_BAD_ID | MBREF_ST_DUP_ID | MBREF_ST_CAPACITY)
+
+/* Move size rule of a placement step (see mbref.c, step O2). */
+enum { MBREF_MOVE_FILL_HOST = 0, MBREF_MOVE_EXCESS_ONLY = 1 };
+
+typedef struct mbref_dims {
+  int32_t n_tokens;       /* N */
+  int32_t top_k;          /* K */
+  int32_t n_experts;      /* E */
+  int32_t n_ranks;        /* P */
+  int32_t slots_per_rank; /* R */
+  int32_t hidden;         /* H */
+  int32_t cap;            /* rows per rank region of the dispatch buffer */
+  int32_t dtype_in;       /* token rows: MBREF_F32 / BF16 / FP8_E4M3 */
+  int32_t dtype_out;      /* expert outputs and combined rows: F32 / BF16 */
+} mbref_dims;
+
+typedef struct mbref_plan_out {
+  int32_t* counts;
+  int32_t* load_pre;
+  int32_t* load_post;
+  int32_t* rep_expert;
+  int32_t* slot_quota;
+  int32_t* cu_seqlens;
+  int32_t* pos;
+  int32_t* row_src;
+  int32_t* host;
+  int32_t* status;
+} mbref_plan_out;
+
+typedef struct mbref_report {
+  double ir_before;      /* max_r L_r / mean_r L_r */
+  double ir_after;       /* max_r load_post / mean */
+  double maxvio;         /* max_e c_e / mean_e c_e - 1 */
+  double excess_removed; /* (ir_before - ir_after) / (ir_before - 1) */
+  int64_t water_level;   /* T */
+  int64_t n_moves;
+  int64_t slots_used;
+  int64_t excess_before; /* sum_r (L_r - T)^+ */
+  int64_t offhome_pairs; /* pairs served by a rank other than home(e) */
+  int64_t nonlocal_pairs;/* pairs served by a rank other than src(t) */
+} mbref_report;
+
+int mbref_version(void);
+
+/* Steps O0-O4 and O7. Outputs must be sized as in the header comment.
+ * Returns MBREF_OK (data-dependent problems are status flags) or a
+ * negative error for invalid sizes. */
+int mbref_plan(const mbref_dims* dims, const int32_t* ids, int32_t move_rule,
+               mbref_plan_out* out, mbref_report* report);
+
+/* Step O5: buf[pos[t][k]] = x[t] (and the fp8 scale row). Rows of buf that
+ * no pair maps to are left untouched. Returns 1 if status is fatal (nothing
+ * written), 0 otherwise. */
+int mbref_dispatch(const mbref_dims* dims, const int32_t* pos,
+                   const int32_t* status, const void* x, const float* x_scale,
+                   void* buf, float* buf_scale);
+
+/* Step O5 restricted to destination rows [row0, row1): writes row p of the
+ * window to buf_win[p - row0]. */
+int mbref_dispatch_window(const mbref_dims* dims, const int32_t* pos,
+                          const int32_t* status, const void* x,
+                          const float* x_scale, int64_t row0, int64_t row1,
+                          void* buf_win, float* buf_scale_win);
+
+/* Step O6 for tokens [t0, t1): y[t - t0][i] = sum_k w[t][k] y_exp[pos[t][k]][i]
+ * in double; mag receives sum_k |w y| (may be NULL). y_exp is read as
+ * dtype_out. Returns 1 if status is fatal, 0 otherwise. */
+int mbref_combine(const mbref_dims* dims, const int32_t* pos,
+                  const int32_t* status, const float* w, const void* y_exp,
+                  int32_t t0, int32_t t1, double* y, double* mag);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBREF_H */

@@ -1,0 +1,112 @@
+"""The five synthetic workloads of the hot path.
+
+Shapes follow the pages' workloads: a tiny case for exhaustive checks, a
+Mixtral-like layer (8 experts, top-2), a DeepSeek-V3-like prefill layer
+(256 routed experts, top-8), a Kimi-K3-like prefill layer (384 experts,
+top-8, two replica slots per rank) and a 61-layer decode sequence with fp8
+rows and a fresh expert popularity permutation per layer call.
+
+Long-tailed routing stands in for the production traces the pages measure
+on: logits are noise plus beta * ln Zipf(s) popularity (see ``mbgen.c``).
+For the two prefill workloads, beta and the seed were picked by
+``workload/tune.py`` from statistics of the routing alone (group shares of
+routed pairs, top-4 expert share, rank imbalance before planning); the
+planner's outcome never enters that search.
+
+Sizes, and the statistic each workload is shaped to hit:
+
+* dsv3_prefill: at 8-way grouping of the 32 logical ranks, the busiest group
+  receives about 24 % of the routed pairs and the least loaded about 10 %
+  (ViBE summary, Challenge 1: the DeepSeek-V3 prefill skew).
+* kimi_prefill: the four hottest of 384 experts take about 13 % of the
+  assignments and max/mean rank load is about 1.45 before planning
+  (ISER-MoE, Background and Key Observation 1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    n_tokens: int
+    n_experts: int
+    top_k: int
+    n_ranks: int
+    slots_per_rank: int
+    hidden: int
+    dtype_in: str  # "f32" | "bf16" | "fp8"
+    dtype_out: str  # "f32" | "bf16" (expert outputs and combined rows)
+    noise: int  # 0 = N(0,1), 1 = Gumbel(0,1)
+    zipf_s: float
+    beta: float
+    seed: int
+    calls: int = 1
+    note: str = ""
+    targets: dict = field(default_factory=dict)
+
+    @property
+    def tokens_per_rank(self) -> int:
+        return self.n_tokens // self.n_ranks
+
+    @property
+    def cap(self) -> int:
+        """Rows per rank region of the dispatch buffer: S * K."""
+        return self.tokens_per_rank * self.top_k
+
+    def seed_for(self, call: int) -> int:
+        return self.seed + call
+
+    def scaled(self, n_tokens: int) -> "Workload":
+        """Same routing model with fewer tokens (a bounded sample)."""
+        d = dict(self.__dict__)
+        d["n_tokens"] = n_tokens
+        d["name"] = f"{self.name}@N={n_tokens}"
+        return Workload(**d)
+
+
+WORKLOADS: dict[str, Workload] = {
+    "tiny": Workload(
+        name="tiny", n_tokens=64, n_experts=16, top_k=2, n_ranks=4, slots_per_rank=1,
+        hidden=128, dtype_in="f32", dtype_out="f32", noise=0, zipf_s=1.2, beta=1.0,
+        seed=1000,
+        note="64 tokens, 16 experts (4 home per rank), top-2, 4 ranks, 1 replica slot, fp32 rows",
+    ),
+    "mixtral": Workload(
+        name="mixtral", n_tokens=4096, n_experts=8, top_k=2, n_ranks=8, slots_per_rank=1,
+        hidden=4096, dtype_in="bf16", dtype_out="bf16", noise=1, zipf_s=1.0, beta=1.0,
+        seed=2000,
+        note="4096 tokens, 8 experts (1 home per rank), top-2, 8 ranks, 1 slot, bf16 H=4096",
+    ),
+    "dsv3_prefill": Workload(
+        name="dsv3_prefill", n_tokens=131072, n_experts=256, top_k=8, n_ranks=32,
+        slots_per_rank=1, hidden=7168, dtype_in="bf16", dtype_out="bf16", noise=0,
+        zipf_s=1.0, beta=0.42, seed=3027,
+        note="32 ranks x 4096 tokens, 256 experts (8 home per rank), top-8, 1 slot, bf16 H=7168",
+        targets={"group8_max_share": 0.24, "group8_min_share": 0.10},
+    ),
+    "kimi_prefill": Workload(
+        name="kimi_prefill", n_tokens=131072, n_experts=384, top_k=8, n_ranks=16,
+        slots_per_rank=2, hidden=7168, dtype_in="bf16", dtype_out="bf16", noise=0,
+        zipf_s=1.0, beta=0.38, seed=4014,
+        note="16 ranks x 8192 tokens, 384 experts (24 home per rank), top-8, 2 slots, bf16 H=7168",
+        targets={"top4_share": 0.13, "ir_before": 1.45},
+    ),
+    "decode_drift": Workload(
+        name="decode_drift", n_tokens=8192, n_experts=256, top_k=8, n_ranks=64,
+        slots_per_rank=1, hidden=7168, dtype_in="fp8", dtype_out="bf16", noise=1,
+        zipf_s=1.1, beta=1.0, seed=5000, calls=61,
+        note="64 ranks x 128 tokens, 256 experts (4 home per rank), top-8, 1 slot, "
+             "fp8 e4m3 H=7168 + fp32 scale per 128, 61 layer calls with fresh popularity",
+    ),
+}
+
+ORDER = ["tiny", "mixtral", "dsv3_prefill", "kimi_prefill", "decode_drift"]
+
+
+def get_workload(name: str) -> Workload:
+    try:
+        return WORKLOADS[name]
+    except KeyError:
+        raise KeyError(f"unknown workload {name!r}; known: {', '.join(ORDER)}") from None

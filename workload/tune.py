@@ -1,0 +1,73 @@
+"""Deterministic search for (beta, seed) of the two prefill workloads.
+
+The objective uses statistics of the generated routing only: routed pairs per
+expert (numpy.bincount), summed into the contiguous home ranks of each expert,
+then into groups of ranks. It never runs the planner.
+
+* dsv3_prefill: group the 32 ranks into 8 groups of 4 consecutive ranks; aim
+  for the busiest group at 24 % of all routed pairs and the least loaded at
+  10 % (the DeepSeek-V3 prefill skew in the ViBE summary, Challenge 1).
+* kimi_prefill: aim for a 13 % share of the four hottest experts and a
+  max/mean rank load of 1.45 (ISER-MoE, Background and Key Observation 1).
+
+Usage: python -m workload.tune [dsv3_prefill|kimi_prefill] [n_seeds]
+Prints one line per candidate improving the objective, then the choice.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import workload as W
+
+
+def routing_stats(ids: np.ndarray, n_experts: int, n_ranks: int, groups: int = 8) -> dict:
+    n_pairs = ids.size
+    c = np.bincount(ids.ravel(), minlength=n_experts).astype(np.int64)
+    eh = n_experts // n_ranks
+    load = c.reshape(n_ranks, eh).sum(1)
+    g = load.reshape(groups, n_ranks // groups).sum(1) if n_ranks % groups == 0 else load
+    top4 = np.sort(c)[::-1][:4].sum()
+    return {
+        "group8_max_share": float(g.max() / n_pairs),
+        "group8_min_share": float(g.min() / n_pairs),
+        "top4_share": float(top4 / n_pairs),
+        "ir_before": float(load.max() / load.mean()),
+        "maxvio": float(c.max() / c.mean() - 1.0),
+    }
+
+
+def objective(name: str, st: dict) -> float:
+    if name == "dsv3_prefill":
+        return (st["group8_max_share"] - 0.24) ** 2 + (st["group8_min_share"] - 0.10) ** 2
+    if name == "kimi_prefill":
+        return ((st["top4_share"] - 0.13) / 0.13) ** 2 + ((st["ir_before"] - 1.45) / 1.45) ** 2
+    raise KeyError(name)
+
+
+def search(name: str, n_seeds: int = 16) -> tuple[float, int, dict]:
+    wl = W.get_workload(name)
+    base = {"dsv3_prefill": 3000, "kimi_prefill": 4000}[name]
+    betas = {"dsv3_prefill": np.arange(0.30, 0.601, 0.02),
+             "kimi_prefill": np.arange(0.30, 0.501, 0.02)}[name]
+    best = (np.inf, None, None, None)
+    for beta in betas:
+        beta = round(float(beta), 2)
+        for seed in range(base, base + n_seeds):
+            ids, _ = W.routing(wl.n_tokens, wl.n_experts, wl.top_k, wl.noise, wl.zipf_s, beta, seed)
+            st = routing_stats(ids, wl.n_experts, wl.n_ranks)
+            f = objective(name, st)
+            if f < best[0]:
+                best = (f, beta, seed, st)
+                print(f"{name} beta={beta:.2f} seed={seed} obj={f:.3e} "
+                      + " ".join(f"{k}={v:.4f}" for k, v in st.items()), flush=True)
+    return best[1], best[2], best[3]
+
+
+if __name__ == "__main__":
+    names = sys.argv[1:2] or ["dsv3_prefill", "kimi_prefill"]
+    n = int(sys.argv[2]) if len(sys.argv) > 2 else 16
+    for nm in names:
+        beta, seed, st = search(nm, n)
+        print(f"CHOICE {nm}: beta={beta} seed={seed} {st}")
