@@ -1,0 +1,296 @@
+"""Benchmark of the hot path: mb_plan + mb_dispatch + mb_combine per step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one MoE layer call of the chosen workload (default: the
+DeepSeek-V3-like prefill layer, 32 logical ranks x 4096 tokens, 256 experts,
+top-8, 1 replica slot per rank, bf16 rows of 7168): plan, dispatch every token
+row to its K rows, combine the K expert-output rows of every token. Inputs are
+seeded synthetic routing and rows, resident in HBM before timing starts.
+Expert outputs are the dispatched rows (identity experts), written once
+before timing into a buffer of their own.
+
+Prints one JSON line. `value` is dispatch + combine algorithmic bytes per
+step divided by the whole step time (plan included). `roofline` refers to the
+kernel with the larger share of the step (HIP events on the launch stream);
+`cpu_baseline` times the CPU oracle (single thread) on a quarter of the
+tokens of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine GB/s (% of HBM peak) and mb_plan µs per MoE layer call"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_k_dispatch_k_combine_dsv3_prefill.md")
+ROW_KERNEL_SOURCE = os.path.join(ROOT, "token_dispatch_mb_amd", "csrc", "rows.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes the method itself must move per layer call (no padding, no
+    staging): dispatch reads each row once and writes it K times, reading
+    pos; combine reads K expert rows, pos and w per token and writes one row."""
+    N, K, H = wl.n_tokens, wl.top_k, wl.hidden
+    b_in = {"f32": 4, "bf16": 2, "fp8": 1}[wl.dtype_in]
+    b_out = {"f32": 4, "bf16": 2}[wl.dtype_out]
+    row_in = H * b_in + (H // 128 * 4 if wl.dtype_in == "fp8" else 0)
+    row_out = H * b_out
+    dispatch = N * row_in + N * K * row_in + N * K * 4
+    combine = N * K * row_out + N * K * 8 + N * row_out
+    return {"dispatch": dispatch, "combine": combine, "row_in": row_in, "row_out": row_out}
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(ROW_KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if absent, for another workload, or taken on different
+    kernel source."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    text = open(PROFILE_PMC).read()
+    m = re.search(r"^source_sha256_16:\s*(\w+)", text, re.M)
+    if not m or m.group(1) != source_hash():
+        return None
+    m = re.search(r"^workload:\s*(\S+)", text, re.M)
+    if not m or m.group(1) != workload:
+        return None
+    m = re.search(rf"^traffic_bytes_per_launch\.{kernel}:\s*([0-9.eE+]+)", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(wl, fraction: int = 4) -> dict:
+    """The CPU oracle as it stands (single thread) on 1/fraction of the
+    tokens of the same workload: plan, dispatch and combine; GB/s over the
+    same algorithmic bytes, plus the oracle's plan time on the full call."""
+    import numpy as np
+
+    import oracle as O
+    import workload as W
+
+    sub = wl.scaled(wl.n_tokens // fraction)
+    ids, w = W.routing_for(sub)
+    x, xs = W.token_rows(sub)
+    od = O.dims_for(sub)
+    t0 = time.perf_counter()
+    p = O.plan(od, ids)
+    t1 = time.perf_counter()
+    buf, bs, _ = O.dispatch(od, p, x, xs)
+    t2 = time.perf_counter()
+    if od.dtype_out == O.BF16 and od.dtype_in == O.BF16:
+        y_exp = buf.view(np.uint16).reshape(-1, od.hidden)
+    elif od.dtype_out == O.F32 and od.dtype_in == O.F32:
+        y_exp = buf.view(np.float32).reshape(-1, od.hidden)
+    else:
+        y_exp = W.rows_bf16(sub.seed, W.TAG_YEXP, od.hidden, n=od.n_ranks * od.cap)
+    t3 = time.perf_counter()
+    O.combine(od, p.pos, p.status, w, y_exp)
+    t4 = time.perf_counter()
+    ab = algorithmic_bytes(sub)
+    full_ids, _ = W.routing_for(wl)
+    f0 = time.perf_counter()
+    O.plan(O.dims_for(wl), full_ids)
+    f1 = time.perf_counter()
+    return {
+        "value": round((ab["dispatch"] + ab["combine"]) / ((t2 - t1) + (t4 - t3)) / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{sub.n_tokens} of {wl.n_tokens} tokens of {wl.name} (same routing model, "
+                  f"same E/K/P/R/H): plan + dispatch + combine, single-threaded C oracle",
+        "plan_us_sample": round((t1 - t0) * 1e6, 1),
+        "dispatch_s": round(t2 - t1, 3),
+        "combine_s": round(t4 - t3, 3),
+        "plan_us_full_call": round((f1 - f0) * 1e6, 1),
+        "host_cpu": _cpu_model(),
+        "host_nproc": os.cpu_count(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--skip-cpu-baseline", action="store_true",
+                    help="leave out the CPU oracle leg (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the P logical ranks of the expert-parallel group are "
+              "partitions of one GPU's memory, so there is nothing to run on more GPUs.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import token_dispatch_mb_amd as mb
+    import workload as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    wl = W.get_workload(args.workload)
+    dims = mb.Dims.for_workload(wl)
+    log(f"workload {wl.name}: {wl.note}")
+
+    ids, w = W.routing_for(wl)
+    x, xs = W.token_rows(wl)
+    log("inputs generated")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+    ids_d = torch.from_numpy(ids).to(dev)
+    w_d = torch.from_numpy(w).to(dev)
+    x_d = torch.from_numpy(x).view(tdt[wl.dtype_in]).to(dev)
+    xs_d = torch.from_numpy(xs).to(dev) if xs is not None else None
+    del x
+    bufs = mb.PlanBuffers.allocate(dims, dev)
+    ws = mb.alloc_workspace(dims, dev)
+    buf = torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_in], device=dev)
+    bs = torch.empty((dims.rows, wl.hidden // 128), dtype=torch.float32, device=dev) \
+        if wl.dtype_in == "fp8" else None
+    y_exp = torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
+    y = torch.empty((wl.n_tokens, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
+
+    # Expert outputs: the dispatched rows (identity experts), or for fp8
+    # rows a generated bf16 buffer.
+    mb.plan(dims, ids_d, ws, bufs)
+    if wl.dtype_in == wl.dtype_out:
+        mb.dispatch(dims, bufs, x_d, y_exp, xs_d, bs)
+    else:
+        y_exp.copy_(torch.from_numpy(
+            W.rows_bf16(wl.seed, W.TAG_YEXP, wl.hidden, n=dims.rows)).view(torch.bfloat16))
+    status = mb.plan_status(bufs)
+    log(f"status {status.tolist()} (flags, T, max load, moves)")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mb.plan(dims, ids_d, ws, bufs)
+        if ev is not None:
+            ev[1].record()
+        mb.dispatch(dims, bufs, x_d, buf, xs_d, bs)
+        if ev is not None:
+            ev[2].record()
+        mb.combine(dims, bufs, y_exp, w_d, y)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+
+    plan_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    disp_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    total_ms = evs[0][0].elapsed_time(evs[-1][3])
+    ms_per_step = total_ms / args.steps
+    ab = algorithmic_bytes(wl)
+    bytes_step = ab["dispatch"] + ab["combine"]
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    d_gbps = ab["dispatch"] / (disp_ms.mean() * 1e-3) / 1e9
+    c_gbps = ab["combine"] / (comb_ms.mean() * 1e-3) / 1e9
+    dominant = "k_combine" if comb_ms.mean() >= disp_ms.mean() else "k_dispatch"
+    dom_bytes = ab["combine"] if dominant == "k_combine" else ab["dispatch"]
+    dom_ms = comb_ms.mean() if dominant == "k_combine" else disp_ms.mean()
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    # Correctness spot check of the timed buffers (identity experts: the
+    # combined row is sum_k w_k x_t).
+    status = mb.plan_status(bufs)
+    mean_load = wl.n_tokens * wl.top_k / wl.n_ranks
+    if wl.dtype_in == wl.dtype_out:
+        samp = torch.arange(0, wl.n_tokens, max(1, wl.n_tokens // 256), device=dev)
+        err = (y[samp].float() - x_d[samp].float() * w_d[samp].sum(1, keepdim=True)).abs().max()
+        log(f"identity-expert check: max |y - x * sum(w)| = {float(err):.3e}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype_in == "bf16" else wl.dtype_in,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "tokens": wl.n_tokens, "experts": wl.n_experts,
+            "top_k": wl.top_k, "logical_ranks": wl.n_ranks, "replica_slots_per_rank":
+                wl.slots_per_rank, "hidden": wl.hidden, "rows_in": wl.dtype_in,
+            "rows_out": wl.dtype_out, "cap": wl.cap,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "dispatch_combine_gbps": round(bytes_step / ((disp_ms.mean() + comb_ms.mean()) * 1e-3) / 1e9, 2),
+        "plan_us": {"mean": round(plan_ms.mean() * 1e3, 2), "p50": round(float(np.median(plan_ms)) * 1e3, 2),
+                    "p99": round(float(np.percentile(plan_ms, 99)) * 1e3, 2)},
+        "dispatch_us": round(disp_ms.mean() * 1e3, 2),
+        "combine_us": round(comb_ms.mean() * 1e3, 2),
+        "dispatch_gbps": round(d_gbps, 2),
+        "combine_gbps": round(c_gbps, 2),
+        "algorithmic_bytes": {"dispatch": ab["dispatch"], "combine": ab["combine"]},
+        "plan_status": {"flags": int(status[0]), "water_level": int(status[1]),
+                        "max_load": int(status[2]), "moves": int(status[3]),
+                        "ir_after": round(float(status[2]) / mean_load, 5)},
+        "wall_s_timed": round(t_wall, 4),
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(dominant, wl.name),
+        },
+    }
+    del buf, y_exp, y, x_d
+    torch.cuda.empty_cache()
+    if not args.skip_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -46,9 +46,9 @@
  *    plan never writes out of bounds. When a fatal bit is set, the plan's
  *    pos and row_src contents are unspecified.
  *
- * Limits: 1 <= P <= 64, E % P == 0, E <= 2048, 1 <= K <= min(E, 32),
- * 0 <= R <= 64, N % P == 0, N*K < 2^31, P*cap < 2^31, row bytes a multiple
- * of 16; fp8 rows need H % 128 == 0.
+ * Limits: 1 <= P <= 64, E % P == 0, E <= 1024, 1 <= K <= min(E, 32),
+ * 0 <= R <= 16, N % P == 0, N*K < 2^31, P*cap < 2^31, row bytes a multiple
+ * of 16; fp8 rows need H % 128 == 0. rep_expert may be NULL when R == 0.
  */
 #ifndef MOEBAL_H
 #define MOEBAL_H
@@ -111,7 +111,8 @@ typedef struct mb_dims {
  *                       r*Eh + i, i >= Eh is replica slot i - Eh
  *   cu_seqlens[P*(NS+1)] per-rank running row offsets of the local slots,
  *                       relative to the rank's region (cu[r][0] = 0)
- *   pos[N*K]            dispatch row of pair (t, k), in [0, P*cap)
+ *   pos[N*K]            dispatch row of pair (t, k), in [0, P*cap) (may be
+ *                       NULL when N == 0)
  *   row_src[P*cap]      token of each dispatch row, -1 for padding rows
  *   status[4]           {flags (mb_status_flag), T, max_r load_post, moves}
  */
@@ -176,7 +177,8 @@ int mb_dispatch(const mb_dims* dims, const mb_plan_bufs* plan, const void* x_dev
                 hipStream_t stream);
 
 /*
- * Combine [Zepp §4.2 merge, combine side; MoonEP fixed buffers]:
+ * Combine [Zepp §4.2, Merge: the combine step aggregates a token's expert
+ * outputs; MoonEP fixed buffers]:
  *   y[t][i] = sum_{k=0..K-1} w[t][k] * y_exp[pos[t][k]][i]
  * accumulated in fp32 in k order, stored as dtype_out (bf16: round to
  * nearest even).

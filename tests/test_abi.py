@@ -1,0 +1,101 @@
+"""The C ABI of libmoebal without a GPU: every symbol include/moebal.h
+declares is exported, and the host-side checks return the documented codes
+before anything reaches the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_dispatch_mb_amd as mb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "moebal.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mb_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(mb.EXPORTS)
+    lib = ctypes.CDLL(mb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    assert mb.version() == 1
+    for code in (mb.OK, mb.ERR_INVALID_ARG, mb.ERR_WORKSPACE, mb.ERR_HIP, mb.ST_BAD_ID,
+                 mb.ST_DUP_ID, mb.ST_UNBALANCED, mb.ST_CAPACITY, 12345):
+        assert isinstance(mb.strerror(code), str) and mb.strerror(code)
+
+
+def test_workspace_bytes_host_only():
+    d = mb.Dims.make(131072, 8, 256, 32, 1, 7168)
+    n = mb.workspace_bytes(d)
+    # per-block counts and offsets dominate: 2 * (32 sources * 16 blocks) * 256 experts * 4 B
+    assert n >= 2 * 512 * 256 * 4
+    assert n % 256 == 0
+
+
+@pytest.mark.parametrize("args,cap", [
+    ((64, 2, 16, 3, 1, 128), 32),      # N % P
+    ((64, 2, 15, 4, 1, 128), 32),      # E % P
+    ((64, 0, 16, 4, 1, 128), 32),      # K = 0
+    ((64, 17, 16, 4, 1, 128), 32),     # K > E
+    ((128, 2, 2048, 128, 1, 128), 32), # P > 64
+    ((64, 2, 2048, 4, 1, 128), 32),    # E > 1024
+    ((64, 2, 16, 4, 17, 128), 32),     # R > 16
+    ((64, 2, 16, 4, -1, 128), 32),     # R < 0
+    ((64, 2, 16, 4, 1, 128), 0),       # cap = 0
+    ((64, 2, 16, 4, 1, 4), 32),        # bf16 row of 8 bytes
+])
+def test_invalid_sizes_rejected_on_host(args, cap):
+    d = mb.Dims.make(*args, cap=cap)
+    d.cap = cap
+    assert mb.workspace_bytes(d) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    bufs = mb._PlanBufsC(*([1 << 20] * 9))
+    rc = mb.raw_call("mb_plan", ctypes.byref(d), fake, fake, 1 << 30, ctypes.byref(bufs), None)
+    assert rc == mb.ERR_INVALID_ARG
+    rc = mb.raw_call("mb_dispatch", ctypes.byref(d), ctypes.byref(bufs), fake, None, fake, None, None)
+    assert rc == mb.ERR_INVALID_ARG
+    rc = mb.raw_call("mb_combine", ctypes.byref(d), ctypes.byref(bufs), fake, fake, fake, None)
+    assert rc == mb.ERR_INVALID_ARG
+
+
+def test_fp8_needs_h_multiple_of_128_and_scales():
+    d = mb.Dims.make(64, 2, 16, 4, 1, 64, dtype_in="fp8", dtype_out="bf16")
+    assert mb.workspace_bytes(d) == 0
+    d = mb.Dims.make(64, 2, 16, 4, 1, 128, dtype_in="fp8", dtype_out="bf16")
+    assert mb.workspace_bytes(d) > 0
+    fake = ctypes.c_void_p(1 << 20)
+    bufs = mb._PlanBufsC(*([1 << 20] * 9))
+    rc = mb.raw_call("mb_dispatch", ctypes.byref(d), ctypes.byref(bufs), fake, None, fake, None, None)
+    assert rc == mb.ERR_INVALID_ARG
+
+
+def test_small_workspace_and_null_pointers_rejected():
+    d = mb.Dims.make(64, 2, 16, 4, 1, 128)
+    need = mb.workspace_bytes(d)
+    fake = ctypes.c_void_p(1 << 20)
+    bufs = mb._PlanBufsC(*([1 << 20] * 9))
+    rc = mb.raw_call("mb_plan", ctypes.byref(d), fake, fake, need - 1, ctypes.byref(bufs), None)
+    assert rc == mb.ERR_WORKSPACE
+    rc = mb.raw_call("mb_plan", ctypes.byref(d), None, fake, need, ctypes.byref(bufs), None)
+    assert rc == mb.ERR_INVALID_ARG
+    nulls = mb._PlanBufsC(*([1 << 20] * 8 + [0]))
+    rc = mb.raw_call("mb_plan", ctypes.byref(d), fake, fake, need, ctypes.byref(nulls), None)
+    assert rc == mb.ERR_INVALID_ARG
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    rc = mb.raw_call("mb_plan", ctypes.byref(d), fake, mis, need, ctypes.byref(bufs), None)
+    assert rc == mb.ERR_INVALID_ARG
+    rc = mb.raw_call("mb_dispatch", ctypes.byref(d), ctypes.byref(bufs), mis, None, fake, None, None)
+    assert rc == mb.ERR_INVALID_ARG
+    rc = mb.raw_call("mb_plan_status", None, None, None)
+    assert rc == mb.ERR_INVALID_ARG

@@ -1,0 +1,326 @@
+"""Parity of libmoebal on the GPU with the CPU oracle, through the C ABI.
+
+Integers (counts, loads, plan, quotas, cu_seqlens, pos, row_src, status) and
+dispatched bytes must be bit-exact; combine must be within the tolerance of
+``gpu_harness.TOL`` relative to sum_k |w_k y_k|. Inputs are seeded synthetic
+workloads from ``workload``; expected values come from ``oracle`` only.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import token_dispatch_mb_amd as mb
+import workload as W
+from tests import gpu_harness as G
+from tests import plan_checks as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_required():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _y_exp_rows(wl_seed: int, dims, n_rows: int):
+    if dims.dtype_out == O.F32:
+        return W.rows_f32(wl_seed, W.TAG_YEXP, dims.hidden, n=n_rows)
+    return W.rows_bf16(wl_seed, W.TAG_YEXP, dims.hidden, n=n_rows)
+
+
+def _full_check(dims_g, od, ids, w, x, xs, y_exp, label=""):
+    """Plan, dispatch and combine on the GPU; compare everything with the oracle."""
+    G.log(f"case {label}: N={od.n_tokens} K={od.top_k} E={od.n_experts} P={od.n_ranks} "
+          f"R={od.slots_per_rank} H={od.hidden} cap={od.cap}")
+    gp = G.GpuPlan(dims_g).run(ids)
+    got = gp.fetch()
+    ref = O.plan(od, ids)
+    G.assert_plan_equal(got, ref)
+    buf, bs, y = G.run_rows(dims_g, gp, x, xs, y_exp, w)
+    fatal = bool(ref.status[0] & O.ST_FATAL)
+    if fatal:
+        assert np.all(buf == 0xA5), "dispatch wrote despite a fatal status"
+        assert np.all(np.isnan(y)), "combine wrote despite a fatal status"
+        return ref
+    ref_buf, ref_bs, _ = O.dispatch(od, ref, x, xs)
+    used = ref.row_src >= 0
+    assert np.array_equal(buf[used], ref_buf[used]), "dispatched rows"
+    assert np.all(buf[~used] == 0xA5), "padding rows were written"
+    if ref_bs is not None:
+        assert np.array_equal(bs[used], ref_bs[used]), "dispatched fp8 scales"
+    y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, y_exp)
+    G.assert_combine_close(y, y_ref, mag, "f32" if od.dtype_out == O.F32 else "bf16")
+    return ref
+
+
+# ---- the small workloads, end to end -------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "decode_drift"])
+def test_workload_end_to_end(name):
+    wl = W.get_workload(name)
+    ids, w = W.routing_for(wl)
+    x, xs = W.token_rows(wl)
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    ye = _y_exp_rows(wl.seed, od, od.n_ranks * od.cap)
+    ref = _full_check(dg, od, ids, w, x, xs, ye, name)
+    assert ref.status[0] == 0
+
+
+def test_decode_drift_61_calls_stateless():
+    """Every call of the 61-layer decode sequence, planned back to back into
+    the same buffers, equals the oracle; calls planned alone into fresh
+    buffers equal the same calls inside the sequence."""
+    wl = W.get_workload("decode_drift")
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    seq = G.GpuPlan(dg)
+    G.log("decode_drift: 61 calls")
+    kept = {}
+    for call in range(wl.calls):
+        ids, _ = W.routing_for(wl, call)
+        got = seq.run(ids).fetch()
+        G.assert_plan_equal(got, O.plan(od, ids))
+        if call in (0, 29, 60):
+            kept[call] = got
+    for call, got_seq in kept.items():
+        ids, _ = W.routing_for(wl, call)
+        alone = G.GpuPlan(dg).run(ids).fetch()
+        for k in G.PLAN_FIELDS:
+            assert np.array_equal(alone[k], got_seq[k]), (call, k)
+
+
+def test_decode_drift_rows_several_calls():
+    wl = W.get_workload("decode_drift")
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    for call in (1, 37):
+        ids, w = W.routing_for(wl, call)
+        x, xs = W.token_rows(wl, call)
+        ye = _y_exp_rows(wl.seed_for(call), od, od.n_ranks * od.cap)
+        _full_check(dg, od, ids, w, x, xs, ye, f"decode_drift call {call}")
+
+
+# ---- shape sweep ------------------------------------------------------------------
+
+def _sweep_cases():
+    rng = np.random.default_rng(2024)
+    cases = []
+    for P in (1, 2, 4, 8, 16, 32, 64):
+        for R in (0, 1, 2, 4):
+            K = int(rng.choice([1, 2, 8]))
+            eh = int(rng.choice([1, 4, 8, 24]))
+            if K > P * eh:
+                K = P * eh
+            S = int(rng.choice([3, 37, 300, 513]))
+            cases.append((P, eh, K, R, S))
+    return cases
+
+
+@pytest.mark.parametrize("P,eh,K,R,S", _sweep_cases())
+def test_shape_sweep(P, eh, K, R, S):
+    E, N = P * eh, P * S
+    ids, w = W.routing(N, E, K, W.NOISE_NORMAL, 1.0, 0.8, 7000 + P * 31 + R * 7 + K)
+    cap = S * K if R > 0 else N * K  # R = 0: make room for the unbalanced load
+    H = 64
+    dg = mb.Dims.make(N, K, E, P, R, H, cap=cap, dtype_in="f32", dtype_out="f32")
+    od = O.make_dims(N, K, E, P, R, H, cap=cap, dtype_in="f32", dtype_out="f32")
+    x = W.rows_f32(P * 1000 + S, W.TAG_X, H, n=N)
+    ye = W.rows_f32(P * 1000 + S, W.TAG_YEXP, H, n=P * cap)
+    _full_check(dg, od, ids, w, x, xs=None, y_exp=ye, label=f"sweep P{P} Eh{eh} K{K} R{R} S{S}")
+
+
+# ---- edge cases ---------------------------------------------------------------------
+
+def _edge(N, K, E, P, R, H, ids, cap=None, din="bf16", dout="bf16", seed=11, label="edge"):
+    dg = mb.Dims.make(N, K, E, P, R, H, cap=cap, dtype_in=din, dtype_out=dout)
+    od = O.make_dims(N, K, E, P, R, H, cap=cap, dtype_in=din, dtype_out=dout)
+    w = np.full((N, K), 1.0 / K, np.float32)
+    if din == "fp8":
+        x, xs, _ = W.rows_fp8(seed, W.TAG_X, H, n=N)
+    elif din == "f32":
+        x, xs = W.rows_f32(seed, W.TAG_X, H, n=N), None
+    else:
+        x, xs = W.rows_bf16(seed, W.TAG_X, H, n=N), None
+    ye = _y_exp_rows(seed, od, od.n_ranks * od.cap)
+    return _full_check(dg, od, np.ascontiguousarray(ids, np.int32), w, x, xs, ye, label)
+
+
+def test_all_tokens_one_expert():
+    P, S = 16, 40
+    ref = _edge(P * S, 1, P * 2, P, 1, 32, np.zeros((P * S, 1)), label="all-to-one")
+    assert ref.status[3] == P - 1
+
+
+def test_uniform_loads():
+    P, S, K, E = 8, 32, 4, 32
+    t = np.arange(P * S)[:, None]
+    ids = (t * K + np.arange(K)[None]) % E
+    ref = _edge(P * S, K, E, P, 2, 64, ids, label="uniform")
+    assert ref.status[3] == 0
+
+
+def test_r0_unbalanced_with_room_and_capacity():
+    wl = W.get_workload("mixtral")
+    ids, _ = W.routing_for(wl)
+    ref = _edge(wl.n_tokens, 2, 8, 8, 0, 256, ids, cap=wl.n_tokens * 2, label="R0 room")
+    assert ref.status[0] == O.ST_UNBALANCED
+    ref = _edge(wl.n_tokens, 2, 8, 8, 0, 256, ids, label="R0 capacity")
+    assert ref.status[0] == O.ST_UNBALANCED | O.ST_CAPACITY
+
+
+def test_capacity_below_water_level():
+    wl = W.get_workload("tiny")
+    ids, _ = W.routing_for(wl)
+    ref = _edge(64, 2, 16, 4, 1, 128, ids, cap=wl.cap - 3, din="f32", dout="f32", label="cap<T")
+    assert ref.status[0] & O.ST_CAPACITY
+
+
+def test_bad_and_duplicate_ids():
+    ids = np.tile(np.array([[0, 1]], np.int32), (64, 1))
+    ids[10, 1] = 16
+    ref = _edge(64, 2, 16, 4, 1, 64, ids, label="bad id")
+    assert ref.status[0] == O.ST_BAD_ID
+    ids[10, 1] = -5
+    _edge(64, 2, 16, 4, 1, 64, ids, label="negative id")
+    ids[10, 1] = 0
+    ref = _edge(64, 2, 16, 4, 1, 64, ids, label="dup id")
+    assert ref.status[0] == O.ST_DUP_ID
+
+
+def test_empty_batch():
+    dg = mb.Dims.make(0, 2, 16, 4, 1, 64, cap=8, dtype_in="bf16", dtype_out="bf16")
+    od = O.make_dims(0, 2, 16, 4, 1, 64, cap=8, dtype_in="bf16", dtype_out="bf16")
+    ids = np.zeros((0, 2), np.int32)
+    got = G.GpuPlan(dg).run(ids).fetch()
+    ref = O.plan(od, ids)
+    G.assert_plan_equal(got, ref)
+
+
+@pytest.mark.parametrize("K", [3, 5, 16, 32])
+def test_generic_top_k(K):
+    """Top-K values without a specialised kernel use the runtime-K path."""
+    P, eh, S = 4, 16, 77
+    E = P * eh
+    ids, w = W.routing(P * S, E, K, W.NOISE_NORMAL, 1.0, 1.0, 900 + K)
+    _edge(P * S, K, E, P, 2, 64, ids, label=f"K={K}")
+
+
+def test_k_equals_e_and_single_rank_and_e_equals_p():
+    ids, _ = W.routing(40, 8, 8, W.NOISE_NORMAL, 1.0, 1.0, 3)
+    _edge(40, 8, 8, 4, 1, 64, ids, label="K=E")
+    ids, _ = W.routing(300, 24, 4, W.NOISE_NORMAL, 1.0, 1.0, 4)
+    _edge(300, 4, 24, 1, 2, 64, ids, label="P=1")
+    ids, _ = W.routing(640, 64, 2, W.NOISE_GUMBEL, 1.0, 1.0, 5)
+    _edge(640, 2, 64, 64, 1, 64, ids, label="E=P=64")
+
+
+def test_maximum_sizes():
+    """E = 1024 experts, P = 64 ranks, R = 16 slots, K = 32, 16-byte rows."""
+    P, eh, S, K, R = 64, 16, 20, 32, 16
+    ids, _ = W.routing(P * S, P * eh, K, W.NOISE_GUMBEL, 1.2, 1.0, 12)
+    _edge(P * S, K, P * eh, P, R, 8, ids, label="max E/P/R/K")
+    ids, _ = W.routing(P * S, P * eh, 8, W.NOISE_GUMBEL, 1.2, 1.0, 13)
+    _edge(P * S, 8, P * eh, P, R, 4, ids, din="f32", dout="f32", label="16-byte f32 rows")
+
+
+def test_fp8_rows_and_scales_small():
+    ids, _ = W.routing(512, 32, 4, W.NOISE_GUMBEL, 1.1, 1.0, 21)
+    _edge(512, 4, 32, 8, 1, 256, ids, din="fp8", dout="bf16", label="fp8")
+
+
+def test_repeat_is_bit_identical():
+    wl = W.get_workload("decode_drift")
+    ids, _ = W.routing_for(wl, 5)
+    gp = G.GpuPlan(mb.Dims.for_workload(wl))
+    first = gp.run(ids).fetch()
+    for _ in range(4):
+        again = gp.run(ids).fetch()
+        for k in G.PLAN_FIELDS:
+            assert np.array_equal(first[k], again[k]), k
+
+
+def test_round_trip_identity_experts():
+    """pi14 on the GPU: with expert outputs equal to the dispatched rows,
+    one-hot weights return x bit-exactly."""
+    wl = W.get_workload("mixtral")
+    ids, _ = W.routing_for(wl)
+    dg = mb.Dims.for_workload(wl)
+    gp = G.GpuPlan(dg).run(ids)
+    x, _ = W.token_rows(wl)
+    x_d = G.torch_rows(x, O.BF16)
+    buf = torch.empty((dg.rows, dg.hidden), dtype=torch.bfloat16, device=G.dev())
+    mb.dispatch(dg, gp.bufs, x_d, buf)
+    onehot = np.zeros((wl.n_tokens, wl.top_k), np.float32)
+    onehot[np.arange(wl.n_tokens), np.arange(wl.n_tokens) % wl.top_k] = 1.0
+    y = torch.empty_like(x_d)
+    mb.combine(dg, gp.bufs, buf, torch.from_numpy(onehot).to(G.dev()), y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), x_d.view(torch.int16))
+
+
+# ---- full-size prefill workloads -----------------------------------------------------
+
+G_ROWS = 4099  # distinct expert-output rows, cycled over the buffer (prime)
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"])
+def test_prefill_full_size(name):
+    """The full prefill workloads in the launch configuration the benchmark
+    times: the whole plan bit-exact; dispatched rows of three rank regions
+    and 2048 random rows bit-exact; combine of 1024 sampled tokens in
+    tolerance. Expert outputs cycle through 4099 generated rows."""
+    wl = W.get_workload(name)
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    G.log(f"{name}: routing")
+    ids, w = W.routing_for(wl)
+    ref = O.plan(od, ids)
+    gp = G.GpuPlan(dg).run(ids)
+    got = gp.fetch()
+    G.assert_plan_equal(got, ref)
+    assert ref.status[0] == 0 and ref.report["ir_after"] <= 1.01
+    G.log(f"{name}: plan bit-exact (IR {ref.report['ir_before']:.3f} -> {ref.report['ir_after']:.4f})")
+
+    x, _ = W.token_rows(wl)
+    d = G.dev()
+    x_d = G.torch_rows(x, O.BF16)
+    buf = torch.empty((dg.rows, dg.hidden), dtype=torch.bfloat16, device=d)
+    mb.dispatch(dg, gp.bufs, x_d, buf)
+    gen = W.rows_bf16(wl.seed, W.TAG_YEXP, dg.hidden, n=G_ROWS)
+    gen_d = torch.from_numpy(gen).view(torch.bfloat16).to(d)
+    ye = gen_d[torch.arange(dg.rows, device=d) % G_ROWS]
+    w_d = torch.from_numpy(w).to(d)
+    y = torch.empty((dg.n_tokens, dg.hidden), dtype=torch.bfloat16, device=d)
+    mb.combine(dg, gp.bufs, ye, w_d, y)
+    torch.cuda.synchronize()
+    G.log(f"{name}: dispatch + combine ran")
+
+    hot = int(np.argmax(ref.load_pre))
+    for r in sorted({0, hot, wl.n_ranks - 1}):
+        r0, r1 = r * od.cap, (r + 1) * od.cap
+        win, _, _ = O.dispatch(od, ref, x, None, row0=r0, row1=r1)
+        got_win = G.rows_to_bytes(buf[r0:r1])
+        used = ref.row_src[r0:r1] >= 0
+        assert np.array_equal(got_win[used], win[used]), f"rank {r} region"
+    rng = np.random.default_rng(1)
+    rows = rng.choice(np.flatnonzero(ref.row_src >= 0), 2048, replace=False)
+    got_rows = G.rows_to_bytes(buf[torch.from_numpy(rows).to(d)])
+    exp_rows = x.view(np.uint8).reshape(wl.n_tokens, -1)[ref.row_src[rows]]
+    assert np.array_equal(got_rows, exp_rows)
+    G.log(f"{name}: dispatch rows bit-exact")
+
+    sample = np.sort(rng.choice(wl.n_tokens, 1024, replace=False))
+    pos_s = ref.pos[sample].astype(np.int64)
+    ye_s = gen[(pos_s % G_ROWS).ravel()]
+    cd = O.make_dims(len(sample), wl.top_k, wl.n_experts, 1, 0, wl.hidden, cap=1,
+                     dtype_in="bf16", dtype_out="bf16")
+    pos_c = np.arange(len(sample) * wl.top_k, dtype=np.int32).reshape(len(sample), wl.top_k)
+    y_ref, mag, _ = O.combine(cd, pos_c, np.zeros(4, np.int32), w[sample], ye_s)
+    y_got = G.y_to_f64(y[torch.from_numpy(sample).to(d)])
+    G.assert_combine_close(y_got, y_ref, mag, "bf16")
+    G.log(f"{name}: combine sample in tolerance")
+    del buf, ye, y, x_d
+    torch.cuda.empty_cache()

@@ -1,0 +1,209 @@
+"""Python binding of libmoebal (include/moebal.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every step of plan / dispatch / combine runs in the HIP
+kernels of ``libmoebal.so``. There is no fallback: importing this package
+fails if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoebal.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+TORCH_DTYPES = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8}
+ELT_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1}
+
+OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3
+ST_BAD_ID, ST_DUP_ID, ST_UNBALANCED, ST_CAPACITY = 1, 2, 4, 8
+ST_FATAL = ST_BAD_ID | ST_DUP_ID | ST_CAPACITY
+
+MAX_RANKS, MAX_EXPERTS, MAX_TOPK, MAX_SLOTS = 64, 1024, 32, 16
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+    )
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class Dims(ctypes.Structure):
+    """mb_dims."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_tokens", "top_k", "n_experts", "n_ranks", "slots_per_rank", "hidden", "cap",
+        "dtype_in", "dtype_out")]
+
+    @classmethod
+    def make(cls, n_tokens, top_k, n_experts, n_ranks, slots_per_rank, hidden, cap=None,
+             dtype_in="bf16", dtype_out="bf16") -> "Dims":
+        if cap is None:
+            cap = (n_tokens // n_ranks) * top_k if n_ranks else 0
+        di = DTYPES[dtype_in] if isinstance(dtype_in, str) else dtype_in
+        do = DTYPES[dtype_out] if isinstance(dtype_out, str) else dtype_out
+        return cls(n_tokens, top_k, n_experts, n_ranks, slots_per_rank, hidden, max(cap, 1), di, do)
+
+    @classmethod
+    def for_workload(cls, wl, cap=None, n_tokens=None) -> "Dims":
+        n = wl.n_tokens if n_tokens is None else n_tokens
+        return cls.make(n, wl.top_k, wl.n_experts, wl.n_ranks, wl.slots_per_rank, wl.hidden,
+                        cap=cap, dtype_in=wl.dtype_in, dtype_out=wl.dtype_out)
+
+    @property
+    def eh(self) -> int:
+        return self.n_experts // self.n_ranks
+
+    @property
+    def n_slots(self) -> int:
+        return self.eh + self.slots_per_rank
+
+    @property
+    def rows(self) -> int:
+        return self.n_ranks * self.cap
+
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class _PlanBufsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "counts", "load_pre", "load_post", "rep_expert", "slot_quota", "cu_seqlens", "pos",
+        "row_src", "status")]
+
+
+_vp = ctypes.c_void_p
+_lib.mb_version.restype = ctypes.c_int
+_lib.mb_strerror.argtypes = [ctypes.c_int]
+_lib.mb_strerror.restype = ctypes.c_char_p
+_lib.mb_plan_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+_lib.mb_plan_workspace_bytes.restype = ctypes.c_size_t
+_lib.mb_plan.argtypes = [ctypes.POINTER(Dims), _vp, _vp, ctypes.c_size_t,
+                         ctypes.POINTER(_PlanBufsC), _vp]
+_lib.mb_plan.restype = ctypes.c_int
+_lib.mb_dispatch.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_PlanBufsC), _vp, _vp, _vp,
+                             _vp, _vp]
+_lib.mb_dispatch.restype = ctypes.c_int
+_lib.mb_combine.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_PlanBufsC), _vp, _vp, _vp, _vp]
+_lib.mb_combine.restype = ctypes.c_int
+_lib.mb_plan_status.argtypes = [ctypes.POINTER(_PlanBufsC), _vp, _i32p]
+_lib.mb_plan_status.restype = ctypes.c_int
+
+EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan", "mb_dispatch",
+           "mb_combine", "mb_plan_status")
+
+
+class MoebalError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+def version() -> int:
+    return _lib.mb_version()
+
+
+def strerror(code: int) -> str:
+    return _lib.mb_strerror(code).decode()
+
+
+def workspace_bytes(dims: Dims) -> int:
+    return int(_lib.mb_plan_workspace_bytes(ctypes.byref(dims)))
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class PlanBuffers:
+    """Caller-owned device outputs of mb_plan (torch int32 tensors)."""
+
+    counts: torch.Tensor
+    load_pre: torch.Tensor
+    load_post: torch.Tensor
+    rep_expert: torch.Tensor
+    slot_quota: torch.Tensor
+    cu_seqlens: torch.Tensor
+    pos: torch.Tensor
+    row_src: torch.Tensor
+    status: torch.Tensor
+
+    @classmethod
+    def allocate(cls, dims: Dims, device) -> "PlanBuffers":
+        P, E, R, N, K = dims.n_ranks, dims.n_experts, dims.slots_per_rank, dims.n_tokens, dims.top_k
+        ns = dims.n_slots
+        z = lambda *s: torch.empty(s, dtype=torch.int32, device=device)  # noqa: E731
+        return cls(counts=z(P, E), load_pre=z(P), load_post=z(P), rep_expert=z(P, max(R, 1)),
+                   slot_quota=z(P, ns), cu_seqlens=z(P, ns + 1), pos=z(N, K),
+                   row_src=z(dims.rows), status=z(4))
+
+    def c_struct(self) -> _PlanBufsC:
+        return _PlanBufsC(*[self.__dict__[n].data_ptr() for n, _ in _PlanBufsC._fields_])
+
+
+def alloc_workspace(dims: Dims, device) -> torch.Tensor:
+    n = workspace_bytes(dims)
+    if n == 0:
+        raise MoebalError("mb_plan_workspace_bytes", ERR_INVALID_ARG)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, stream=None) -> None:
+    """mb_plan: enqueue the plan of one MoE layer call on `stream`."""
+    assert ids.dtype == torch.int32 and ids.is_contiguous()
+    rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), ws.numel(),
+                      ctypes.byref(bufs.c_struct()), _stream(stream))
+    if rc != OK:
+        raise MoebalError("mb_plan", rc)
+
+
+def dispatch(dims: Dims, bufs: PlanBuffers, x: torch.Tensor, buf: torch.Tensor,
+             x_scale: torch.Tensor | None = None, buf_scale: torch.Tensor | None = None,
+             stream=None) -> None:
+    """mb_dispatch: buf[pos[t][k]] = x[t] (and the fp8 scale rows)."""
+    assert x.is_contiguous() and buf.is_contiguous()
+    rc = _lib.mb_dispatch(ctypes.byref(dims), ctypes.byref(bufs.c_struct()), _ptr(x),
+                          _ptr(x_scale), _ptr(buf), _ptr(buf_scale), _stream(stream))
+    if rc != OK:
+        raise MoebalError("mb_dispatch", rc)
+
+
+def combine(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, w: torch.Tensor, y: torch.Tensor,
+            stream=None) -> None:
+    """mb_combine: y[t] = sum_k w[t][k] * y_exp[pos[t][k]] (fp32 accumulation)."""
+    assert y_exp.is_contiguous() and w.is_contiguous() and y.is_contiguous()
+    assert w.dtype == torch.float32
+    rc = _lib.mb_combine(ctypes.byref(dims), ctypes.byref(bufs.c_struct()), _ptr(y_exp), _ptr(w),
+                         _ptr(y), _stream(stream))
+    if rc != OK:
+        raise MoebalError("mb_combine", rc)
+
+
+def plan_status(bufs: PlanBuffers, stream=None):
+    """mb_plan_status: [flags, T, max load, moves] on the host (synchronises)."""
+    import numpy as np
+
+    out = (ctypes.c_int32 * 4)()
+    rc = _lib.mb_plan_status(ctypes.byref(bufs.c_struct()), _stream(stream), out)
+    if rc != OK:
+        raise MoebalError("mb_plan_status", rc)
+    return np.array(list(out), dtype=np.int32)
+
+
+def raw_call(fn: str, *args) -> int:
+    """Call an exported mb_* function with raw ctypes arguments (for tests of
+    the argument checks)."""
+    return getattr(_lib, fn)(*args)

@@ -1,0 +1,172 @@
+// api.hip — libmoebal's C ABI: argument checks, workspace layout, launches.
+// The operations and conventions are documented in include/moebal.h.
+#include <string.h>
+
+#include "mb_internal.h"
+
+namespace mb {
+
+Geometry geometry(const mb_dims& d) {
+  Geometry g;
+  g.S = d.n_tokens / d.n_ranks;
+  g.Eh = d.n_experts / d.n_ranks;
+  g.NS = g.Eh + d.slots_per_rank;
+  g.nbps = (g.S + kTokensPerBlock - 1) / kTokensPerBlock;
+  g.nblk = g.nbps * d.n_ranks;
+  // Water level T = ceil(N*K / P) (ISER-MoE, HALO-Q Objective 1).
+  g.T = (int32_t)(((int64_t)d.n_tokens * d.top_k + d.n_ranks - 1) / d.n_ranks);
+  return g;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const mb_dims& d, const Geometry& g) {
+  WsLayout L;
+  size_t off = 0;
+  const size_t per_block = (size_t)g.nblk * d.n_experts * sizeof(int32_t);
+  L.blockcnt = off;
+  off = align256(off + per_block);
+  L.blockoff = off;
+  off = align256(off + per_block);
+  L.blockflags = off;
+  off = align256(off + (size_t)g.nblk * sizeof(int32_t) + sizeof(int32_t));
+  L.expert_total = off;
+  off = align256(off + (size_t)d.n_experts * sizeof(int32_t));
+  L.pair_tab = off;
+  off = align256(off + (size_t)d.n_ranks * d.n_experts * sizeof(PairEntry));
+  L.host_list = off;
+  off = align256(off + (size_t)host_list_cap(d) * sizeof(HostEntry));
+  L.host_range = off;
+  off = align256(off + (size_t)d.n_experts * sizeof(int2));
+  L.total = off;
+  return L;
+}
+
+}  // namespace mb
+
+using namespace mb;
+
+static int validate(const mb_dims* d) {
+  if (!d) return MB_ERR_INVALID_ARG;
+  if (d->n_ranks < 1 || d->n_ranks > kMaxRanks) return MB_ERR_INVALID_ARG;
+  if (d->n_tokens < 0 || d->n_tokens % d->n_ranks) return MB_ERR_INVALID_ARG;
+  if (d->n_experts < 1 || d->n_experts > kMaxExperts || d->n_experts % d->n_ranks)
+    return MB_ERR_INVALID_ARG;
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > kMaxTopK) return MB_ERR_INVALID_ARG;
+  if (d->slots_per_rank < 0 || d->slots_per_rank > kMaxSlots) return MB_ERR_INVALID_ARG;
+  if (d->hidden < 1 || d->cap < 1) return MB_ERR_INVALID_ARG;
+  if ((int64_t)d->n_tokens * d->top_k > INT32_MAX) return MB_ERR_INVALID_ARG;
+  if ((int64_t)d->n_ranks * d->cap > INT32_MAX) return MB_ERR_INVALID_ARG;
+  const int64_t bin = elt_bytes(d->dtype_in);
+  if (!bin) return MB_ERR_INVALID_ARG;
+  if (d->dtype_out != MB_F32 && d->dtype_out != MB_BF16) return MB_ERR_INVALID_ARG;
+  if ((int64_t)d->hidden * bin % 16 || (int64_t)d->hidden * elt_bytes(d->dtype_out) % 16)
+    return MB_ERR_INVALID_ARG;
+  if ((int64_t)d->hidden * bin / 16 > INT32_MAX) return MB_ERR_INVALID_ARG;
+  if (d->dtype_in == MB_FP8_E4M3 && d->hidden % 128) return MB_ERR_INVALID_ARG;
+  return MB_OK;
+}
+
+// pos may be NULL only when there are no pairs (N == 0).
+static bool plan_ptrs_ok(const mb_dims* d, const mb_plan_bufs* o) {
+  return o && o->counts && o->load_pre && o->load_post && o->slot_quota && o->cu_seqlens &&
+         (o->pos || d->n_tokens == 0) && o->row_src && o->status;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" {
+
+int mb_version(void) { return MB_VERSION; }
+
+const char* mb_strerror(int code) {
+  switch (code) {
+    case MB_OK: return "ok";
+    case MB_ERR_INVALID_ARG: return "invalid argument (sizes outside the limits or null pointer)";
+    case MB_ERR_WORKSPACE: return "workspace smaller than mb_plan_workspace_bytes()";
+    case MB_ERR_HIP: return "HIP runtime error";
+    case MB_ST_BAD_ID: return "status: an expert id outside [0, E)";
+    case MB_ST_DUP_ID: return "status: a token lists one expert twice";
+    case MB_ST_UNBALANCED: return "status: placement stopped with a rank above the water level";
+    case MB_ST_CAPACITY: return "status: a rank needs more rows than cap";
+    default: return "unknown code";
+  }
+}
+
+size_t mb_plan_workspace_bytes(const mb_dims* dims) {
+  if (validate(dims) != MB_OK) return 0;
+  const Geometry g = geometry(*dims);
+  return ws_layout(*dims, g).total;
+}
+
+int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws_bytes,
+            const mb_plan_bufs* out, hipStream_t stream) {
+  int rc = validate(dims);
+  if (rc != MB_OK) return rc;
+  if (!plan_ptrs_ok(dims, out) || !ws_dev || (dims->n_tokens > 0 && !ids_dev) ||
+      (dims->slots_per_rank > 0 && !out->rep_expert) || !aligned16(ws_dev))
+    return MB_ERR_INVALID_ARG;
+  const Geometry g = geometry(*dims);
+  const WsLayout L = ws_layout(*dims, g);
+  if (ws_bytes < L.total) return MB_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  int32_t* blockcnt = reinterpret_cast<int32_t*>(ws + L.blockcnt);
+  int32_t* blockoff = reinterpret_cast<int32_t*>(ws + L.blockoff);
+  int32_t* blockflags = reinterpret_cast<int32_t*>(ws + L.blockflags);
+  PairEntry* pair_tab = reinterpret_cast<PairEntry*>(ws + L.pair_tab);
+  HostEntry* host_list = reinterpret_cast<HostEntry*>(ws + L.host_list);
+  int2* host_range = reinterpret_cast<int2*>(ws + L.host_range);
+  int32_t* expert_total = reinterpret_cast<int32_t*>(ws + L.expert_total);
+
+  // count -> per-source offsets and totals -> greedy placement -> lookup
+  // tables -> per-pair rows, all on `stream`, no host synchronisation.
+  if (launch_count(*dims, g, ids_dev, blockcnt, blockflags, stream) != hipSuccess) return MB_ERR_HIP;
+  if (launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
+    return MB_ERR_HIP;
+  if (launch_plan(*dims, g, *out, blockflags, expert_total, host_range, stream) != hipSuccess)
+    return MB_ERR_HIP;
+  if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
+    return MB_ERR_HIP;
+  if (launch_assign(*dims, g, ids_dev, blockoff, pair_tab, host_list, host_range, *out, stream) !=
+      hipSuccess)
+    return MB_ERR_HIP;
+  return MB_OK;
+}
+
+int mb_dispatch(const mb_dims* dims, const mb_plan_bufs* plan, const void* x_dev,
+                const float* x_scale_dev, void* buf_dev, float* buf_scale_dev,
+                hipStream_t stream) {
+  int rc = validate(dims);
+  if (rc != MB_OK) return rc;
+  if (!plan || (dims->n_tokens > 0 && (!plan->pos || !x_dev)) || !plan->status || !buf_dev)
+    return MB_ERR_INVALID_ARG;
+  if (!aligned16(x_dev) || !aligned16(buf_dev)) return MB_ERR_INVALID_ARG;
+  if (dims->dtype_in == MB_FP8_E4M3 && (!x_scale_dev || !buf_scale_dev)) return MB_ERR_INVALID_ARG;
+  return launch_dispatch(*dims, *plan, x_dev, x_scale_dev, buf_dev, buf_scale_dev, stream) ==
+                 hipSuccess
+             ? MB_OK
+             : MB_ERR_HIP;
+}
+
+int mb_combine(const mb_dims* dims, const mb_plan_bufs* plan, const void* y_exp_dev,
+               const float* w_dev, void* y_dev, hipStream_t stream) {
+  int rc = validate(dims);
+  if (rc != MB_OK) return rc;
+  if (!plan || !plan->status || !y_exp_dev ||
+      (dims->n_tokens > 0 && (!plan->pos || !w_dev || !y_dev)))
+    return MB_ERR_INVALID_ARG;
+  if (!aligned16(y_exp_dev) || !aligned16(y_dev)) return MB_ERR_INVALID_ARG;
+  return launch_combine(*dims, *plan, y_exp_dev, w_dev, y_dev, stream) == hipSuccess ? MB_OK
+                                                                                     : MB_ERR_HIP;
+}
+
+int mb_plan_status(const mb_plan_bufs* plan, hipStream_t stream, int32_t host_status[4]) {
+  if (!plan || !plan->status || !host_status) return MB_ERR_INVALID_ARG;
+  if (hipMemcpyAsync(host_status, plan->status, 4 * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess)
+    return MB_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MB_ERR_HIP;
+  return MB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// mb_internal.h — declarations shared by libmoebal's own translation units:
+// block geometry, workspace layout and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moebal.h"
+
+namespace mb {
+
+// Tokens handled by one routing workgroup: four wave64s, one token per lane.
+constexpr int kTokensPerBlock = 256;
+constexpr int kWaves = kTokensPerBlock / 64;
+
+constexpr int kMaxRanks = 64;     // one wave lane per logical rank in k_plan
+constexpr int kMaxExperts = 1024; // LDS: kWaves * E * 8 bytes of token masks
+constexpr int kMaxTopK = 32;
+constexpr int kMaxSlots = 16;
+
+// One entry per (source rank s, expert e), written by k_plan, read by
+// k_assign for every pair (s, e):
+//   x = local quota of s for e (0 when s holds no copy of e)
+//   y = first row of s's local pairs of e, absolute in the dispatch buffer
+//   z = (surplus pairs of e from ranks < s) - x, so that a surplus pair of
+//       stable rank rho has surplus index u = rho + z
+struct alignas(16) PairEntry {
+  int32_t local_quota;
+  int32_t local_base;
+  int32_t surplus_shift;
+  int32_t pad;
+};
+
+// Hosts of expert e that take surplus pairs, ascending rank, stored in a
+// compact list: expert e owns entries [host_range[e].x, host_range[e].x +
+// host_range[e].y); its capacity (1 + replicas of e) is fixed by k_plan.
+//   end  = surplus index one past this host's share
+//   base = dispatch row of surplus index 0 on this host (row - start index)
+//   rank = host rank
+//   lt   = local pairs this host keeps (they precede surplus from higher
+//          source ranks in token order)
+struct alignas(16) HostEntry {
+  int32_t end;
+  int32_t base;
+  int32_t rank;
+  int32_t lt;
+};
+
+struct Geometry {
+  int32_t S, Eh, NS;     // tokens per rank, home experts per rank, slots per rank
+  int32_t nbps, nblk;    // routing blocks per source rank, in total
+  int32_t T;             // water level ceil(N*K/P)
+};
+
+struct WsLayout {
+  size_t blockcnt, blockoff, blockflags, expert_total, pair_tab, host_list, host_range, total;
+};
+
+// Entries of the compact host list: one home per expert plus one per
+// replica slot.
+inline int host_list_cap(const mb_dims& d) { return d.n_experts + d.n_ranks * d.slots_per_rank; }
+
+Geometry geometry(const mb_dims& d);
+WsLayout ws_layout(const mb_dims& d, const Geometry& g);
+
+// Launchers (each returns hipSuccess or the launch error).
+hipError_t launch_count(const mb_dims& d, const Geometry& g, const int32_t* ids,
+                        int32_t* blockcnt, int32_t* blockflags, hipStream_t st);
+hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* blockcnt,
+                       int32_t* blockoff, int32_t* counts, int32_t* expert_total,
+                       hipStream_t st);
+hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
+                       const int32_t* blockflags, const int32_t* expert_total,
+                       int2* host_range, hipStream_t st);
+hipError_t launch_tables(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
+                         PairEntry* pair_tab, HostEntry* host_list, int2* host_range,
+                         hipStream_t st);
+hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids,
+                         const int32_t* blockoff, const PairEntry* pair_tab,
+                         const HostEntry* host_list, const int2* host_range,
+                         const mb_plan_bufs& o, hipStream_t st);
+hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* x,
+                           const float* x_scale, void* buf, float* buf_scale, hipStream_t st);
+hipError_t launch_combine(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
+                          const float* w, void* y, hipStream_t st);
+
+// Launch KERNEL<K> for the top-K values with a specialised kernel, KERNEL<0>
+// (runtime K) otherwise.
+#define MB_DISPATCH_TOPK(K, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                     \
+  do {                                                                                   \
+    switch (K) {                                                                         \
+      case 1: hipLaunchKernelGGL(KERNEL<1>, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__); break; \
+      case 2: hipLaunchKernelGGL(KERNEL<2>, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__); break; \
+      case 4: hipLaunchKernelGGL(KERNEL<4>, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__); break; \
+      case 8: hipLaunchKernelGGL(KERNEL<8>, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__); break; \
+      default: hipLaunchKernelGGL(KERNEL<0>, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__); break; \
+    }                                                                                    \
+  } while (0)
+
+inline int64_t elt_bytes(int32_t dtype) {
+  return dtype == MB_F32 ? 4 : dtype == MB_BF16 ? 2 : dtype == MB_FP8_E4M3 ? 1 : 0;
+}
+
+}  // namespace mb

@@ -1,0 +1,362 @@
+// plan.hip — the single-workgroup replica planner of libmoebal.
+//
+// One workgroup of 256 threads:
+//  1. routed pairs per expert c_e (summed over sources by k_scan);
+//  2. wave 0 runs the greedy with lane r = logical rank r (P <= 64): the
+//     busiest rank above the water level T gives a replica of its heaviest
+//     home expert to the least loaded rank below T that has a free slot and
+//     no copy yet, filling that rank up to T;
+//  3. all threads write slot quotas, cu_seqlens, loads and the status word.
+// The lookup tables that turn a pair's stable rank into its dispatch row are
+// built afterwards by k_tables (route.hip), one wave per expert.
+//
+// Every choice is made by full-wave DPP reductions followed by a ballot that
+// picks the lowest lane (or a per-lane scan in index order), so ties resolve
+// to the lowest rank / expert index and the result does not depend on timing.
+//
+// Sources: ISER-MoE, Methodology, HALO-Q Scheduler — Objective 1 (water
+// level T = ceil(sum L_r / P)), stage 2 (busiest rank's heaviest home expert
+// goes where a slot is free), stage 3 (smallest free helper index), stage 5
+// (surplus routes onto the hosts' spare quotas); Zepp summary §4.1 (R replica
+// slots per GPU); MoonEP, "What MoonEP enforces and how" (S*K rows per rank,
+// planner-made cu_seqlens) and "Implementation details" (home experts, then
+// prefetch slots, in one numbering).
+#include "mb_internal.h"
+#include "wave.h"
+
+namespace mb {
+namespace {
+
+struct PlanArgs {
+  int N, K, E, P, R, cap, Eh, NS, nblk, T;
+  const int32_t* expert_total;
+  const int32_t* blockflags;
+  int32_t* load_pre;
+  int32_t* load_post;
+  int32_t* rep_expert;
+  int32_t* slot_quota;
+  int32_t* cu_seqlens;
+  int32_t* status;
+  int2* host_range;
+};
+
+constexpr int kPlanThreads = 256;
+
+struct PlanSmem {
+  int32_t* c;       // [E] routed pairs per expert
+  int32_t* qh;      // [E] remaining home quota
+  int32_t* repE;    // [P*R] expert of replica slot, -1 empty
+  int32_t* repM;    // [P*R] quota of replica slot
+  int32_t* loadv;   // [64] load after planning
+  int32_t* lpre;    // [64] load before planning
+  int32_t* misc;    // [4] moves, unbalanced
+};
+
+__host__ __device__ inline size_t plan_smem_bytes(int E, int P, int R, int NS) {
+  return sizeof(int32_t) * (2 * (size_t)E + 2 * (size_t)P * R + 64 + 64 + 4);
+}
+
+__device__ inline PlanSmem carve(uint8_t* base, int E, int P, int R, int NS) {
+  PlanSmem m;
+  int32_t* p = reinterpret_cast<int32_t*>(base);
+  m.c = p;
+  p += E;
+  m.qh = p;
+  p += E;
+  m.repE = p;
+  p += P * R;
+  m.repM = p;
+  p += P * R;
+  m.loadv = p;
+  p += 64;
+  m.lpre = p;
+  p += 64;
+  m.misc = p;
+  return m;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Greedy placement, run by the 64 lanes of wave 0 (lane = rank).
+//
+// A move gives its destination min(T - load, remaining home quota) pairs, so
+// a rank that receives a replica of an expert either ends at T or exhausts
+// that expert's home quota, and a rank at or below T never sheds. Hence, for
+// an expert with home quota left, every holder other than its home is at T:
+// no open rank (load below T, slot free) holds it, and the destination of a
+// move is the least loaded open rank whatever expert the busiest rank gives.
+// A step is then two independent wave reductions over the loads (busiest
+// rank, least loaded open rank) plus reads of the busiest rank's heaviest
+// expert, which each rank lane keeps up to date in registers.
+//
+// EHM >= Eh: registers per lane for the home quotas of its rank.
+template <int EHM>
+__device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
+  const int lane = threadIdx.x;
+  const int P = a.P, R = a.R, Eh = a.Eh, T = a.T;
+  const bool rank_lane = lane < P;
+  int q[EHM];
+  int load = 0;
+#pragma unroll
+  for (int j = 0; j < EHM; ++j) {
+    q[j] = (rank_lane && j < Eh) ? m.c[lane * Eh + j] : 0;
+    load += q[j];
+  }
+  // Heaviest remaining home expert of this rank, lowest index on ties.
+  auto best = [&](int& bq, int& bj) {
+    bq = -1;
+    bj = 0;
+#pragma unroll
+    for (int j = 0; j < EHM; ++j)
+      if (q[j] > bq) {
+        bq = q[j];
+        bj = j;
+      }
+  };
+  int bq, bj;
+  best(bq, bj);
+  const int lpre = load;
+  int used = 0, moves = 0, unbalanced = 0;
+
+  for (;;) {
+    const bool open_lane = rank_lane && used < R && load < T;
+    int lmax, lmin;
+    wave_max_min_i32(rank_lane ? load : INT32_MIN, open_lane ? load : INT32_MAX, lmax, lmin);
+    if (lmax <= T) break;
+    if (lmin == INT32_MAX) {  // no open rank
+      unbalanced = 1;
+      break;
+    }
+    const int rs = lowest_lane(ballot64(rank_lane && load == lmax));
+    const int d = lowest_lane(ballot64(open_lane && load == lmin));
+    const int qmax = __builtin_amdgcn_readlane(bq, rs);
+    const int jb = __builtin_amdgcn_readlane(bj, rs);
+    const int slot = __builtin_amdgcn_readlane(used, d);  // slots fill in index order
+    const int mv = min(T - lmin, qmax);
+    const int e = rs * Eh + jb;
+    if (lane == 0) {
+      m.repE[d * R + slot] = e;
+      m.repM[d * R + slot] = mv;
+    }
+    if (lane == rs) {
+      load -= mv;
+#pragma unroll
+      for (int j = 0; j < EHM; ++j)
+        if (j == jb) q[j] -= mv;
+      best(bq, bj);
+    }
+    if (lane == d) {
+      load += mv;
+      used += 1;
+    }
+    ++moves;
+  }
+  if (rank_lane) {
+#pragma unroll
+    for (int j = 0; j < EHM; ++j)
+      if (j < Eh) m.qh[lane * Eh + j] = q[j];
+    m.loadv[lane] = load;
+    m.lpre[lane] = lpre;
+  }
+  if (lane == 0) {
+    m.misc[0] = moves;
+    m.misc[1] = unbalanced;
+  }
+}
+
+// The same greedy for ranks with more home experts than fit in registers:
+// home quotas stay in LDS and the heaviest expert of the busiest rank is a
+// wave reduction per step.
+__device__ void greedy_lds(const PlanArgs& a, PlanSmem& m) {
+  const int lane = threadIdx.x;
+  const int P = a.P, R = a.R, Eh = a.Eh, T = a.T;
+  const bool rank_lane = lane < P;
+  int load = 0;
+  if (rank_lane)
+    for (int i = 0; i < Eh; ++i) load += m.c[lane * Eh + i];
+  const int lpre = load;
+  int used = 0, moves = 0, unbalanced = 0;
+  for (;;) {
+    const bool open_lane = rank_lane && used < R && load < T;
+    const int lmax = wave_max_i32(rank_lane ? load : INT32_MIN);
+    const int lmin = wave_min_i32(open_lane ? load : INT32_MAX);
+    if (lmax <= T) break;
+    if (lmin == INT32_MAX) {
+      unbalanced = 1;
+      break;
+    }
+    const int rs = lowest_lane(ballot64(rank_lane && load == lmax));
+    const int d = lowest_lane(ballot64(open_lane && load == lmin));
+    int myq = 0, myj = INT32_MAX;
+    for (int j = lane; j < Eh; j += 64) {
+      const int qq = m.qh[rs * Eh + j];
+      if (qq > myq) {
+        myq = qq;
+        myj = j;
+      }
+    }
+    const int qmax = wave_max_i32(myq);
+    const int jb = wave_min_i32(myq == qmax ? myj : INT32_MAX);
+    const int e = rs * Eh + jb;
+    const int slot = __builtin_amdgcn_readlane(used, d);
+    const int mv = min(T - lmin, qmax);
+    if (lane == 0) {
+      m.qh[e] = qmax - mv;
+      m.repE[d * R + slot] = e;
+      m.repM[d * R + slot] = mv;
+    }
+    if (lane == rs) load -= mv;
+    if (lane == d) {
+      load += mv;
+      used += 1;
+    }
+    ++moves;
+    wave_lds_sync();
+  }
+  if (rank_lane) {
+    m.loadv[lane] = load;
+    m.lpre[lane] = lpre;
+  }
+  if (lane == 0) {
+    m.misc[0] = moves;
+    m.misc[1] = unbalanced;
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int E = a.E, P = a.P, R = a.R, Eh = a.Eh, NS = a.NS;
+  PlanSmem m = carve(smem, E, P, R, NS);
+
+  // Status bits of the routing decisions.
+  int fl = 0;
+  for (int i = tid; i < a.nblk; i += kPlanThreads) fl |= a.blockflags[i];
+  const int bad = __syncthreads_or(fl & MB_ST_BAD_ID);
+  const int dup = __syncthreads_or(fl & MB_ST_DUP_ID);
+  if (bad || dup) {
+    if (tid == 0) {
+      a.status[0] = (bad ? MB_ST_BAD_ID : 0) | (dup ? MB_ST_DUP_ID : 0);
+      a.status[1] = a.T;
+      a.status[2] = 0;
+      a.status[3] = 0;
+    }
+    return;
+  }
+
+  // c_e (summed over sources by k_scan); initial quotas and holders.
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int c = a.expert_total[e];
+    m.c[e] = c;
+    m.qh[e] = c;
+  }
+  for (int i = tid; i < P * R; i += kPlanThreads) {
+    m.repE[i] = -1;
+    m.repM[i] = 0;
+  }
+  __syncthreads();
+
+  if (tid < 64) {
+    if (Eh <= 4)
+      greedy_regs<4>(a, m);
+    else if (Eh <= 8)
+      greedy_regs<8>(a, m);
+    else if (Eh <= 16)
+      greedy_regs<16>(a, m);
+    else if (Eh <= 32)
+      greedy_regs<32>(a, m);
+    else
+      greedy_lds(a, m);
+  }
+  __syncthreads();
+
+  // Slot quotas, cu_seqlens and loads, one thread per rank.
+  for (int r = tid; r < P; r += kPlanThreads) {
+    int acc = 0;
+    a.cu_seqlens[r * (NS + 1)] = 0;
+    for (int i = 0; i < NS; ++i) {
+      const int q = i < Eh ? m.qh[r * Eh + i] : m.repM[r * R + (i - Eh)];
+      a.slot_quota[r * NS + i] = q;
+      acc += q;
+      a.cu_seqlens[r * (NS + 1) + i + 1] = acc;
+    }
+    a.load_pre[r] = m.lpre[r];
+    a.load_post[r] = m.loadv[r];
+  }
+  for (int i = tid; i < P * R; i += kPlanThreads) a.rep_expert[i] = m.repE[i];
+  int mymax = 0;
+  for (int r = tid; r < P; r += kPlanThreads) mymax = max(mymax, m.loadv[r]);
+  if (tid < 64) {
+    const int mx = wave_max_i32(mymax);
+    if (tid == 0) m.misc[2] = mx;
+  }
+  // Compact host-list ranges: expert e gets 1 + (replicas of e) entries,
+  // offsets by a block-wide exclusive scan in expert order.
+  for (int e = tid; e < E; e += kPlanThreads) m.c[e] = 1;
+  __syncthreads();
+  for (int i = tid; i < P * R; i += kPlanThreads)
+    if (m.repE[i] >= 0) atomicAdd(&m.c[m.repE[i]], 1);
+  __syncthreads();
+  const int per = (E + kPlanThreads - 1) / kPlanThreads;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) local += m.c[e];
+  }
+  const int incl = wave_inclusive_sum(local);
+  if ((tid & 63) == 63) m.lpre[tid >> 6] = incl;  // per-wave totals (lpre is free now)
+  const int max_load = m.misc[2];
+  __syncthreads();
+  int before = incl - local;
+  for (int w = 0; w < (tid >> 6); ++w) before += m.lpre[w];
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < E) {
+      a.host_range[e] = make_int2(before, 0);
+      before += m.c[e];
+    }
+  }
+  const bool over_cap = max_load > a.cap;
+  if (tid == 0) {
+    a.status[0] = (m.misc[1] ? MB_ST_UNBALANCED : 0) | (over_cap ? MB_ST_CAPACITY : 0);
+    a.status[1] = a.T;
+    a.status[2] = max_load;
+    a.status[3] = m.misc[0];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
+                       const int32_t* blockflags, const int32_t* expert_total,
+                       int2* host_range, hipStream_t st) {
+  PlanArgs a;
+  a.N = d.n_tokens;
+  a.K = d.top_k;
+  a.E = d.n_experts;
+  a.P = d.n_ranks;
+  a.R = d.slots_per_rank;
+  a.cap = d.cap;
+  a.Eh = g.Eh;
+  a.NS = g.NS;
+  a.nblk = g.nblk;
+  a.T = g.T;
+  a.expert_total = expert_total;
+  a.blockflags = blockflags;
+  a.load_pre = o.load_pre;
+  a.load_post = o.load_post;
+  a.rep_expert = o.rep_expert;
+  a.slot_quota = o.slot_quota;
+  a.cu_seqlens = o.cu_seqlens;
+  a.status = o.status;
+  a.host_range = host_range;
+  const size_t shmem = plan_smem_bytes(a.E, a.P, a.R, a.NS);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), shmem, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace mb

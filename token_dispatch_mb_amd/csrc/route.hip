@@ -1,0 +1,344 @@
+// route.hip — counting, per-source prefix offsets and the per-pair
+// assignment of libmoebal's plan.
+//
+// Stable ranks without atomics deciding order. A routing workgroup owns 256
+// consecutive tokens of one source rank (one token per lane). Each wave64
+// builds, in LDS, one 64-bit mask per expert whose bit l says "lane l's token
+// routes to this expert" (ds_or_b64: commutative, so the masks do not depend
+// on timing). A pair's rank among the earlier pairs of its (source rank,
+// expert) is then
+//   rho = (pairs in earlier workgroups of the same source, from k_scan)
+//       + popcount of the masks of earlier waves
+//       + popcount of its own wave's mask below its lane (mbcnt).
+// Tokens list distinct experts, so "earlier pair with the same expert" and
+// "earlier token with that expert" coincide.
+//
+// Sources: ISER-MoE, HALO-Q stage 1 (route counts per rank) and stage 5
+// (local-first rewrite of surplus routes onto the hosts' spare quotas);
+// Zepp summary §4.1, eq. (1) (demand d_i^e per source GPU, locality-preferred
+// routing); MoonEP, "What MoonEP enforces and how" (fixed per-rank regions
+// indexed by cu_seqlens).
+#include "mb_internal.h"
+#include "wave.h"
+
+namespace mb {
+namespace {
+
+// Sets this lane's bit in the wave's mask of each of its token's experts and
+// returns the token's status bits (bad or repeated ids).
+template <int KT>
+__device__ __forceinline__ int mark_token(const int32_t* __restrict__ row, int K_, int E,
+                                          unsigned long long* wmask, int lane) {
+  const int K = KT ? KT : K_;
+  int flags = 0;
+  for (int k = 0; k < K; ++k) {
+    const int e = row[k];
+    for (int k2 = 0; k2 < k; ++k2)
+      if (row[k2] == e) flags |= MB_ST_DUP_ID;
+    if ((unsigned)e >= (unsigned)E) {
+      flags |= MB_ST_BAD_ID;
+      continue;
+    }
+    atomicOr(&wmask[e], 1ull << lane);
+  }
+  return flags;
+}
+
+template <int KT>
+__global__ __launch_bounds__(kTokensPerBlock) void k_count(
+    const int32_t* __restrict__ ids, int K_, int E, int S, int nbps,
+    int32_t* __restrict__ blockcnt, int32_t* __restrict__ blockflags) {
+  extern __shared__ unsigned long long masks[];  // [kWaves][E]
+  const int K = KT ? KT : K_;
+  const int b = blockIdx.x;
+  const int s = b / nbps, j = b - s * nbps;
+  const int tl = threadIdx.x;
+  const int nt = min(kTokensPerBlock, S - j * kTokensPerBlock);
+  for (int i = tl; i < kWaves * E; i += kTokensPerBlock) masks[i] = 0ull;
+  __syncthreads();
+  const int w = tl >> 6, lane = tl & 63;
+  int flags = 0;
+  if (tl < nt) {
+    const size_t t = (size_t)s * S + (size_t)j * kTokensPerBlock + tl;
+    flags = mark_token<KT>(ids + t * K, K, E, masks + w * E, lane);
+  }
+  const int bad = __syncthreads_or(flags & MB_ST_BAD_ID);
+  const int dup = __syncthreads_or(flags & MB_ST_DUP_ID);
+  for (int e = tl; e < E; e += kTokensPerBlock) {
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) c += __popcll(masks[ww * E + e]);
+    blockcnt[(size_t)b * E + e] = c;
+  }
+  if (tl == 0) blockflags[b] = (bad ? MB_ST_BAD_ID : 0) | (dup ? MB_ST_DUP_ID : 0);
+}
+
+// Exclusive scan over the workgroups of each source rank, per expert; the
+// per-source totals d[s][e]; and c_e = sum_s d[s][e]. A workgroup covers
+// 256 / P experts for all P sources (thread = (source, expert)), so c_e is
+// a reduction inside the workgroup.
+__global__ __launch_bounds__(256) void k_scan(const int32_t* __restrict__ blockcnt, int E, int P,
+                                               int nbps, int32_t* __restrict__ blockoff,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ expert_total) {
+  __shared__ int32_t part[256];
+  const int epw = 256 / P;
+  const int tid = threadIdx.x;
+  const int s = tid / epw, el = tid - s * epw;
+  const int e = blockIdx.x * epw + el;
+  int off = 0;
+  if (s < P && e < E) {
+    const size_t b0 = (size_t)s * nbps;
+    int j = 0;
+    for (; j + 8 <= nbps; j += 8) {
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = blockcnt[(b0 + j + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        blockoff[(b0 + j + i) * E + e] = off;
+        off += c[i];
+      }
+    }
+    for (; j < nbps; ++j) {
+      const int c = blockcnt[(b0 + j) * E + e];
+      blockoff[(b0 + j) * E + e] = off;
+      off += c;
+    }
+    counts[(size_t)s * E + e] = off;
+  }
+  part[tid] = off;
+  __syncthreads();
+  if (tid < epw && blockIdx.x * epw + tid < E) {
+    int c = 0;
+    for (int q = 0; q < P; ++q) c += part[q * epw + tid];
+    expert_total[blockIdx.x * epw + tid] = c;
+  }
+}
+
+// Dispatch row of every pair, and the token of every row (-1 for padding).
+// The workgroup stages in LDS its rows of the offset and pair tables and,
+// when it fits (kStageHosts), the whole compact host list.
+template <int KT, bool kStageHosts>
+__global__ __launch_bounds__(kTokensPerBlock) void k_assign(
+    const int32_t* __restrict__ ids, int K_, int E, int S, int P, int nbps, int nblk, int cap,
+    int nhost, const int32_t* __restrict__ blockoff, const PairEntry* __restrict__ pair_tab,
+    const HostEntry* __restrict__ host_list, const int2* __restrict__ host_range,
+    const int32_t* __restrict__ status, const int32_t* __restrict__ load_post,
+    int32_t* __restrict__ pos, int32_t* __restrict__ row_src) {
+  // LDS: masks [kWaves][E] | offsets [E] | pairs [E] | ranges [E] | hosts [nhost]
+  extern __shared__ unsigned long long masks[];
+  if (status[0] & MB_ST_FATAL) return;
+  const int K = KT ? KT : K_;
+  const int b = blockIdx.x;
+  const int tl = threadIdx.x;
+
+  // Padding rows: region r has rows [r*cap + load_post[r], (r+1)*cap).
+  // With every region full (a balanced plan at cap = T) there are none.
+  __shared__ int32_t lp_s[kMaxRanks];
+  int pad = 0;
+  if (tl < P) {
+    lp_s[tl] = load_post[tl];
+    pad = cap - lp_s[tl];
+  }
+  if (__syncthreads_or(pad > 0)) {
+    for (int r = 0; r < P; ++r) {
+      const int lp = lp_s[r];
+      for (int i = b * kTokensPerBlock + tl; i < cap - lp; i += gridDim.x * kTokensPerBlock)
+        row_src[r * cap + lp + i] = -1;
+    }
+  }
+  if (b >= nblk) return;
+
+  const int s = b / nbps, j = b - s * nbps;
+  const int nt = min(kTokensPerBlock, S - j * kTokensPerBlock);
+  const int E4 = (E + 3) & ~3;
+  int32_t* boff = reinterpret_cast<int32_t*>(masks + kWaves * E);
+  PairEntry* ptab = reinterpret_cast<PairEntry*>(boff + E4);
+  int2* hrange = reinterpret_cast<int2*>(ptab + E);
+  HostEntry* hl = reinterpret_cast<HostEntry*>(hrange + E4);
+  for (int i = tl; i < E; i += kTokensPerBlock) {
+    boff[i] = blockoff[(size_t)b * E + i];
+    ptab[i] = pair_tab[(size_t)s * E + i];
+    hrange[i] = host_range[i];
+  }
+  if constexpr (kStageHosts)
+    for (int i = tl; i < nhost; i += kTokensPerBlock) hl[i] = host_list[i];
+  const HostEntry* hosts = kStageHosts ? hl : host_list;
+  for (int i = tl; i < kWaves * E; i += kTokensPerBlock) masks[i] = 0ull;
+  const int w = tl >> 6, lane = tl & 63;
+  const size_t t = (size_t)s * S + (size_t)j * kTokensPerBlock + tl;
+  const int32_t* row = ids + t * K;
+  __syncthreads();
+  if (tl < nt) mark_token<KT>(row, K, E, masks + w * E, lane);
+  __syncthreads();
+  if (tl >= nt) return;
+
+  const int rows = P * cap;
+  auto rank_of = [&](int e) {
+    int rho = boff[e];
+    for (int ww = 0; ww < w; ++ww) rho += __popcll(masks[ww * E + e]);
+    return rho + lanes_below(masks[w * E + e]);
+  };
+  // Pass 1 keeps the first local_quota pairs of (s, e) on s; a later pair is
+  // surplus number u of e and goes to the host whose share covers u.
+  auto row_of = [&](int e, int rho) {
+    const PairEntry pe = ptab[e];
+    if (rho < pe.local_quota) return pe.local_base + rho;
+    const int u = rho + pe.surplus_shift;
+    const int2 rg = hrange[e];
+    for (int q = 0; q < rg.y; ++q) {
+      const HostEntry h = hosts[rg.x + q];
+      if (u < h.end) return h.base + u + (h.rank < s ? h.lt : 0);
+    }
+    return -1;
+  };
+  if constexpr (KT > 0) {
+    int er[KT], rho[KT], p[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) er[k] = row[k];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) rho[k] = rank_of(er[k]);
+#pragma unroll
+    for (int k = 0; k < KT; ++k) p[k] = row_of(er[k], rho[k]);
+#pragma unroll
+    for (int k = 0; k < KT; ++k) pos[t * K + k] = p[k];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+      if ((unsigned)p[k] < (unsigned)rows) row_src[p[k]] = (int32_t)t;
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const int e = row[k];
+      const int p = row_of(e, rank_of(e));
+      pos[t * K + k] = p;
+      if ((unsigned)p < (unsigned)rows) row_src[p] = (int32_t)t;
+    }
+  }
+}
+
+// Lookup tables of k_assign, one wave per expert e, lane = source rank s:
+//   pass 1 keeps min(d[s][e], quota of s) pairs on each holder s; the
+//   remaining (surplus) pairs, in token order, fill the holders' spare quota
+//   in ascending rank order. Prefix sums over s are wave scans.
+__global__ __launch_bounds__(256) void k_tables(
+    int E, int P, int R, int Eh, int NS, int cap, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ rep_expert, const int32_t* __restrict__ slot_quota,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ status,
+    PairEntry* __restrict__ pair_tab, HostEntry* __restrict__ host_list,
+    int2* __restrict__ host_range) {
+  if (status[0] & MB_ST_FATAL) return;
+  const int e = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (e >= E) return;
+  const int s = threadIdx.x & 63;
+  const bool valid = s < P;
+  const int home = e / Eh;
+  int d = 0, slot = -1, lq = 0, rowbase = 0;
+  if (valid) {
+    d = counts[(size_t)s * E + e];
+    if (s == home) {
+      slot = e - s * Eh;
+    } else {
+      for (int q = 0; q < R; ++q)
+        if (rep_expert[s * R + q] == e) slot = Eh + q;
+    }
+    if (slot >= 0) {
+      lq = slot_quota[s * NS + slot];
+      rowbase = s * cap + cu_seqlens[s * (NS + 1) + slot];
+    }
+  }
+  const int lt = min(d, lq);
+  const int sur = d - lt, sp = lq - lt;
+  const int sur_before = wave_inclusive_sum(sur) - sur;
+  const int sp_before = wave_inclusive_sum(sp) - sp;
+  if (valid) {
+    PairEntry pe;
+    pe.local_quota = lq;
+    pe.local_base = slot >= 0 ? rowbase + min(max(sur_before - sp_before, 0), sp) : 0;
+    pe.surplus_shift = sur_before - lq;
+    pe.pad = 0;
+    pair_tab[(size_t)s * E + e] = pe;
+  }
+  const uint64_t hb = ballot64(valid && sp > 0);
+  const int off = host_range[e].x;  // set by k_plan
+  if (valid && sp > 0) {
+    HostEntry h;
+    h.end = sp_before + sp;
+    h.base = rowbase - sp_before;
+    h.rank = s;
+    h.lt = lt;
+    host_list[off + lanes_below(hb)] = h;
+  }
+  if (s == 0) host_range[e].y = __popcll(hb);
+}
+
+}  // namespace
+
+
+hipError_t launch_count(const mb_dims& d, const Geometry& g, const int32_t* ids,
+                        int32_t* blockcnt, int32_t* blockflags, hipStream_t st) {
+  if (g.nblk == 0) return hipSuccess;
+  const size_t shmem = sizeof(unsigned long long) * kWaves * d.n_experts;
+  MB_DISPATCH_TOPK(d.top_k, k_count, dim3(g.nblk), dim3(kTokensPerBlock), shmem, st, ids,
+                   d.top_k, d.n_experts, g.S, g.nbps, blockcnt, blockflags);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* blockcnt,
+                       int32_t* blockoff, int32_t* counts, int32_t* expert_total,
+                       hipStream_t st) {
+  const int epw = 256 / d.n_ranks;
+  hipLaunchKernelGGL(k_scan, dim3((d.n_experts + epw - 1) / epw), dim3(256), 0, st, blockcnt,
+                     d.n_experts, d.n_ranks, g.nbps, blockoff, counts, expert_total);
+  return hipGetLastError();
+}
+
+hipError_t launch_tables(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
+                         PairEntry* pair_tab, HostEntry* host_list, int2* host_range,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_tables, dim3((d.n_experts + 3) / 4), dim3(256), 0, st, d.n_experts,
+                     d.n_ranks, d.slots_per_rank, g.Eh, g.NS, d.cap, o.counts, o.rep_expert,
+                     o.slot_quota, o.cu_seqlens, o.status, pair_tab, host_list, host_range);
+  return hipGetLastError();
+}
+
+hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids,
+                         const int32_t* blockoff, const PairEntry* pair_tab,
+                         const HostEntry* host_list, const int2* host_range,
+                         const mb_plan_bufs& o, hipStream_t st) {
+  const int64_t rows = (int64_t)d.n_ranks * d.cap;
+  int grid = g.nblk;
+  const int64_t pad_blocks = (rows + kTokensPerBlock - 1) / kTokensPerBlock;
+  if (grid == 0) grid = (int)(pad_blocks < 1024 ? pad_blocks : 1024);
+  if (grid < 1) grid = 1;
+  const int E4 = (d.n_experts + 3) & ~3;
+  const int nhost = host_list_cap(d);
+  const size_t base = sizeof(unsigned long long) * kWaves * d.n_experts +
+                      sizeof(int32_t) * E4 + sizeof(PairEntry) * d.n_experts + sizeof(int2) * E4;
+  const size_t with_hosts = base + sizeof(HostEntry) * nhost;
+  const bool stage = with_hosts <= 60 * 1024;
+  const size_t shmem = stage ? with_hosts : base;
+#define MB_A(KT)                                                                            \
+  do {                                                                                      \
+    if (stage)                                                                              \
+      hipLaunchKernelGGL((k_assign<KT, true>), dim3(grid), dim3(kTokensPerBlock), shmem, st, \
+                         ids, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps, g.nblk, d.cap,  \
+                         nhost, blockoff, pair_tab, host_list, host_range, o.status,        \
+                         o.load_post, o.pos, o.row_src);                                    \
+    else                                                                                    \
+      hipLaunchKernelGGL((k_assign<KT, false>), dim3(grid), dim3(kTokensPerBlock), shmem, st, \
+                         ids, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps, g.nblk, d.cap,  \
+                         nhost, blockoff, pair_tab, host_list, host_range, o.status,        \
+                         o.load_post, o.pos, o.row_src);                                    \
+  } while (0)
+  switch (d.top_k) {
+    case 1: MB_A(1); break;
+    case 2: MB_A(2); break;
+    case 4: MB_A(4); break;
+    case 8: MB_A(8); break;
+    default: MB_A(0); break;
+  }
+#undef MB_A
+  return hipGetLastError();
+}
+
+}  // namespace mb

@@ -1,0 +1,300 @@
+// rows.hip — row dispatch (scatter) and combine (weighted gather-reduce).
+//
+// Both kernels are HBM-bound byte movers: one wave64 per token, every lane
+// moving 16-byte chunks (global_load/store_dwordx4) with a whole row piece
+// (up to 16 KiB per wave) in flight at once. The cache hint of each access
+// (temporal or nontemporal) is the one measured fastest on MI355X for that
+// kernel's traffic mix; see the comment at each kernel.
+//
+// Dispatch reads each token row once and stores it to its K rows (the
+// one-GPU form of "a token's experts on one node share a transfer" in the
+// Zepp summary §4.2, Merge). Combine reads the K expert-output rows of a
+// token, accumulates w[t][k] * row in fp32 in k order and stores the result
+// once.
+//
+// Sources: MoonEP, "What MoonEP enforces and how" (tokens written straight
+// into fixed-shape expert-grouped buffers, kernels indexing rows through the
+// planner's layout); Zepp summary §4.2 (Merge: dispatch shares a token's
+// transfer, combine aggregates a token's expert outputs).
+#include "mb_internal.h"
+
+namespace mb {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowThreads = 256;
+constexpr int kTokensPerRowBlock = kRowThreads / 64;
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A row is moved in pieces of CPL 16-byte chunks per lane (CPL * 1 KiB per
+// wave). When the row is exactly CPL * 1 KiB long the whole row sits in
+// registers and no access needs a bounds check.
+template <bool kChecked, int CPL>
+__device__ __forceinline__ void load_piece(u32x4 (&v)[CPL], const u32x4* __restrict__ src,
+                                           int c0, int rb16, bool nt) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int i = c0 + c * 64;
+    if (!kChecked || i < rb16) v[c] = nt ? __builtin_nontemporal_load(src + i) : src[i];
+  }
+}
+
+// Dispatch: one wave per token. Measured on MI355X, plain (temporal) loads
+// and stores move this 1-read / K-write pattern faster than nontemporal ones.
+template <int CPL, bool kExact>
+__global__ __launch_bounds__(kRowThreads) void k_dispatch(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ status, u32x4* __restrict__ buf, int N, int K, int rb16,
+    int rows, const float* __restrict__ xs, float* __restrict__ bs, int nsc) {
+  const int lane = threadIdx.x & 63;
+  const int t = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  if (t >= N) return;
+  if (status[0] & MB_ST_FATAL) return;
+  const u32x4* src = x + (size_t)t * rb16;
+  const int32_t* pt = pos + (size_t)t * K;
+  for (int c0 = lane; c0 < rb16; c0 += CPL * 64) {
+    u32x4 v[CPL];
+    load_piece<!kExact, CPL>(v, src, c0, rb16, false);
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if ((unsigned)p >= (unsigned)rows) continue;
+      u32x4* dst = buf + (size_t)p * rb16;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int i = c0 + c * 64;
+        if (kExact || i < rb16) dst[i] = v[c];
+      }
+    }
+  }
+  for (int i = lane; i < nsc; i += 64) {
+    const float v = xs[(size_t)t * nsc + i];
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if ((unsigned)p < (unsigned)rows) bs[(size_t)p * nsc + i] = v;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (b >> 16) | 0x40u;  // quiet NaN
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// acc[0..7] += w * (8 bf16 of v), or acc[0..3] += w * (4 f32 of v).
+template <bool kBF16>
+__device__ __forceinline__ void fma_row(float* acc, float w, u32x4 v) {
+  if constexpr (kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xffff0000u), acc[2 * i + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, __uint_as_float(v[i]), acc[i]);
+  }
+}
+
+template <bool kBF16>
+__device__ __forceinline__ u32x4 pack_row(const float* acc) {
+  u32x4 o;
+  if constexpr (kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+  }
+  return o;
+}
+
+// The whole row (CPL * 1 KiB) of one token, every row valid: straight-line
+// code, so the compiler issues all K * CPL loads before the first FMA.
+template <int KT, int CPL, bool kBF16>
+__device__ __forceinline__ void combine_whole_row(const u32x4* __restrict__ ye, const int (&p)[KT],
+                                                  const float* __restrict__ wt,
+                                                  u32x4* __restrict__ dst, int lane, int rb16) {
+  constexpr int EPC = kBF16 ? 8 : 4;
+  float acc[CPL][EPC];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) acc[c][i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    const u32x4* src = ye + (size_t)p[k] * rb16 + lane;
+    const float wk = wt[k];
+    u32x4 v[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = __builtin_nontemporal_load(src + c * 64);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) fma_row<kBF16>(acc[c], wk, v[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(pack_row<kBF16>(acc[c]), dst + lane + c * 64);
+}
+
+// Combine: one wave per token; a piece of the row keeps fp32 accumulators
+// in registers while the K expert rows stream through in k order. With a
+// compile-time K and every row inside the buffer, the loads of all K rows
+// are issued before the first FMA. Nontemporal loads and stores measured
+// fastest for this K-read / 1-write pattern on MI355X.
+template <int KT, int CPL, bool kExact, bool kBF16>
+__global__ __launch_bounds__(kRowThreads) void k_combine(
+    const u32x4* __restrict__ ye, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    const int32_t* __restrict__ status, u32x4* __restrict__ y, int N, int K_, int rb16,
+    int rows) {
+  constexpr int EPC = kBF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int K = KT ? KT : K_;
+  const int lane = threadIdx.x & 63;
+  const int t = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  if (t >= N) return;
+  if (status[0] & MB_ST_FATAL) return;
+  u32x4* dst = y + (size_t)t * rb16;
+  const int32_t* pt = pos + (size_t)t * K;
+  const float* wt = w + (size_t)t * K;
+
+  if constexpr (KT > 0) {
+    int p[KT];
+    bool all_ok = true;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      p[k] = pt[k];
+      all_ok &= (unsigned)p[k] < (unsigned)rows;
+    }
+    if (all_ok) {
+      if constexpr (kExact) {
+        combine_whole_row<KT, CPL, kBF16>(ye, p, wt, dst, lane, rb16);
+      } else {
+        for (int c0 = lane; c0 < rb16; c0 += CPL * 64) {
+          float acc[CPL][EPC];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int i = 0; i < EPC; ++i) acc[c][i] = 0.0f;
+#pragma unroll
+          for (int k = 0; k < KT; ++k) {
+            u32x4 v[CPL];
+            load_piece<true, CPL>(v, ye + (size_t)p[k] * rb16, c0, rb16, true);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              if (c0 + c * 64 < rb16) fma_row<kBF16>(acc[c], wt[k], v[c]);
+          }
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            if (c0 + c * 64 < rb16) __builtin_nontemporal_store(pack_row<kBF16>(acc[c]), dst + c0 + c * 64);
+        }
+      }
+      return;
+    }
+  }
+  // Runtime K, or a row outside the buffer (only a broken plan makes one):
+  // such a row contributes nothing.
+  for (int c0 = lane; c0 < rb16; c0 += CPL * 64) {
+    float acc[CPL][EPC];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) acc[c][i] = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if ((unsigned)p >= (unsigned)rows) continue;
+      const float wk = wt[k];
+      u32x4 v[CPL];
+      load_piece<!kExact, CPL>(v, ye + (size_t)p * rb16, c0, rb16, true);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        if (kExact || c0 + c * 64 < rb16) fma_row<kBF16>(acc[c], wk, v[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int i = c0 + c * 64;
+      if (kExact || i < rb16) __builtin_nontemporal_store(pack_row<kBF16>(acc[c]), dst + i);
+    }
+  }
+}
+
+// Chunks per lane of one piece: the whole row when it is a multiple of
+// 1 KiB up to 16 KiB, else 16-chunk pieces with bounds checks.
+inline int pick_cpl(int rb16, bool& exact) {
+  exact = rb16 % 64 == 0 && rb16 / 64 <= 16;
+  return exact ? rb16 / 64 : 16;
+}
+
+}  // namespace
+
+#define MB_CPL_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
+
+hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* x,
+                           const float* x_scale, void* buf, float* buf_scale, hipStream_t st) {
+  if (d.n_tokens == 0) return hipSuccess;
+  const int rb16 = (int)(d.hidden * elt_bytes(d.dtype_in) / 16);
+  const int nsc = d.dtype_in == MB_FP8_E4M3 ? d.hidden / 128 : 0;
+  const int rows = d.n_ranks * d.cap;
+  const dim3 grid((d.n_tokens + kTokensPerRowBlock - 1) / kTokensPerRowBlock);
+  bool exact;
+  const int cpl = pick_cpl(rb16, exact);
+  const u32x4* xx = static_cast<const u32x4*>(x);
+  u32x4* bb = static_cast<u32x4*>(buf);
+#define MB_D(C)                                                                           \
+  case C:                                                                                 \
+    hipLaunchKernelGGL((k_dispatch<C, true>), grid, dim3(kRowThreads), 0, st, xx, o.pos,  \
+                       o.status, bb, d.n_tokens, d.top_k, rb16, rows, x_scale, buf_scale, nsc); \
+    break;
+  if (exact) {
+    switch (cpl) { MB_CPL_CASES(MB_D) default: return hipErrorInvalidValue; }
+  } else {
+    hipLaunchKernelGGL((k_dispatch<16, false>), grid, dim3(kRowThreads), 0, st, xx, o.pos,
+                       o.status, bb, d.n_tokens, d.top_k, rb16, rows, x_scale, buf_scale, nsc);
+  }
+#undef MB_D
+  return hipGetLastError();
+}
+
+template <bool kBF16>
+static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x4* ye,
+                             const float* w, u32x4* yy, int rb16, int rows, hipStream_t st) {
+  const dim3 grid((d.n_tokens + kTokensPerRowBlock - 1) / kTokensPerRowBlock);
+  bool exact;
+  const int cpl = pick_cpl(rb16, exact);
+  const int K = d.top_k;
+#define MB_C(KT, C)                                                                        \
+  hipLaunchKernelGGL((k_combine<KT, C, true, kBF16>), grid, dim3(kRowThreads), 0, st, ye,  \
+                     o.pos, w, o.status, yy, d.n_tokens, K, rb16, rows)
+#define MB_CK(C)                       \
+  case C:                              \
+    if (K == 8) MB_C(8, C);            \
+    else if (K == 2) MB_C(2, C);       \
+    else if (K == 1) MB_C(1, C);       \
+    else if (K == 4) MB_C(4, C);       \
+    else MB_C(0, C);                   \
+    break;
+  if (exact) {
+    switch (cpl) { MB_CPL_CASES(MB_CK) default: break; }
+  } else {
+    hipLaunchKernelGGL((k_combine<0, 16, false, kBF16>), grid, dim3(kRowThreads), 0, st, ye,
+                       o.pos, w, o.status, yy, d.n_tokens, K, rb16, rows);
+  }
+#undef MB_CK
+#undef MB_C
+}
+
+hipError_t launch_combine(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
+                          const float* w, void* y, hipStream_t st) {
+  if (d.n_tokens == 0) return hipSuccess;
+  const int rb16 = (int)(d.hidden * elt_bytes(d.dtype_out) / 16);
+  const int rows = d.n_ranks * d.cap;
+  const u32x4* ye = static_cast<const u32x4*>(y_exp);
+  u32x4* yy = static_cast<u32x4*>(y);
+  if (d.dtype_out == MB_BF16)
+    launch_combine_t<true>(d, o, ye, w, yy, rb16, rows, st);
+  else
+    launch_combine_t<false>(d, o, ye, w, yy, rb16, rows, st);
+  return hipGetLastError();
+}
+
+}  // namespace mb

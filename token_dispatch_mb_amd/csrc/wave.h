@@ -1,0 +1,83 @@
+// wave.h — wave64 primitives for gfx950 used by libmoebal's kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mb {
+
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// DPP row shift / broadcast with `identity` for lanes that receive nothing.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_or_identity(int identity, int v) {
+  return __builtin_amdgcn_update_dpp(identity, v, kCtrl, kRowMask, 0xf, false);
+}
+
+// Full-wave reductions; every lane of the wave must be active. The result is
+// uniform (read from lane 63 after an inclusive DPP scan: row_shr 1, 2, 4, 8
+// inside 16-lane rows, then row_bcast 15 and row_bcast 31).
+__device__ __forceinline__ int wave_max_i32(int v) {
+  constexpr int I = INT32_MIN;
+  v = max(v, dpp_or_identity<0x111, 0xf>(I, v));
+  v = max(v, dpp_or_identity<0x112, 0xf>(I, v));
+  v = max(v, dpp_or_identity<0x114, 0xf>(I, v));
+  v = max(v, dpp_or_identity<0x118, 0xf>(I, v));
+  v = max(v, dpp_or_identity<0x142, 0xa>(I, v));
+  v = max(v, dpp_or_identity<0x143, 0xc>(I, v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+  constexpr int I = INT32_MAX;
+  v = min(v, dpp_or_identity<0x111, 0xf>(I, v));
+  v = min(v, dpp_or_identity<0x112, 0xf>(I, v));
+  v = min(v, dpp_or_identity<0x114, 0xf>(I, v));
+  v = min(v, dpp_or_identity<0x118, 0xf>(I, v));
+  v = min(v, dpp_or_identity<0x142, 0xa>(I, v));
+  v = min(v, dpp_or_identity<0x143, 0xc>(I, v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// max of `a` and min of `b` over the wave, the two DPP chains interleaved so
+// that each hides the other's latency.
+__device__ __forceinline__ void wave_max_min_i32(int a, int b, int& amax, int& bmin) {
+  constexpr int IA = INT32_MIN, IB = INT32_MAX;
+  a = max(a, dpp_or_identity<0x111, 0xf>(IA, a));
+  b = min(b, dpp_or_identity<0x111, 0xf>(IB, b));
+  a = max(a, dpp_or_identity<0x112, 0xf>(IA, a));
+  b = min(b, dpp_or_identity<0x112, 0xf>(IB, b));
+  a = max(a, dpp_or_identity<0x114, 0xf>(IA, a));
+  b = min(b, dpp_or_identity<0x114, 0xf>(IB, b));
+  a = max(a, dpp_or_identity<0x118, 0xf>(IA, a));
+  b = min(b, dpp_or_identity<0x118, 0xf>(IB, b));
+  a = max(a, dpp_or_identity<0x142, 0xa>(IA, a));
+  b = min(b, dpp_or_identity<0x142, 0xa>(IB, b));
+  a = max(a, dpp_or_identity<0x143, 0xc>(IA, a));
+  b = min(b, dpp_or_identity<0x143, 0xc>(IB, b));
+  amax = __builtin_amdgcn_readlane(a, 63);
+  bmin = __builtin_amdgcn_readlane(b, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes (every lane active).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += dpp_or_identity<0x111, 0xf>(0, v);
+  v += dpp_or_identity<0x112, 0xf>(0, v);
+  v += dpp_or_identity<0x114, 0xf>(0, v);
+  v += dpp_or_identity<0x118, 0xf>(0, v);
+  v += dpp_or_identity<0x142, 0xa>(0, v);
+  v += dpp_or_identity<0x143, 0xc>(0, v);
+  return v;
+}
+
+__device__ __forceinline__ int lowest_lane(uint64_t mask) {
+  return mask ? __builtin_ctzll(mask) : -1;
+}
+
+}  // namespace mb
