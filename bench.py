@@ -13,7 +13,7 @@ before timing into a buffer of their own.
 Prints one JSON line. `value` is dispatch + combine algorithmic bytes per
 step divided by the whole step time (plan included). `roofline` refers to the
 kernel with the larger share of the step (HIP events on the launch stream);
-`cpu_baseline` times the CPU oracle (single thread) on a quarter of the
+`cpu_baseline` times the CPU oracle (single thread) on half of the
 tokens of the same workload.
 """
 from __future__ import annotations
@@ -74,7 +74,7 @@ def measured_traffic(kernel: str, workload: str):
     return float(m.group(1)) if m else None
 
 
-def cpu_baseline(wl, fraction: int = 4) -> dict:
+def cpu_baseline(wl, fraction: int = 2) -> dict:
     """The CPU oracle as it stands (single thread) on 1/fraction of the
     tokens of the same workload: plan, dispatch and combine; GB/s over the
     same algorithmic bytes, plus the oracle's plan time on the full call."""
@@ -86,21 +86,33 @@ def cpu_baseline(wl, fraction: int = 4) -> dict:
     sub = wl.scaled(wl.n_tokens // fraction)
     ids, w = W.routing_for(sub)
     x, xs = W.token_rows(sub)
-    od = O.dims_for(sub)
+    # The smaller routing sample need not balance to exactly T with the same
+    # slots, so its regions get room for 2 * S * K rows (same per-pair work).
+    od = O.dims_for(sub, cap=2 * sub.cap)
+    rows = od.n_ranks * od.cap
+    # Outputs allocated and touched outside the timed region.
+    buf = np.empty((rows, O.row_bytes_in(od)), np.uint8)
+    buf.fill(0)
+    y64 = np.empty((sub.n_tokens, od.hidden), np.float64)
+    y64.fill(0.0)
+    mag = np.empty_like(y64)
+    mag.fill(0.0)
     t0 = time.perf_counter()
     p = O.plan(od, ids)
     t1 = time.perf_counter()
-    buf, bs, _ = O.dispatch(od, p, x, xs)
+    O.dispatch(od, p, x, xs, out=buf)
     t2 = time.perf_counter()
     if od.dtype_out == O.BF16 and od.dtype_in == O.BF16:
         y_exp = buf.view(np.uint16).reshape(-1, od.hidden)
     elif od.dtype_out == O.F32 and od.dtype_in == O.F32:
         y_exp = buf.view(np.float32).reshape(-1, od.hidden)
     else:
-        y_exp = W.rows_bf16(sub.seed, W.TAG_YEXP, od.hidden, n=od.n_ranks * od.cap)
+        y_exp = W.rows_bf16(sub.seed, W.TAG_YEXP, od.hidden, n=rows)
     t3 = time.perf_counter()
-    O.combine(od, p.pos, p.status, w, y_exp)
+    O.combine(od, p.pos, p.status, w, y_exp, out=(y64, mag))
     t4 = time.perf_counter()
+    if p.flags & O.ST_FATAL:
+        raise RuntimeError(f"oracle sample plan failed: status {p.status.tolist()}")
     ab = algorithmic_bytes(sub)
     full_ids, _ = W.routing_for(wl)
     f0 = time.perf_counter()
@@ -112,7 +124,8 @@ def cpu_baseline(wl, fraction: int = 4) -> dict:
         "cores": 1,
         "kind": "oracle",
         "sample": f"{sub.n_tokens} of {wl.n_tokens} tokens of {wl.name} (same routing model, "
-                  f"same E/K/P/R/H): plan + dispatch + combine, single-threaded C oracle",
+                  f"same E/K/P/R/H, regions of 2*S*K rows): plan + dispatch + combine, "
+                  f"single-threaded C oracle",
         "plan_us_sample": round((t1 - t0) * 1e6, 1),
         "dispatch_s": round(t2 - t1, 3),
         "combine_s": round(t4 - t3, 3),
@@ -140,6 +153,9 @@ def main() -> int:
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="leave out the CPU oracle leg (for profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch's device copy of MIB MiB three times (the known-size "
+                         "reference for the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the P logical ranks of the expert-parallel group are "
@@ -157,6 +173,15 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return 0
     wl = W.get_workload(args.workload)
     dims = mb.Dims.for_workload(wl)
     log(f"workload {wl.name}: {wl.note}")

@@ -161,12 +161,17 @@ def row_bytes_in(dims: Dims) -> int:
 
 
 def dispatch(dims: Dims, p: Plan, x: np.ndarray, x_scale: np.ndarray | None = None,
-             row0: int = 0, row1: int | None = None, fill: int = 0):
+             row0: int = 0, row1: int | None = None, fill: int = 0, out: np.ndarray | None = None):
     """Rows [row0, row1) of the dispatch buffer as uint8 [rows, row_bytes]
-    (rows no pair maps to hold ``fill``), plus the fp8 scale rows or None."""
+    (rows no pair maps to hold ``fill``, or are left as they are in ``out``),
+    plus the fp8 scale rows or None."""
     row1 = dims.n_ranks * dims.cap if row1 is None else row1
     rb = row_bytes_in(dims)
-    buf = np.full((row1 - row0, rb), fill, dtype=np.uint8)
+    if out is not None:
+        assert out.dtype == np.uint8 and out.shape == (row1 - row0, rb) and out.flags.c_contiguous
+        buf = out
+    else:
+        buf = np.full((row1 - row0, rb), fill, dtype=np.uint8)
     nsc = dims.hidden // 128 if dims.dtype_in == FP8_E4M3 else 0
     bs = np.zeros((row1 - row0, nsc), np.float32) if nsc else None
     x = np.ascontiguousarray(x)
@@ -181,13 +186,19 @@ def dispatch(dims: Dims, p: Plan, x: np.ndarray, x_scale: np.ndarray | None = No
 
 
 def combine(dims: Dims, pos: np.ndarray, status: np.ndarray, w: np.ndarray, y_exp: np.ndarray,
-            t0: int = 0, t1: int | None = None):
+            t0: int = 0, t1: int | None = None, out: tuple | None = None):
     """(y, mag) in float64 for tokens [t0, t1); y_exp is the [rows, H] expert
-    output array in dims.dtype_out (float32, or uint16 bf16 bits)."""
+    output array in dims.dtype_out (float32, or uint16 bf16 bits). ``out`` may
+    supply preallocated (y, mag) arrays."""
     t1 = dims.n_tokens if t1 is None else t1
     H = dims.hidden
-    y = np.zeros((t1 - t0, H), np.float64)
-    mag = np.zeros((t1 - t0, H), np.float64)
+    if out is not None:
+        y, mag = out
+        assert y.shape == (t1 - t0, H) and mag.shape == (t1 - t0, H)
+        assert y.dtype == np.float64 and mag.dtype == np.float64
+    else:
+        y = np.zeros((t1 - t0, H), np.float64)
+        mag = np.zeros((t1 - t0, H), np.float64)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     w = np.ascontiguousarray(w, dtype=np.float32)
     y_exp = np.ascontiguousarray(y_exp)
