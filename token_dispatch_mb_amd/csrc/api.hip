@@ -30,6 +30,8 @@ WsLayout ws_layout(const mb_dims& d, const Geometry& g) {
   off = align256(off + per_block);
   L.blockflags = off;
   off = align256(off + (size_t)g.nblk * sizeof(int32_t) + sizeof(int32_t));
+  L.brank = off;
+  off = align256(off + (size_t)d.n_tokens * d.top_k);
   L.expert_total = off;
   off = align256(off + (size_t)d.n_experts * sizeof(int32_t));
   L.pair_tab = off;
@@ -63,6 +65,9 @@ static int validate(const mb_dims* d) {
   if ((int64_t)d->hidden * bin % 16 || (int64_t)d->hidden * elt_bytes(d->dtype_out) % 16)
     return MB_ERR_INVALID_ARG;
   if ((int64_t)d->hidden * bin / 16 > INT32_MAX) return MB_ERR_INVALID_ARG;
+  // dispatch runs one wave per 1 KiB chunk of every token row
+  if ((int64_t)d->n_tokens * (((int64_t)d->hidden * bin / 16 + 63) / 64) > INT32_MAX)
+    return MB_ERR_INVALID_ARG;
   if (d->dtype_in == MB_FP8_E4M3 && d->hidden % 128) return MB_ERR_INVALID_ARG;
   return MB_OK;
 }
@@ -117,17 +122,20 @@ int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws
   HostEntry* host_list = reinterpret_cast<HostEntry*>(ws + L.host_list);
   int2* host_range = reinterpret_cast<int2*>(ws + L.host_range);
   int32_t* expert_total = reinterpret_cast<int32_t*>(ws + L.expert_total);
+  uint8_t* brank = ws + L.brank;
 
   // count -> per-source offsets and totals -> greedy placement -> lookup
   // tables -> per-pair rows, all on `stream`, no host synchronisation.
-  if (launch_count(*dims, g, ids_dev, blockcnt, blockflags, stream) != hipSuccess) return MB_ERR_HIP;
+  if (launch_count(*dims, g, ids_dev, blockcnt, blockflags, brank, stream) != hipSuccess)
+    return MB_ERR_HIP;
   if (launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_plan(*dims, g, *out, blockflags, expert_total, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_assign(*dims, g, ids_dev, blockoff, pair_tab, host_list, host_range, *out, stream) !=
+  if (launch_assign(*dims, g, ids_dev, brank, blockoff, pair_tab, host_list, host_range, *out,
+                    stream) !=
       hipSuccess)
     return MB_ERR_HIP;
   return MB_OK;

@@ -54,7 +54,8 @@ struct Geometry {
 };
 
 struct WsLayout {
-  size_t blockcnt, blockoff, blockflags, expert_total, pair_tab, host_list, host_range, total;
+  size_t blockcnt, blockoff, blockflags, brank, expert_total, pair_tab, host_list, host_range,
+      total;
 };
 
 // Entries of the compact host list: one home per expert plus one per
@@ -66,7 +67,7 @@ WsLayout ws_layout(const mb_dims& d, const Geometry& g);
 
 // Launchers (each returns hipSuccess or the launch error).
 hipError_t launch_count(const mb_dims& d, const Geometry& g, const int32_t* ids,
-                        int32_t* blockcnt, int32_t* blockflags, hipStream_t st);
+                        int32_t* blockcnt, int32_t* blockflags, uint8_t* brank, hipStream_t st);
 hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* blockcnt,
                        int32_t* blockoff, int32_t* counts, int32_t* expert_total,
                        hipStream_t st);
@@ -77,7 +78,7 @@ hipError_t launch_tables(const mb_dims& d, const Geometry& g, const mb_plan_bufs
                          PairEntry* pair_tab, HostEntry* host_list, int2* host_range,
                          hipStream_t st);
 hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids,
-                         const int32_t* blockoff, const PairEntry* pair_tab,
+                         const uint8_t* brank, const int32_t* blockoff, const PairEntry* pair_tab,
                          const HostEntry* host_list, const int2* host_range,
                          const mb_plan_bufs& o, hipStream_t st);
 hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* x,

@@ -106,16 +106,26 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     q[j] = (rank_lane && j < Eh) ? m.c[lane * Eh + j] : 0;
     load += q[j];
   }
-  // Heaviest remaining home expert of this rank, lowest index on ties.
+  // Heaviest remaining home expert of this rank, lowest index on ties: a
+  // pairwise tournament (log2 EHM levels) so the compares of a level are
+  // independent of each other.
   auto best = [&](int& bq, int& bj) {
-    bq = -1;
-    bj = 0;
+    int v[EHM], ix[EHM];
 #pragma unroll
-    for (int j = 0; j < EHM; ++j)
-      if (q[j] > bq) {
-        bq = q[j];
-        bj = j;
+    for (int j = 0; j < EHM; ++j) {
+      v[j] = q[j];
+      ix[j] = j;
+    }
+#pragma unroll
+    for (int width = EHM / 2; width >= 1; width /= 2)
+#pragma unroll
+      for (int j = 0; j < width; ++j) {
+        const bool right = v[2 * j + 1] > v[2 * j];  // ties keep the lower index
+        v[j] = right ? v[2 * j + 1] : v[2 * j];
+        ix[j] = right ? ix[2 * j + 1] : ix[2 * j];
       }
+    bq = v[0];
+    bj = ix[0];
   };
   int bq, bj;
   best(bq, bj);

@@ -2,14 +2,15 @@
 // assignment of libmoebal's plan.
 //
 // Stable ranks without atomics deciding order. A routing workgroup owns 256
-// consecutive tokens of one source rank (one token per lane). Each wave64
-// builds, in LDS, one 64-bit mask per expert whose bit l says "lane l's token
-// routes to this expert" (ds_or_b64: commutative, so the masks do not depend
-// on timing). A pair's rank among the earlier pairs of its (source rank,
-// expert) is then
+// consecutive tokens of one source rank (one token per lane). In k_count each
+// wave64 builds, in LDS, one 64-bit mask per expert whose bit l says "lane
+// l's token routes to this expert" (ds_or_b64: commutative, so the masks do
+// not depend on timing). A pair's rank among the earlier pairs of its (source
+// rank, expert) is then
 //   rho = (pairs in earlier workgroups of the same source, from k_scan)
 //       + popcount of the masks of earlier waves
-//       + popcount of its own wave's mask below its lane (mbcnt).
+//       + popcount of its own wave's mask below its lane (mbcnt);
+// k_count stores the in-workgroup part (below 256, one byte) for k_assign.
 // Tokens list distinct experts, so "earlier pair with the same expert" and
 // "earlier token with that expert" coincide.
 //
@@ -47,7 +48,8 @@ __device__ __forceinline__ int mark_token(const int32_t* __restrict__ row, int K
 template <int KT>
 __global__ __launch_bounds__(kTokensPerBlock) void k_count(
     const int32_t* __restrict__ ids, int K_, int E, int S, int nbps,
-    int32_t* __restrict__ blockcnt, int32_t* __restrict__ blockflags) {
+    int32_t* __restrict__ blockcnt, int32_t* __restrict__ blockflags,
+    uint8_t* __restrict__ brank) {
   extern __shared__ unsigned long long masks[];  // [kWaves][E]
   const int K = KT ? KT : K_;
   const int b = blockIdx.x;
@@ -57,11 +59,10 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_count(
   for (int i = tl; i < kWaves * E; i += kTokensPerBlock) masks[i] = 0ull;
   __syncthreads();
   const int w = tl >> 6, lane = tl & 63;
+  const size_t t = (size_t)s * S + (size_t)j * kTokensPerBlock + tl;
+  const int32_t* row = ids + t * K;
   int flags = 0;
-  if (tl < nt) {
-    const size_t t = (size_t)s * S + (size_t)j * kTokensPerBlock + tl;
-    flags = mark_token<KT>(ids + t * K, K, E, masks + w * E, lane);
-  }
+  if (tl < nt) flags = mark_token<KT>(row, K, E, masks + w * E, lane);
   const int bad = __syncthreads_or(flags & MB_ST_BAD_ID);
   const int dup = __syncthreads_or(flags & MB_ST_DUP_ID);
   for (int e = tl; e < E; e += kTokensPerBlock) {
@@ -71,6 +72,29 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_count(
     blockcnt[(size_t)b * E + e] = c;
   }
   if (tl == 0) blockflags[b] = (bad ? MB_ST_BAD_ID : 0) | (dup ? MB_ST_DUP_ID : 0);
+  if (tl >= nt) return;
+  // In-workgroup rank of each of the token's pairs (0 for a bad id).
+  auto rank_in_block = [&](int e) -> uint32_t {
+    if ((unsigned)e >= (unsigned)E) return 0u;
+    int r = 0;
+    for (int ww = 0; ww < w; ++ww) r += __popcll(masks[ww * E + e]);
+    return (uint32_t)(r + lanes_below(masks[w * E + e]));
+  };
+  if constexpr (KT == 8) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lo |= rank_in_block(row[k]) << (8 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hi |= rank_in_block(row[4 + k]) << (8 * k);
+    reinterpret_cast<uint2*>(brank)[t] = make_uint2(lo, hi);
+  } else if constexpr (KT == 4) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v |= rank_in_block(row[k]) << (8 * k);
+    reinterpret_cast<uint32_t*>(brank)[t] = v;
+  } else {
+    for (int k = 0; k < K; ++k) brank[t * K + k] = (uint8_t)rank_in_block(row[k]);
+  }
 }
 
 // Exclusive scan over the workgroups of each source rank, per expert; the
@@ -121,26 +145,56 @@ __global__ __launch_bounds__(256) void k_scan(const int32_t* __restrict__ blockc
 // when it fits (kStageHosts), the whole compact host list.
 template <int KT, bool kStageHosts>
 __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
-    const int32_t* __restrict__ ids, int K_, int E, int S, int P, int nbps, int nblk, int cap,
-    int nhost, const int32_t* __restrict__ blockoff, const PairEntry* __restrict__ pair_tab,
-    const HostEntry* __restrict__ host_list, const int2* __restrict__ host_range,
-    const int32_t* __restrict__ status, const int32_t* __restrict__ load_post,
-    int32_t* __restrict__ pos, int32_t* __restrict__ row_src) {
-  // LDS: masks [kWaves][E] | offsets [E] | pairs [E] | ranges [E] | hosts [nhost]
-  extern __shared__ unsigned long long masks[];
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ brank, int K_, int E, int S,
+    int P, int nbps, int nblk, int cap, int nhost, const int32_t* __restrict__ blockoff,
+    const PairEntry* __restrict__ pair_tab, const HostEntry* __restrict__ host_list,
+    const int2* __restrict__ host_range, const int32_t* __restrict__ status,
+    const int32_t* __restrict__ load_post, int32_t* __restrict__ pos,
+    int32_t* __restrict__ row_src) {
+  // LDS: offsets [E4] | pairs [E] | ranges [E4] | hosts [nhost]
+  extern __shared__ int4 lds[];
+  __shared__ int32_t lp_s[kMaxRanks];
   if (status[0] & MB_ST_FATAL) return;
   const int K = KT ? KT : K_;
   const int b = blockIdx.x;
   const int tl = threadIdx.x;
+  const int s = b / max(nbps, 1), j = b - s * nbps;
+  const bool has_tokens = b < nblk;
+  const int nt = has_tokens ? min(kTokensPerBlock, S - j * kTokensPerBlock) : 0;
+  const int E4 = (E + 3) & ~3;
+  int32_t* boff = reinterpret_cast<int32_t*>(lds);
+  PairEntry* ptab = reinterpret_cast<PairEntry*>(boff + E4);
+  int2* hrange = reinterpret_cast<int2*>(ptab + E);
+  HostEntry* hl = reinterpret_cast<HostEntry*>(hrange + E4);
 
-  // Padding rows: region r has rows [r*cap + load_post[r], (r+1)*cap).
-  // With every region full (a balanced plan at cap = T) there are none.
-  __shared__ int32_t lp_s[kMaxRanks];
+  // The lane's token: expert ids and in-workgroup ranks, fetched first.
+  const size_t t = (size_t)s * S + (size_t)j * kTokensPerBlock + tl;
+  constexpr int KR = KT ? KT : 1;
+  int er[KR], br[KR];
+  if (KT && tl < nt) {
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      er[k] = ids[t * K + k];
+      br[k] = brank[t * K + k];
+    }
+  }
   int pad = 0;
   if (tl < P) {
     lp_s[tl] = load_post[tl];
     pad = cap - lp_s[tl];
   }
+  if (has_tokens) {
+    for (int i = tl; i < E; i += kTokensPerBlock) {
+      boff[i] = blockoff[(size_t)b * E + i];
+      ptab[i] = pair_tab[(size_t)s * E + i];
+      hrange[i] = host_range[i];
+    }
+    if constexpr (kStageHosts)
+      for (int i = tl; i < nhost; i += kTokensPerBlock) hl[i] = host_list[i];
+  }
+  const HostEntry* hosts = kStageHosts ? hl : host_list;
+  // Padding rows: region r has rows [r*cap + load_post[r], (r+1)*cap); with
+  // every region full (a balanced plan at cap = T) there are none.
   if (__syncthreads_or(pad > 0)) {
     for (int r = 0; r < P; ++r) {
       const int lp = lp_s[r];
@@ -148,59 +202,50 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
         row_src[r * cap + lp + i] = -1;
     }
   }
-  if (b >= nblk) return;
-
-  const int s = b / nbps, j = b - s * nbps;
-  const int nt = min(kTokensPerBlock, S - j * kTokensPerBlock);
-  const int E4 = (E + 3) & ~3;
-  int32_t* boff = reinterpret_cast<int32_t*>(masks + kWaves * E);
-  PairEntry* ptab = reinterpret_cast<PairEntry*>(boff + E4);
-  int2* hrange = reinterpret_cast<int2*>(ptab + E);
-  HostEntry* hl = reinterpret_cast<HostEntry*>(hrange + E4);
-  for (int i = tl; i < E; i += kTokensPerBlock) {
-    boff[i] = blockoff[(size_t)b * E + i];
-    ptab[i] = pair_tab[(size_t)s * E + i];
-    hrange[i] = host_range[i];
-  }
-  if constexpr (kStageHosts)
-    for (int i = tl; i < nhost; i += kTokensPerBlock) hl[i] = host_list[i];
-  const HostEntry* hosts = kStageHosts ? hl : host_list;
-  for (int i = tl; i < kWaves * E; i += kTokensPerBlock) masks[i] = 0ull;
-  const int w = tl >> 6, lane = tl & 63;
-  const size_t t = (size_t)s * S + (size_t)j * kTokensPerBlock + tl;
-  const int32_t* row = ids + t * K;
-  __syncthreads();
-  if (tl < nt) mark_token<KT>(row, K, E, masks + w * E, lane);
-  __syncthreads();
   if (tl >= nt) return;
 
   const int rows = P * cap;
-  auto rank_of = [&](int e) {
-    int rho = boff[e];
-    for (int ww = 0; ww < w; ++ww) rho += __popcll(masks[ww * E + e]);
-    return rho + lanes_below(masks[w * E + e]);
-  };
   // Pass 1 keeps the first local_quota pairs of (s, e) on s; a later pair is
   // surplus number u of e and goes to the host whose share covers u.
-  auto row_of = [&](int e, int rho) {
-    const PairEntry pe = ptab[e];
-    if (rho < pe.local_quota) return pe.local_base + rho;
-    const int u = rho + pe.surplus_shift;
+  auto search = [&](int e, int u, int q0) {
     const int2 rg = hrange[e];
-    for (int q = 0; q < rg.y; ++q) {
+    for (int q = q0; q < rg.y; ++q) {
       const HostEntry h = hosts[rg.x + q];
       if (u < h.end) return h.base + u + (h.rank < s ? h.lt : 0);
     }
     return -1;
   };
   if constexpr (KT > 0) {
-    int er[KT], rho[KT], p[KT];
+    // All table reads of the K pairs are independent; the first two hosts of
+    // each expert are probed unconditionally (clamped indices stay inside
+    // the expert's own range), the rest only when a share lies further out.
+    PairEntry pe[KT];
+    int2 rg[KT];
+    HostEntry h0[KT], h1[KT];
+    int rho[KT], p[KT];
 #pragma unroll
-    for (int k = 0; k < KT; ++k) er[k] = row[k];
+    for (int k = 0; k < KT; ++k) {
+      rho[k] = boff[er[k]] + br[k];
+      pe[k] = ptab[er[k]];
+      rg[k] = hrange[er[k]];
+    }
 #pragma unroll
-    for (int k = 0; k < KT; ++k) rho[k] = rank_of(er[k]);
+    for (int k = 0; k < KT; ++k) {
+      h0[k] = hosts[rg[k].x];
+      h1[k] = hosts[rg[k].x + (rg[k].y > 1 ? 1 : 0)];
+    }
 #pragma unroll
-    for (int k = 0; k < KT; ++k) p[k] = row_of(er[k], rho[k]);
+    for (int k = 0; k < KT; ++k) {
+      const int u = rho[k] + pe[k].surplus_shift;
+      if (rho[k] < pe[k].local_quota)
+        p[k] = pe[k].local_base + rho[k];
+      else if (u < h0[k].end)
+        p[k] = h0[k].base + u + (h0[k].rank < s ? h0[k].lt : 0);
+      else if (rg[k].y > 1 && u < h1[k].end)
+        p[k] = h1[k].base + u + (h1[k].rank < s ? h1[k].lt : 0);
+      else
+        p[k] = search(er[k], u, 2);
+    }
 #pragma unroll
     for (int k = 0; k < KT; ++k) pos[t * K + k] = p[k];
 #pragma unroll
@@ -208,8 +253,11 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
       if ((unsigned)p[k] < (unsigned)rows) row_src[p[k]] = (int32_t)t;
   } else {
     for (int k = 0; k < K; ++k) {
-      const int e = row[k];
-      const int p = row_of(e, rank_of(e));
+      const int e = ids[t * K + k];
+      const int rho = boff[e] + brank[t * K + k];
+      const PairEntry pe = ptab[e];
+      const int p = rho < pe.local_quota ? pe.local_base + rho
+                                         : search(e, rho + pe.surplus_shift, 0);
       pos[t * K + k] = p;
       if ((unsigned)p < (unsigned)rows) row_src[p] = (int32_t)t;
     }
@@ -275,11 +323,11 @@ __global__ __launch_bounds__(256) void k_tables(
 
 
 hipError_t launch_count(const mb_dims& d, const Geometry& g, const int32_t* ids,
-                        int32_t* blockcnt, int32_t* blockflags, hipStream_t st) {
+                        int32_t* blockcnt, int32_t* blockflags, uint8_t* brank, hipStream_t st) {
   if (g.nblk == 0) return hipSuccess;
   const size_t shmem = sizeof(unsigned long long) * kWaves * d.n_experts;
   MB_DISPATCH_TOPK(d.top_k, k_count, dim3(g.nblk), dim3(kTokensPerBlock), shmem, st, ids,
-                   d.top_k, d.n_experts, g.S, g.nbps, blockcnt, blockflags);
+                   d.top_k, d.n_experts, g.S, g.nbps, blockcnt, blockflags, brank);
   return hipGetLastError();
 }
 
@@ -302,7 +350,7 @@ hipError_t launch_tables(const mb_dims& d, const Geometry& g, const mb_plan_bufs
 }
 
 hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids,
-                         const int32_t* blockoff, const PairEntry* pair_tab,
+                         const uint8_t* brank, const int32_t* blockoff, const PairEntry* pair_tab,
                          const HostEntry* host_list, const int2* host_range,
                          const mb_plan_bufs& o, hipStream_t st) {
   const int64_t rows = (int64_t)d.n_ranks * d.cap;
@@ -312,23 +360,23 @@ hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids
   if (grid < 1) grid = 1;
   const int E4 = (d.n_experts + 3) & ~3;
   const int nhost = host_list_cap(d);
-  const size_t base = sizeof(unsigned long long) * kWaves * d.n_experts +
-                      sizeof(int32_t) * E4 + sizeof(PairEntry) * d.n_experts + sizeof(int2) * E4;
+  const size_t base =
+      sizeof(int32_t) * E4 + sizeof(PairEntry) * d.n_experts + sizeof(int2) * E4;
   const size_t with_hosts = base + sizeof(HostEntry) * nhost;
-  const bool stage = with_hosts <= 60 * 1024;
+  const bool stage = with_hosts <= 48 * 1024;
   const size_t shmem = stage ? with_hosts : base;
-#define MB_A(KT)                                                                            \
-  do {                                                                                      \
-    if (stage)                                                                              \
+#define MB_A(KT)                                                                             \
+  do {                                                                                       \
+    if (stage)                                                                               \
       hipLaunchKernelGGL((k_assign<KT, true>), dim3(grid), dim3(kTokensPerBlock), shmem, st, \
-                         ids, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps, g.nblk, d.cap,  \
-                         nhost, blockoff, pair_tab, host_list, host_range, o.status,        \
-                         o.load_post, o.pos, o.row_src);                                    \
-    else                                                                                    \
-      hipLaunchKernelGGL((k_assign<KT, false>), dim3(grid), dim3(kTokensPerBlock), shmem, st, \
-                         ids, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps, g.nblk, d.cap,  \
-                         nhost, blockoff, pair_tab, host_list, host_range, o.status,        \
-                         o.load_post, o.pos, o.row_src);                                    \
+                         ids, brank, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps, g.nblk,   \
+                         d.cap, nhost, blockoff, pair_tab, host_list, host_range, o.status,  \
+                         o.load_post, o.pos, o.row_src);                                     \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_assign<KT, false>), dim3(grid), dim3(kTokensPerBlock), shmem,    \
+                         st, ids, brank, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps,       \
+                         g.nblk, d.cap, nhost, blockoff, pair_tab, host_list, host_range,    \
+                         o.status, o.load_post, o.pos, o.row_src);                           \
   } while (0)
   switch (d.top_k) {
     case 1: MB_A(1); break;

@@ -41,38 +41,45 @@ __device__ __forceinline__ void load_piece(u32x4 (&v)[CPL], const u32x4* __restr
   }
 }
 
-// Dispatch: one wave per token. Measured on MI355X, plain (temporal) loads
-// and stores move this 1-read / K-write pattern faster than nontemporal ones.
-template <int CPL, bool kExact>
+// Dispatch: one wave per 1 KiB chunk of a token row (64 lanes x 16 bytes),
+// the chunks of a token on consecutive waves; each wave loads its chunk once
+// and stores it to the token's K rows. On MI355X this shape moved the
+// 1-read / K-write traffic faster than a wave holding a whole row (many small
+// waves keep more independent store streams in flight), and plain (temporal)
+// loads and stores beat nontemporal ones here.
+template <int KT>
 __global__ __launch_bounds__(kRowThreads) void k_dispatch(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ status, u32x4* __restrict__ buf, int N, int K, int rb16,
-    int rows, const float* __restrict__ xs, float* __restrict__ bs, int nsc) {
+    const int32_t* __restrict__ status, u32x4* __restrict__ buf, int N, int K_, int rb16,
+    int wpt, int rows, const float* __restrict__ xs, float* __restrict__ bs, int nsc) {
+  const int K = KT ? KT : K_;
   const int lane = threadIdx.x & 63;
-  const int t = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  const int gw = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  const int t = gw / wpt, part = gw - t * wpt;
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
-  const u32x4* src = x + (size_t)t * rb16;
+  const int i = part * 64 + lane;
   const int32_t* pt = pos + (size_t)t * K;
-  for (int c0 = lane; c0 < rb16; c0 += CPL * 64) {
-    u32x4 v[CPL];
-    load_piece<!kExact, CPL>(v, src, c0, rb16, false);
-    for (int k = 0; k < K; ++k) {
+  if (i < rb16) {
+    const u32x4 v = x[(size_t)t * rb16 + i];
+    auto put = [&](int k) {
       const int p = pt[k];
-      if ((unsigned)p >= (unsigned)rows) continue;
-      u32x4* dst = buf + (size_t)p * rb16;
+      if ((unsigned)p < (unsigned)rows) buf[(size_t)p * rb16 + i] = v;
+    };
+    if constexpr (KT > 0) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int i = c0 + c * 64;
-        if (kExact || i < rb16) dst[i] = v[c];
-      }
+      for (int k = 0; k < KT; ++k) put(k);
+    } else {
+      for (int k = 0; k < K; ++k) put(k);
     }
   }
-  for (int i = lane; i < nsc; i += 64) {
-    const float v = xs[(size_t)t * nsc + i];
-    for (int k = 0; k < K; ++k) {
-      const int p = pt[k];
-      if ((unsigned)p < (unsigned)rows) bs[(size_t)p * nsc + i] = v;
+  if (part == 0) {
+    for (int c = lane; c < nsc; c += 64) {
+      const float v = xs[(size_t)t * nsc + c];
+      for (int k = 0; k < K; ++k) {
+        const int p = pt[k];
+        if ((unsigned)p < (unsigned)rows) bs[(size_t)p * nsc + c] = v;
+      }
     }
   }
 }
@@ -235,23 +242,12 @@ hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* 
   const int rb16 = (int)(d.hidden * elt_bytes(d.dtype_in) / 16);
   const int nsc = d.dtype_in == MB_FP8_E4M3 ? d.hidden / 128 : 0;
   const int rows = d.n_ranks * d.cap;
-  const dim3 grid((d.n_tokens + kTokensPerRowBlock - 1) / kTokensPerRowBlock);
-  bool exact;
-  const int cpl = pick_cpl(rb16, exact);
-  const u32x4* xx = static_cast<const u32x4*>(x);
-  u32x4* bb = static_cast<u32x4*>(buf);
-#define MB_D(C)                                                                           \
-  case C:                                                                                 \
-    hipLaunchKernelGGL((k_dispatch<C, true>), grid, dim3(kRowThreads), 0, st, xx, o.pos,  \
-                       o.status, bb, d.n_tokens, d.top_k, rb16, rows, x_scale, buf_scale, nsc); \
-    break;
-  if (exact) {
-    switch (cpl) { MB_CPL_CASES(MB_D) default: return hipErrorInvalidValue; }
-  } else {
-    hipLaunchKernelGGL((k_dispatch<16, false>), grid, dim3(kRowThreads), 0, st, xx, o.pos,
-                       o.status, bb, d.n_tokens, d.top_k, rb16, rows, x_scale, buf_scale, nsc);
-  }
-#undef MB_D
+  const int wpt = (rb16 + 63) / 64;  // waves per token
+  const int64_t waves = (int64_t)d.n_tokens * wpt;
+  const dim3 grid((unsigned)((waves + kTokensPerRowBlock - 1) / kTokensPerRowBlock));
+  MB_DISPATCH_TOPK(d.top_k, k_dispatch, grid, dim3(kRowThreads), 0, st,
+                   static_cast<const u32x4*>(x), o.pos, o.status, static_cast<u32x4*>(buf),
+                   d.n_tokens, d.top_k, rb16, wpt, rows, x_scale, buf_scale, nsc);
   return hipGetLastError();
 }
 
