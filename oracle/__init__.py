@@ -17,7 +17,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmbref.so")
+# MBREF_LIB points the tests at another build of mbref.c (the mutation test
+# builds deliberately broken copies to check that the pins catch them).
+LIB_PATH = os.environ.get("MBREF_LIB") or os.path.join(_HERE, "libmbref.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}

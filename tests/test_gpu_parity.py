@@ -324,3 +324,28 @@ def test_prefill_full_size(name):
     G.log(f"{name}: combine sample in tolerance")
     del buf, ye, y, x_d
     torch.cuda.empty_cache()
+
+
+# ---- hand-derived examples (tie-breaks, host order) ------------------------------
+
+@pytest.mark.parametrize("golden", ["hand_example_fill.json", "hand_example_expert_tie.json",
+                                    "hand_example_destination_tie.json",
+                                    "hand_example_surplus_order.json"])
+def test_hand_examples_on_gpu(golden):
+    """The GPU plan of each hand-derived example equals its stored values
+    (and the oracle's)."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", golden)))
+    dd = dict(g["dims"])
+    dd["hidden"] = 8  # 16-byte bf16 rows; the plan does not depend on H
+    ids = np.array(g["ids"], np.int32).reshape(dd["n_tokens"], dd["top_k"])
+    dg = mb.Dims.make(**dd, dtype_in="bf16", dtype_out="bf16")
+    got = G.GpuPlan(dg).run(ids).fetch()
+    exp = g.get("fill_host", g)
+    for key in ("counts", "load_pre", "load_post", "rep_expert", "slot_quota", "cu_seqlens",
+                "row_src", "status"):
+        assert np.array_equal(got[key].reshape(np.array(exp[key]).shape), np.array(exp[key])), key
+    assert np.array_equal(got["pos"].ravel(), exp["pos"])
+    G.assert_plan_equal(got, O.plan(O.make_dims(**dd, dtype_in="bf16", dtype_out="bf16"), ids))

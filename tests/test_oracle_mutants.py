@@ -1,0 +1,75 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one slip in a copy of oracle/mbref.c (a flipped tie-break,
+the other move-size reading, a lost term, a transposed index, ...), builds it
+into a temporary library and runs the pin suite against it in a subprocess;
+the suite has to fail. All on the CPU.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mbref.c")
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("busiest rank tie -> highest index",
+     "if (load[r] > load[rs]) rs = r;", "if (load[r] >= load[rs]) rs = r;"),
+    ("heaviest expert tie -> highest id",
+     "if (best < 0 || qh[e] > qh[best]) best = e;", "if (best < 0 || qh[e] >= qh[best]) best = e;"),
+    ("destination tie -> highest index",
+     "if (dst < 0 || load[r] < load[dst]) dst = r;", "if (dst < 0 || load[r] <= load[dst]) dst = r;"),
+    ("destination -> most loaded open rank",
+     "if (dst < 0 || load[r] < load[dst]) dst = r;", "if (dst < 0 || load[r] > load[dst]) dst = r;"),
+    ("move size capped at the busiest rank's excess",
+     "int64_t m = T - load[dst];", "int64_t m = T - load[dst];\n      if (load[rs] - T < m) m = load[rs] - T;"),
+    ("water level rounded down",
+     "const int64_t T = (N * K + P - 1) / P;", "const int64_t T = (N * K) / P - (N * K % P == 0 ? 1 : 0);"),
+    ("highest free slot",
+     "while (o->rep_expert[dst * R + j] >= 0) ++j;", "j = R - 1;\n      while (o->rep_expert[dst * R + j] >= 0) --j;"),
+    ("no local preference (pass 1 off)",
+     "if (is_host[e * P + s] && used[e * P + s] < Q[e * P + s]) {", "if (0) {"),
+    ("surplus to the highest-index host",
+     "int64_t h = 0;\n      while (h < P && !(is_host[e * P + h] && used[e * P + h] < Q[e * P + h])) ++h;",
+     "int64_t h = P - 1;\n      while (h >= 0 && !(is_host[e * P + h] && used[e * P + h] < Q[e * P + h])) --h;\n      if (h < 0) h = P;"),
+    ("replica slots numbered before home slots",
+     "slot_of[h * E + e] = e - h * Eh;", "slot_of[h * E + e] = R + e - h * Eh;"),
+    ("token source is t % P",
+     "const int64_t s = t / S;\n    for (int64_t k = 0; k < K; ++k) o->counts[s * E + ids[t * K + k]] += 1;",
+     "const int64_t s = t % P;\n    for (int64_t k = 0; k < K; ++k) o->counts[s * E + ids[t * K + k]] += 1;"),
+    ("combine drops the last expert",
+     "for (int64_t k = 0; k < K; ++k) {\n        const double v = out_elem", "for (int64_t k = 0; k < K - 1; ++k) {\n        const double v = out_elem"),
+    ("combine ignores the weights",
+     "const double term = (double)w[t * K + k] * v;", "const double term = v / (double)K;"),
+    ("dispatch copies the next token",
+     "memcpy((char*)buf_win + (p - row0) * rb, (const char*)x + t * rb, (size_t)rb);",
+     "memcpy((char*)buf_win + (p - row0) * rb, (const char*)x + ((t + 1) % N) * rb, (size_t)rb);"),
+    ("duplicate ids not flagged",
+     "if (ids[t * K + k2] == e) flags |= MBREF_ST_DUP_ID;", "if (0) flags |= MBREF_ST_DUP_ID;"),
+]
+
+FAST_PINS = "not prefill and not decode_drift_sequence and not dsv3 and not milp"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mutated = src.replace(old, new, 1)
+    c = tmp_path / "mbref.c"
+    c.write_text(mutated)
+    (tmp_path / "mbref.h").write_text(open(os.path.join(ROOT, "oracle", "mbref.h")).read())
+    lib = tmp_path / "libmbref_mutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC", "-o", str(lib),
+                    str(c), "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, MBREF_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-m", "not gpu", "-k", FAST_PINS,
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch: {name}\n{r.stdout[-2000:]}"

@@ -81,6 +81,65 @@ def test_hand_example_excess_only_stalls():
     assert np.all(p.pos == -1) and np.all(p.row_src == -1)
 
 
+def test_hand_example_expert_tie():
+    """P=2 ranks, 2 home experts each, R=1, K=1, 8 tokens, T = 4.
+
+    c = [3, 3, 2, 0], L = [6, 2]. Rank 0 is above T; its experts 0 and 1 tie
+    at quota 3, so expert 0 (the lower id) gets the replica, on rank 1 (the
+    only open rank): m = min(4 - 2, 3) = 2, loads [4, 4]. Pass 1 keeps t0
+    (e0, quota 1), t1 and t3 (e1) on rank 0 and t4 (replica of e0), t6, t7
+    (e2) on rank 1; pass 2 sends t2 (e0: rank 0 full) to rank 1 and t5 (e1)
+    to rank 0. Rank 1's replica slot holds t2, t4 in token order.
+    """
+    g = json.load(open(os.path.join(GOLDEN, "hand_example_expert_tie.json")))
+    d = O.make_dims(**g["dims"])
+    ids = np.array(g["ids"], np.int32).reshape(-1, 1)
+    p = O.plan(d, ids)
+    for key in ("counts", "load_pre", "load_post", "rep_expert", "slot_quota", "cu_seqlens",
+                "status", "row_src"):
+        assert np.array_equal(getattr(p, key), np.array(g[key])), key
+    assert np.array_equal(p.host.ravel(), g["host"])
+    assert np.array_equal(p.pos.ravel(), g["pos"])
+
+
+def _check_golden(name):
+    g = json.load(open(os.path.join(GOLDEN, name)))
+    d = O.make_dims(**g["dims"])
+    ids = np.array(g["ids"], np.int32).reshape(-1, 1)
+    p = O.plan(d, ids)
+    for key in ("counts", "load_pre", "load_post", "rep_expert", "slot_quota", "cu_seqlens",
+                "status", "row_src"):
+        assert np.array_equal(getattr(p, key), np.array(g[key])), key
+    assert np.array_equal(p.host.ravel(), g["host"])
+    assert np.array_equal(p.pos.ravel(), g["pos"])
+
+
+def test_hand_example_destination_tie():
+    """P=3, 2 home experts each, R=1, K=1, 6 tokens, T = 2.
+
+    c = [0, 1, 1, 0, 2, 2], L = [1, 1, 4]. Step 1: rank 2's experts 4 and 5
+    tie at 2 -> expert 4; ranks 0 and 1 tie as open ranks at load 1 -> rank
+    0 (lower index) gets expert 4, m = min(2 - 1, 2) = 1 -> loads [2, 1, 3].
+    Step 2: rank 2's heaviest is now expert 5 (2 > 1); the only open rank is
+    1: m = 1 -> loads [2, 2, 2]. Pass 1 keeps t1 (e1) on 0, t3 (e2) on 1, t4
+    (e4) and t5 (e5) on 2; pass 2 sends t0 (e5) to its replica on rank 1 and
+    t2 (e4) to its replica on rank 0 (lower index than home rank 2).
+    """
+    _check_golden("hand_example_destination_tie.json")
+
+
+def test_hand_example_surplus_order():
+    """P=3, 1 home expert each, R=1, K=1, 6 tokens, T = 2.
+
+    c = [3, 2, 1], L = [3, 2, 1]. Rank 0 gives expert 0 to rank 2 (the only
+    rank below T): m = min(2 - 1, 3) = 1, quotas e0: rank 0 two, rank 2 one.
+    Pass 1 keeps only t1 (e0 on its home). Pass 2 in token order: t0 (e2) to
+    rank 2; t2 (e0) to the lowest-index holder with quota left, rank 0; t3
+    (e0) then finds rank 0 full and goes to rank 2; t4, t5 (e1) to rank 1.
+    """
+    _check_golden("hand_example_surplus_order.json")
+
+
 # ---- invariants on every workload -------------------------------------------
 
 SMALL = ["tiny", "mixtral", "decode_drift"]
