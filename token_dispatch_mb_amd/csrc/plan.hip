@@ -94,6 +94,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // expert, which each rank lane keeps up to date in registers.
 //
 // EHM >= Eh: registers per lane for the home quotas of its rank.
+//
+// One basic block per move: the tournament for every lane's heaviest expert
+// (which only the previous donor's quota changed) sits next to the two load
+// reductions it does not depend on, so their dependency chains interleave;
+// the state updates are selects, and each move is recorded in the registers
+// of lane (move mod 64) and written to LDS 64 moves at a time.
 template <int EHM>
 __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
@@ -106,10 +112,13 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     q[j] = (rank_lane && j < Eh) ? m.c[lane * Eh + j] : 0;
     load += q[j];
   }
-  // Heaviest remaining home expert of this rank, lowest index on ties: a
-  // pairwise tournament (log2 EHM levels) so the compares of a level are
-  // independent of each other.
-  auto best = [&](int& bq, int& bj) {
+  const int lpre = load;
+  int used = 0, moves = 0, unbalanced = 0;
+  int rec_e = 0, rec_m = 0, rec_i = 0;  // the move recorded in this lane
+
+  for (;;) {
+    // Heaviest remaining home expert of this lane's rank, lowest index on
+    // ties: a pairwise tournament, log2(EHM) levels.
     int v[EHM], ix[EHM];
 #pragma unroll
     for (int j = 0; j < EHM; ++j) {
@@ -124,15 +133,8 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
         v[j] = right ? v[2 * j + 1] : v[2 * j];
         ix[j] = right ? ix[2 * j + 1] : ix[2 * j];
       }
-    bq = v[0];
-    bj = ix[0];
-  };
-  int bq, bj;
-  best(bq, bj);
-  const int lpre = load;
-  int used = 0, moves = 0, unbalanced = 0;
+    const int bq = v[0], bj = ix[0];
 
-  for (;;) {
     const bool open_lane = rank_lane && used < R && load < T;
     int lmax, lmin;
     wave_max_min_i32(rank_lane ? load : INT32_MIN, open_lane ? load : INT32_MAX, lmax, lmin);
@@ -147,23 +149,23 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     const int jb = __builtin_amdgcn_readlane(bj, rs);
     const int slot = __builtin_amdgcn_readlane(used, d);  // slots fill in index order
     const int mv = min(T - lmin, qmax);
-    const int e = rs * Eh + jb;
-    if (lane == 0) {
-      m.repE[d * R + slot] = e;
-      m.repM[d * R + slot] = mv;
-    }
-    if (lane == rs) {
-      load -= mv;
+    const int mi = moves & 63;
+    rec_e = lane == mi ? rs * Eh + jb : rec_e;
+    rec_m = lane == mi ? mv : rec_m;
+    rec_i = lane == mi ? d * R + slot : rec_i;
+    load += (lane == d ? mv : 0) - (lane == rs ? mv : 0);
+    used += lane == d ? 1 : 0;
 #pragma unroll
-      for (int j = 0; j < EHM; ++j)
-        if (j == jb) q[j] -= mv;
-      best(bq, bj);
-    }
-    if (lane == d) {
-      load += mv;
-      used += 1;
-    }
+    for (int j = 0; j < EHM; ++j) q[j] -= (lane == rs && j == jb) ? mv : 0;
     ++moves;
+    if ((moves & 63) == 0) {
+      m.repE[rec_i] = rec_e;
+      m.repM[rec_i] = rec_m;
+    }
+  }
+  if (lane < (moves & 63)) {
+    m.repE[rec_i] = rec_e;
+    m.repM[rec_i] = rec_m;
   }
   if (rank_lane) {
 #pragma unroll
