@@ -267,10 +267,10 @@ def test_round_trip_identity_experts():
 G_ROWS = 4099  # distinct expert-output rows, cycled over the buffer (prime)
 
 
-@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"])
+@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"] + W.configs.SWEEP_ORDER)
 def test_prefill_full_size(name):
-    """The full prefill workloads in the launch configuration the benchmark
-    times: the whole plan bit-exact; dispatched rows of three rank regions
+    """The full prefill and maxvio-sweep workloads in the launch configuration
+    the benchmark times: the whole plan bit-exact; dispatched rows of three rank regions
     and 2048 random rows bit-exact; combine of 1024 sampled tokens in
     tolerance. Expert outputs cycle through 4099 generated rows."""
     wl = W.get_workload(name)

@@ -164,9 +164,9 @@ def test_invariants_small_workloads(name):
     assert p.status[3] <= wl.n_ranks * wl.slots_per_rank
 
 
-@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"])
+@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"] + W.configs.SWEEP_ORDER)
 def test_invariants_prefill_plans(name):
-    """Full-size plans (1 M pairs) of the two prefill workloads."""
+    """Full-size plans (0.5-1 M pairs) of the prefill and maxvio-sweep workloads."""
     wl, ids, w, d, p = _plan_workload(name)
     dmat = C.check_counts(p, ids, wl.n_ranks, wl.n_experts)
     assert p.flags == 0
@@ -185,6 +185,30 @@ def test_dsv3_prefill_balance_target():
     """Post-plan rank imbalance at most 1.01 on the DeepSeek-V3-like prefill."""
     wl, ids, w, d, p = _plan_workload("dsv3_prefill")
     assert p.report["ir_after"] <= 1.01
+
+
+@pytest.mark.parametrize("name", W.configs.SWEEP_ORDER)
+def test_maxvio_sweep_holds_s_times_k(name):
+    """MoonEP's invariant at every skew of its sweep: with two replica slots
+    every rank receives exactly S*K rows; the reported maxvio is the routing's
+    (pairs per expert over their mean, minus one)."""
+    wl, ids, w, d, p = _plan_workload(name)
+    c = np.bincount(ids.ravel(), minlength=wl.n_experts)
+    assert p.report["maxvio"] == pytest.approx(c.max() / c.mean() - 1.0)
+    assert np.all(p.load_post == wl.cap)
+    assert p.report["ir_after"] == 1.0
+
+
+def test_maxvio_sweep_one_slot_breaks_at_high_skew():
+    """With one replica slot per rank the S*K regions overflow at maxvio 10
+    (UNBALANCED and CAPACITY), which is why the sweep uses two."""
+    wl = W.get_workload("moonep_maxvio_10")
+    ids, _ = W.routing_for(wl)
+    d = O.make_dims(wl.n_tokens, wl.top_k, wl.n_experts, wl.n_ranks, 1, wl.hidden,
+                    dtype_in=wl.dtype_in, dtype_out=wl.dtype_out)
+    p = O.plan(d, ids)
+    assert p.flags == O.ST_UNBALANCED | O.ST_CAPACITY
+    assert p.status[2] > wl.cap
 
 
 def test_decode_drift_sequence_invariants():

@@ -100,7 +100,7 @@ def test_fp8_rows_scales_and_dequant():
 
 
 def test_workloads_recipe():
-    for name in W.configs.ORDER:
+    for name in W.configs.ORDER + W.configs.SWEEP_ORDER:
         wl = W.get_workload(name)
         assert wl.n_tokens % wl.n_ranks == 0 and wl.n_experts % wl.n_ranks == 0
         assert wl.cap == wl.tokens_per_rank * wl.top_k
@@ -119,3 +119,15 @@ def test_prefill_skew_near_targets(name):
     else:
         assert abs(st["top4_share"] - 0.13) < 0.01
         assert abs(st["ir_before"] - 1.45) < 0.05
+
+
+@pytest.mark.parametrize("name", W.configs.SWEEP_ORDER)
+def test_maxvio_sweep_targets(name):
+    """The MoonEP-shaped sweep reaches its maxvio target from the routing
+    alone (max over mean routed pairs per expert, minus one)."""
+    wl = W.get_workload(name)
+    ids, _ = W.routing_for(wl)
+    c = np.bincount(ids.ravel(), minlength=wl.n_experts)
+    maxvio = c.max() / c.mean() - 1.0
+    target = wl.targets["maxvio"]
+    assert abs(maxvio - target) < 0.01 * target

@@ -21,6 +21,13 @@ Sizes, and the statistic each workload is shaped to hit:
 * kimi_prefill: the four hottest of 384 experts take about 13 % of the
   assignments and max/mean rank load is about 1.45 before planning
   (ISER-MoE, Background and Key Observation 1).
+* moonep_maxvio_{0p2,1,10,20}: MoonEP's benchmark shape (8 ranks x 8192
+  tokens, 384 experts, top-8, H = 7168) at the four skew targets its sweep
+  uses, maxvio = max_e c_e / mean_e c_e - 1 = 0.2, 1, 10 and 20 (MoonEP
+  blog, "Benchmarks and the repo's claims" and the metric definitions).
+  beta is where the routing crosses the target (to 1e-4, by bisection at
+  seed 6000; ``workload/tune.py``). Two replica slots per rank: with one, the
+  planner cannot hold every rank to S * K at maxvio 10 and 20.
 """
 from __future__ import annotations
 
@@ -102,11 +109,25 @@ WORKLOADS: dict[str, Workload] = {
     ),
 }
 
+MAXVIO_SWEEP = {"moonep_maxvio_0p2": (0.2, 0.0158), "moonep_maxvio_1": (1.0, 0.0654),
+                "moonep_maxvio_10": (10.0, 0.2822), "moonep_maxvio_20": (20.0, 0.4236)}
+for _name, (_target, _beta) in MAXVIO_SWEEP.items():
+    WORKLOADS[_name] = Workload(
+        name=_name, n_tokens=65536, n_experts=384, top_k=8, n_ranks=8, slots_per_rank=2,
+        hidden=7168, dtype_in="bf16", dtype_out="bf16", noise=0, zipf_s=1.0, beta=_beta,
+        seed=6000,
+        note=f"8 ranks x 8192 tokens, 384 experts (48 home per rank), top-8, 2 slots, "
+             f"bf16 H=7168, maxvio {_target}",
+        targets={"maxvio": _target},
+    )
+
 ORDER = ["tiny", "mixtral", "dsv3_prefill", "kimi_prefill", "decode_drift"]
+SWEEP_ORDER = list(MAXVIO_SWEEP)
 
 
 def get_workload(name: str) -> Workload:
     try:
         return WORKLOADS[name]
     except KeyError:
-        raise KeyError(f"unknown workload {name!r}; known: {', '.join(ORDER)}") from None
+        raise KeyError(f"unknown workload {name!r}; known: "
+                       f"{', '.join(ORDER + SWEEP_ORDER)}") from None

@@ -10,7 +10,13 @@ then into groups of ranks. It never runs the planner.
 * kimi_prefill: aim for a 13 % share of the four hottest experts and a
   max/mean rank load of 1.45 (ISER-MoE, Background and Key Observation 1).
 
+* moonep_maxvio_*: MoonEP's benchmark shape (8 ranks x 8192 tokens, 384
+  experts, top-8) at maxvio = max_e c_e / mean_e c_e - 1 of 0.2, 1, 10 and
+  20 ("Benchmarks and the repo's claims"); beta by bisection at a fixed
+  seed (maxvio grows with beta under this routing model).
+
 Usage: python -m workload.tune [dsv3_prefill|kimi_prefill] [n_seeds]
+       python -m workload.tune maxvio
 Prints one line per candidate improving the objective, then the choice.
 """
 from __future__ import annotations
@@ -65,7 +71,30 @@ def search(name: str, n_seeds: int = 16) -> tuple[float, int, dict]:
     return best[1], best[2], best[3]
 
 
+def maxvio_beta(target: float, seed: int = 6000, n_tokens: int = 65536, n_experts: int = 384,
+                top_k: int = 8, n_ranks: int = 8, iters: int = 30) -> tuple[float, dict]:
+    """beta (to 1e-4) at which the routing crosses the target maxvio."""
+    lo, hi = 0.0, 2.0
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        ids, _ = W.routing(n_tokens, n_experts, top_k, 0, 1.0, mid, seed)
+        if routing_stats(ids, n_experts, n_ranks)["maxvio"] < target:
+            lo = mid
+        else:
+            hi = mid
+        if hi - lo < 1e-4:
+            break
+    beta = round(hi, 4)
+    ids, _ = W.routing(n_tokens, n_experts, top_k, 0, 1.0, beta, seed)
+    return beta, routing_stats(ids, n_experts, n_ranks)
+
+
 if __name__ == "__main__":
+    if sys.argv[1:2] == ["maxvio"]:
+        for target in (0.2, 1.0, 10.0, 20.0):
+            beta, st = maxvio_beta(target)
+            print(f"CHOICE maxvio {target}: beta={beta} {st}", flush=True)
+        sys.exit(0)
     names = sys.argv[1:2] or ["dsv3_prefill", "kimi_prefill"]
     n = int(sys.argv[2]) if len(sys.argv) > 2 else 16
     for nm in names:
