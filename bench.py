@@ -74,6 +74,15 @@ def measured_traffic(kernel: str, workload: str):
     return float(m.group(1)) if m else None
 
 
+def _speed_ratio(load, speeds, wl):
+    """max_r load_r / (N*K * s_r / sum s): a rank's rows over its share in
+    proportion to its speed (1 = every rank finishes together)."""
+    import numpy as np
+
+    share = wl.n_tokens * wl.top_k * speeds.astype(np.float64) / float(speeds.sum())
+    return (load / share).max()
+
+
 def cpu_baseline(wl, fraction: int = 2) -> dict:
     """The CPU oracle as it stands (single thread) on 1/fraction of the
     tokens of the same workload: plan, dispatch and combine; GB/s over the
@@ -97,8 +106,9 @@ def cpu_baseline(wl, fraction: int = 2) -> dict:
     y64.fill(0.0)
     mag = np.empty_like(y64)
     mag.fill(0.0)
+    speeds = W.rank_speeds(wl)
     t0 = time.perf_counter()
-    p = O.plan(od, ids)
+    p = O.plan(od, ids, speeds=speeds)
     t1 = time.perf_counter()
     O.dispatch(od, p, x, xs, out=buf)
     t2 = time.perf_counter()
@@ -116,7 +126,7 @@ def cpu_baseline(wl, fraction: int = 2) -> dict:
     ab = algorithmic_bytes(sub)
     full_ids, _ = W.routing_for(wl)
     f0 = time.perf_counter()
-    O.plan(O.dims_for(wl), full_ids)
+    O.plan(O.dims_for(wl), full_ids, speeds=speeds)
     f1 = time.perf_counter()
     return {
         "value": round((ab["dispatch"] + ab["combine"]) / ((t2 - t1) + (t4 - t3)) / 1e9, 3),
@@ -203,9 +213,18 @@ def main() -> int:
     y_exp = torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
     y = torch.empty((wl.n_tokens, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
 
+    # Rank speeds of a workload planned against per-rank targets (None: the
+    # single water level). For comparison, the equal-target plan's largest
+    # ratio of load to the speed-proportional share, outside the timing.
+    speeds = W.rank_speeds(wl)
+    wir_equal = None
+    if speeds is not None:
+        mb.plan(dims, ids_d, ws, bufs)
+        wir_equal = float(_speed_ratio(bufs.load_post.cpu().numpy(), speeds, wl))
+
     # Expert outputs: the dispatched rows (identity experts), or for fp8
     # rows a generated bf16 buffer.
-    mb.plan(dims, ids_d, ws, bufs)
+    mb.plan(dims, ids_d, ws, bufs, speeds=speeds)
     if wl.dtype_in == wl.dtype_out:
         mb.dispatch(dims, bufs, x_d, y_exp, xs_d, bs)
     else:
@@ -217,7 +236,7 @@ def main() -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        mb.plan(dims, ids_d, ws, bufs)
+        mb.plan(dims, ids_d, ws, bufs, speeds=speeds)
         if ev is not None:
             ev[1].record()
         mb.dispatch(dims, bufs, x_d, buf, xs_d, bs)
@@ -295,6 +314,9 @@ def main() -> int:
         "plan_status": {"flags": int(status[0]), "water_level": int(status[1]),
                         "max_load": int(status[2]), "moves": int(status[3]),
                         "ir_after": round(float(status[2]) / mean_load, 5)},
+        "speed_targets": None if speeds is None else {
+            "max_load_over_share": round(float(_speed_ratio(bufs.load_post.cpu().numpy(), speeds, wl)), 5),
+            "same_with_equal_targets": round(wir_equal, 5)},
         "wall_s_timed": round(t_wall, 4),
         "roofline": {
             "kernel": dominant,

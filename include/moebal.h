@@ -29,6 +29,9 @@
  *           planner-made cu_seqlens, fixed-shape expert-grouped buffers,
  *           no host synchronisation) and "Implementation details"
  *           (home experts then prefetch slots in one numbering).
+ *  [ViBE]   ViBE summary (picx.dev/p/p7vJoN), Methodology, Variability-
+ *           Informed Expert Placement (token targets in proportion to GPU
+ *           speed; experts go to the GPU farthest below its target).
  *
  * Conventions
  *  - Every buffer is owned by the caller and lives in device memory unless
@@ -83,10 +86,13 @@ enum mb_error {
 enum mb_status_flag {
   MB_ST_BAD_ID = 1,     /* an id outside [0, E) (fatal) */
   MB_ST_DUP_ID = 2,     /* a token lists one expert twice (fatal) */
-  MB_ST_UNBALANCED = 4, /* placement stopped with a rank above T (not fatal) */
+  MB_ST_UNBALANCED = 4, /* placement stopped with a rank above its target (not fatal) */
   MB_ST_CAPACITY = 8    /* a rank needs more than cap rows (fatal) */
 };
 #define MB_ST_FATAL (MB_ST_BAD_ID | MB_ST_DUP_ID | MB_ST_CAPACITY)
+
+/* Largest rank speed accepted by mb_plan_weighted. */
+#define MB_MAX_SPEED (1 << 20)
 
 /* Problem sizes of one MoE layer call. */
 typedef struct mb_dims {
@@ -114,7 +120,8 @@ typedef struct mb_dims {
  *   pos[N*K]            dispatch row of pair (t, k), in [0, P*cap) (may be
  *                       NULL when N == 0)
  *   row_src[P*cap]      token of each dispatch row, -1 for padding rows
- *   status[4]           {flags (mb_status_flag), T, max_r load_post, moves}
+ *   status[4]           {flags (mb_status_flag), T, max_r load_post, moves};
+ *                       from mb_plan_weighted, T is the largest target tau_r
  */
 typedef struct mb_plan_bufs {
   int32_t* counts;
@@ -162,6 +169,26 @@ size_t mb_plan_workspace_bytes(const mb_dims* dims);
  */
 int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws_bytes,
             const mb_plan_bufs* out, hipStream_t stream);
+
+/*
+ * mb_plan with per-rank targets in place of the single water level [ViBE,
+ * Variability-Informed Expert Placement]: rank r of speed s_r aims at
+ *   tau_r = ceil(N*K * s_r / sum_h s_h)
+ * rows. The busiest rank is the one farthest above its target (largest
+ * load - tau), a move's destination the eligible rank farthest below its
+ * own (largest tau - load), and a move gives min(tau_dst - load_dst,
+ * remaining home quota) pairs; everything else is as in mb_plan, which is
+ * this call with equal speeds.
+ *  rank_speed  [P] int32 HOST array, each in [1, MB_MAX_SPEED] (relative
+ *              throughput, e.g. the inverse of a rank's measured latency at
+ *              a reference load, scaled to integers); read during the call
+ *              only. NULL or a value out of range -> MB_ERR_INVALID_ARG.
+ * Fast ranks' targets exceed N*K/P: size cap to at least the largest
+ * target, or the plan reports MB_ST_CAPACITY.
+ */
+int mb_plan_weighted(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
+                     void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out,
+                     hipStream_t stream);
 
 /*
  * Dispatch [MoonEP, "What MoonEP enforces and how": tokens written into

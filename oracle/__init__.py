@@ -53,7 +53,8 @@ class Report(ctypes.Structure):
                 ("maxvio", ctypes.c_double), ("excess_removed", ctypes.c_double),
                 ("water_level", ctypes.c_int64), ("n_moves", ctypes.c_int64),
                 ("slots_used", ctypes.c_int64), ("excess_before", ctypes.c_int64),
-                ("offhome_pairs", ctypes.c_int64), ("nonlocal_pairs", ctypes.c_int64)]
+                ("offhome_pairs", ctypes.c_int64), ("nonlocal_pairs", ctypes.c_int64),
+                ("wir_before", ctypes.c_double), ("wir_after", ctypes.c_double)]
 
 
 _lib = None
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.mbref_plan.argtypes = [ctypes.POINTER(Dims), vp, ctypes.c_int32,
                                  ctypes.POINTER(PlanOut), ctypes.POINTER(Report)]
         L.mbref_plan.restype = ctypes.c_int
+        L.mbref_plan_weighted.argtypes = [ctypes.POINTER(Dims), vp, vp, ctypes.c_int32,
+                                          ctypes.POINTER(PlanOut), ctypes.POINTER(Report)]
+        L.mbref_plan_weighted.restype = ctypes.c_int
         L.mbref_dispatch.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp]
         L.mbref_dispatch.restype = ctypes.c_int
         L.mbref_dispatch_window.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp,
@@ -93,8 +97,10 @@ def make_dims(n_tokens, top_k, n_experts, n_ranks, slots_per_rank, hidden, cap=N
 
 def dims_for(wl, cap=None, n_tokens=None) -> Dims:
     n = wl.n_tokens if n_tokens is None else n_tokens
+    if cap is None:
+        cap = wl.cap if n_tokens is None else (n // wl.n_ranks) * wl.top_k
     return make_dims(n, wl.top_k, wl.n_experts, wl.n_ranks, wl.slots_per_rank, wl.hidden,
-                     cap=cap if cap is not None else (n // wl.n_ranks) * wl.top_k,
+                     cap=cap,
                      dtype_in=wl.dtype_in, dtype_out=wl.dtype_out)
 
 
@@ -122,7 +128,10 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def plan(dims: Dims, ids: np.ndarray, move_rule: int = MOVE_FILL_HOST) -> Plan:
+def plan(dims: Dims, ids: np.ndarray, move_rule: int = MOVE_FILL_HOST,
+         speeds: np.ndarray | None = None) -> Plan:
+    """Steps O0-O4 and O7. ``speeds`` (int32 [P]) gives per-rank targets in
+    proportion to rank speed in place of the single water level."""
     N, K, E, P, R = dims.n_tokens, dims.top_k, dims.n_experts, dims.n_ranks, dims.slots_per_rank
     ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(N, K)
     eh = E // P if P > 0 else 0
@@ -136,16 +145,23 @@ def plan(dims: Dims, ids: np.ndarray, move_rule: int = MOVE_FILL_HOST) -> Plan:
     }
     po = PlanOut(**{k: v.ctypes.data_as(_i32p) for k, v in a.items()})
     rep = Report()
-    rc = lib().mbref_plan(ctypes.byref(dims), _ptr(ids), move_rule, ctypes.byref(po),
-                          ctypes.byref(rep))
+    if speeds is None:
+        rc = lib().mbref_plan(ctypes.byref(dims), _ptr(ids), move_rule, ctypes.byref(po),
+                              ctypes.byref(rep))
+    else:
+        sp = np.ascontiguousarray(speeds, dtype=np.int32)
+        assert sp.shape == (P,)
+        rc = lib().mbref_plan_weighted(ctypes.byref(dims), _ptr(ids), _ptr(sp), move_rule,
+                                       ctypes.byref(po), ctypes.byref(rep))
     if rc != 0:
         raise ValueError(f"mbref_plan returned {rc}")
     report = {n: getattr(rep, n) for n, _ in Report._fields_}
     return Plan(dims=dims, report=report, **a)
 
 
-def plan_rc(dims: Dims, ids: np.ndarray) -> int:
-    """Return code of mbref_plan alone (for invalid-size checks)."""
+def plan_rc(dims: Dims, ids: np.ndarray, speeds: np.ndarray | None = None) -> int:
+    """Return code of mbref_plan (or mbref_plan_weighted) alone, for invalid
+    sizes and speeds."""
     N = max(dims.n_tokens, 0)
     K = max(dims.top_k, 0)
     P = max(dims.n_ranks, 1)
@@ -155,7 +171,11 @@ def plan_rc(dims: Dims, ids: np.ndarray) -> int:
     bufs = [np.zeros(big, np.int32) for _ in range(10)]
     po = PlanOut(*[b.ctypes.data_as(_i32p) for b in bufs])
     ids = np.ascontiguousarray(ids, dtype=np.int32)
-    return lib().mbref_plan(ctypes.byref(dims), _ptr(ids), 0, ctypes.byref(po), None)
+    if speeds is None:
+        return lib().mbref_plan(ctypes.byref(dims), _ptr(ids), 0, ctypes.byref(po), None)
+    sp = np.ascontiguousarray(speeds, dtype=np.int32)
+    return lib().mbref_plan_weighted(ctypes.byref(dims), _ptr(ids), _ptr(sp), 0,
+                                     ctypes.byref(po), None)
 
 
 def row_bytes_in(dims: Dims) -> int:

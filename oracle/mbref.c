@@ -24,16 +24,25 @@
  *           indexed by planner-made cu_seqlens; "Variables and core terms":
  *           maxvio; "Implementation details": home experts, then prefetch
  *           rows, in one [E+B, H, H'] numbering.
+ *  [ViBE]   ViBE summary (picx.dev/p/p7vJoN) — Methodology, Variability-
+ *           Informed Expert Placement: a token target per GPU in proportion
+ *           to its speed, and experts go to the GPU farthest below its
+ *           target.
  *
  * Readings taken where the pages leave a step open (each one is also listed
  * with its reason in the design notes of the repository):
  *  - token t originates on rank t / S; expert e is homed on rank e / Eh;
  *  - L_r counts (token, expert) pairs whose expert is homed on r, so
  *    T = ceil(N*K / P) = S*K;
+ *  - with rank speeds s_r, rank r's target is tau_r = ceil(N*K*s_r / sum s)
+ *    (integer speeds, so the targets are exact); the busiest rank is the one
+ *    farthest above its target and the destination the one farthest below
+ *    its own. With equal speeds every tau_r = T and these are the busiest
+ *    and least loaded ranks;
  *  - ties: busiest rank -> lowest index; heaviest expert -> largest remaining
  *    home quota, then lowest id; destination -> least loaded, then lowest
  *    index; replica slot -> lowest free index;
- *  - a move gives the destination min(T - load[dst], remaining home quota)
+ *  - a move gives the destination min(tau - load[dst], remaining home quota)
  *    pairs (it fills the host's spare quota); MBREF_MOVE_EXCESS_ONLY also
  *    caps it at the busiest rank's excess, for comparison only;
  *  - if the busiest rank's heaviest expert has no eligible destination its
@@ -76,14 +85,33 @@ static int valid_dims(const mbref_dims* d) {
 
 int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
                mbref_plan_out* o, mbref_report* rep) {
+  return mbref_plan_weighted(dm, ids, NULL, move_rule, o, rep);
+}
+
+int mbref_plan_weighted(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
+                        int32_t move_rule, mbref_plan_out* o, mbref_report* rep) {
   if (!dm || !o || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
   if (move_rule != MBREF_MOVE_FILL_HOST && move_rule != MBREF_MOVE_EXCESS_ONLY)
     return MBREF_ERR_INVALID_ARG;
   const int64_t N = dm->n_tokens, K = dm->top_k, E = dm->n_experts;
   const int64_t P = dm->n_ranks, R = dm->slots_per_rank, cap = dm->cap;
   const int64_t S = N / P, Eh = E / P, NS = Eh + R;
-  /* [ISER] Objective 1: T = ceil(sum_r L_r / P); sum_r L_r = N*K. */
-  const int64_t T = (N * K + P - 1) / P;
+  if (speed)
+    for (int64_t r = 0; r < P; ++r)
+      if (speed[r] < 1 || speed[r] > MBREF_MAX_SPEED) return MBREF_ERR_INVALID_ARG;
+  /* [ISER] Objective 1: T = ceil(sum_r L_r / P); sum_r L_r = N*K.
+   * [ViBE] token target tau_r = (total load) * s_r / sum_h s_h, rounded up;
+   * equal speeds give tau_r = T. */
+  int64_t* tau = calloc((size_t)(P > 0 ? P : 1), sizeof(int64_t)); /* tau_r */
+  if (!tau) return MBREF_ERR_NOMEM;
+  int64_t sum_s = 0;
+  for (int64_t r = 0; r < P; ++r) sum_s += speed ? speed[r] : 1;
+  int64_t T = 0; /* the largest target */
+  for (int64_t r = 0; r < P; ++r) {
+    const int64_t sr = speed ? speed[r] : 1;
+    tau[r] = (N * K * sr + sum_s - 1) / sum_s;
+    if (tau[r] > T) T = tau[r];
+  }
 
   memset(o->counts, 0, sizeof(int32_t) * P * E);
   memset(o->load_pre, 0, sizeof(int32_t) * P);
@@ -111,6 +139,7 @@ int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
     }
   if (flags) {
     o->status[0] = flags;
+    free(tau);
     return MBREF_OK;
   }
 
@@ -157,10 +186,10 @@ int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
   int64_t moves = 0;
   int unbalanced = 0;
   for (;;) {
-    int64_t rs = 0; /* busiest rank, lowest index on ties */
+    int64_t rs = 0; /* busiest rank (farthest above its target), lowest index on ties */
     for (int64_t r = 1; r < P; ++r)
-      if (load[r] > load[rs]) rs = r;
-    if (load[rs] <= T) break;
+      if (load[r] - tau[r] > load[rs] - tau[rs]) rs = r;
+    if (load[rs] <= tau[rs]) break;
     memset(tried, 0, (size_t)Eh);
     int moved = 0;
     for (;;) {
@@ -172,18 +201,20 @@ int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
       }
       if (best < 0) break;
       tried[best - rs * Eh] = 1;
-      int64_t dst = -1; /* least loaded eligible rank, lowest index on ties */
+      /* eligible rank farthest below its target (the least loaded one when
+       * targets are equal), lowest index on ties */
+      int64_t dst = -1;
       for (int64_t r = 0; r < P; ++r) {
         int64_t nfree = 0;
         for (int64_t j = 0; j < R; ++j)
           if (o->rep_expert[r * R + j] < 0) ++nfree;
-        if (nfree == 0 || load[r] >= T || is_host[best * P + r]) continue;
-        if (dst < 0 || load[r] < load[dst]) dst = r;
+        if (nfree == 0 || load[r] >= tau[r] || is_host[best * P + r]) continue;
+        if (dst < 0 || tau[r] - load[r] > tau[dst] - load[dst]) dst = r;
       }
       if (dst < 0) continue;
-      int64_t m = T - load[dst];
+      int64_t m = tau[dst] - load[dst];
       if (qh[best] < m) m = qh[best];
-      if (move_rule == MBREF_MOVE_EXCESS_ONLY && load[rs] - T < m) m = load[rs] - T;
+      if (move_rule == MBREF_MOVE_EXCESS_ONLY && load[rs] - tau[rs] < m) m = load[rs] - tau[rs];
       int64_t j = 0; /* smallest free slot index */
       while (o->rep_expert[dst * R + j] >= 0) ++j;
       o->rep_expert[dst * R + j] = (int32_t)best;
@@ -290,7 +321,15 @@ int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
     int64_t maxL = 0, maxc = 0;
     for (int64_t r = 0; r < P; ++r) {
       if (L[r] > maxL) maxL = L[r];
-      if (L[r] > T) rep->excess_before += L[r] - T;
+      if (L[r] > tau[r]) rep->excess_before += L[r] - tau[r];
+    }
+    /* the same ratios against each rank's unrounded target
+     * tau*_r = N*K*s_r / sum s (no pairs: balanced) */
+    rep->wir_before = rep->wir_after = N * K > 0 ? 0.0 : 1.0;
+    for (int64_t r = 0; r < P && N * K > 0; ++r) {
+      const double ts = (double)(N * K) * (double)(speed ? speed[r] : 1) / (double)sum_s;
+      if (L[r] / ts > rep->wir_before) rep->wir_before = L[r] / ts;
+      if (o->load_post[r] / ts > rep->wir_after) rep->wir_after = o->load_post[r] / ts;
     }
     for (int64_t e = 0; e < E; ++e)
       if (c[e] > maxc) maxc = c[e];
@@ -313,7 +352,7 @@ int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
 
 done:
   free(c); free(L); free(load); free(qh); free(rq); free(is_host); free(tried);
-  free(Q); free(used); free(slot_of); free(rows); free(cu); free(fill);
+  free(Q); free(used); free(slot_of); free(rows); free(cu); free(fill); free(tau);
   return rc;
 }
 

@@ -22,6 +22,8 @@
  *   row_src[P*cap]                        token of each row, -1 for padding
  *   host[N][K]                            rank serving each pair
  *   status[4]                             {flags, T, max load_post, moves}
+ *                                         (T = the largest target tau_r when
+ *                                         planned with rank speeds)
  */
 #ifndef MBREF_H
 #define MBREF_H
@@ -45,13 +47,16 @@ enum {
 enum {
   MBREF_ST_BAD_ID = 1,     /* an id outside [0, E) */
   MBREF_ST_DUP_ID = 2,     /* an expert listed twice for one token */
-  MBREF_ST_UNBALANCED = 4, /* placement stopped with a rank above T */
+  MBREF_ST_UNBALANCED = 4, /* placement stopped with a rank above its target */
   MBREF_ST_CAPACITY = 8    /* a rank needs more than cap rows */
 };
 #define MBREF_ST_FATAL (MBREF_ST_BAD_ID | MBREF_ST_DUP_ID | MBREF_ST_CAPACITY)
 
 /* Move size rule of a placement step (see mbref.c, step O2). */
 enum { MBREF_MOVE_FILL_HOST = 0, MBREF_MOVE_EXCESS_ONLY = 1 };
+
+/* Largest rank speed accepted by mbref_plan_weighted. */
+#define MBREF_MAX_SPEED (1 << 20)
 
 typedef struct mbref_dims {
   int32_t n_tokens;       /* N */
@@ -89,6 +94,8 @@ typedef struct mbref_report {
   int64_t excess_before; /* sum_r (L_r - T)^+ */
   int64_t offhome_pairs; /* pairs served by a rank other than home(e) */
   int64_t nonlocal_pairs;/* pairs served by a rank other than src(t) */
+  double wir_before;     /* max_r L_r / tau*_r, tau*_r = N*K*s_r / sum s */
+  double wir_after;      /* max_r load_post / tau*_r */
 } mbref_report;
 
 int mbref_version(void);
@@ -98,6 +105,13 @@ int mbref_version(void);
  * negative error for invalid sizes. */
 int mbref_plan(const mbref_dims* dims, const int32_t* ids, int32_t move_rule,
                mbref_plan_out* out, mbref_report* report);
+
+/* The same with per-rank targets tau_r = ceil(N*K*s_r / sum_h s_h) in place
+ * of the single water level (speed[P], each in [1, MBREF_MAX_SPEED]; NULL
+ * means equal speeds, which is mbref_plan). */
+int mbref_plan_weighted(const mbref_dims* dims, const int32_t* ids,
+                        const int32_t* speed, int32_t move_rule,
+                        mbref_plan_out* out, mbref_report* report);
 
 /* Step O5: buf[pos[t][k]] = x[t] (and the fp8 scale row). Rows of buf that
  * no pair maps to are left untouched. Returns 1 if status is fatal (nothing

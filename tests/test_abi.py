@@ -99,3 +99,23 @@ def test_small_workspace_and_null_pointers_rejected():
     assert rc == mb.ERR_INVALID_ARG
     rc = mb.raw_call("mb_plan_status", None, None, None)
     assert rc == mb.ERR_INVALID_ARG
+
+
+def test_weighted_plan_speed_checks():
+    """mb_plan_weighted rejects a missing or out-of-range speed array on the
+    host; valid speeds get as far as the workspace check."""
+    d = mb.Dims.make(64, 2, 16, 4, 1, 128)
+    need = mb.workspace_bytes(d)
+    fake = ctypes.c_void_p(1 << 20)
+    bufs = mb._PlanBufsC(*([1 << 20] * 9))
+    I4 = ctypes.c_int32 * 4
+    rc = mb.raw_call("mb_plan_weighted", ctypes.byref(d), fake, None, fake, need,
+                     ctypes.byref(bufs), None)
+    assert rc == mb.ERR_INVALID_ARG
+    for bad in ((0, 1, 1, 1), (1, -3, 1, 1), (1, 1, 1, mb.MAX_SPEED + 1)):
+        rc = mb.raw_call("mb_plan_weighted", ctypes.byref(d), fake, I4(*bad), fake, need,
+                         ctypes.byref(bufs), None)
+        assert rc == mb.ERR_INVALID_ARG, bad
+    rc = mb.raw_call("mb_plan_weighted", ctypes.byref(d), fake, I4(3, 1, mb.MAX_SPEED, 2), fake,
+                     need - 1, ctypes.byref(bufs), None)
+    assert rc == mb.ERR_WORKSPACE

@@ -34,13 +34,13 @@ def _y_exp_rows(wl_seed: int, dims, n_rows: int):
     return W.rows_bf16(wl_seed, W.TAG_YEXP, dims.hidden, n=n_rows)
 
 
-def _full_check(dims_g, od, ids, w, x, xs, y_exp, label=""):
+def _full_check(dims_g, od, ids, w, x, xs, y_exp, label="", speeds=None):
     """Plan, dispatch and combine on the GPU; compare everything with the oracle."""
     G.log(f"case {label}: N={od.n_tokens} K={od.top_k} E={od.n_experts} P={od.n_ranks} "
           f"R={od.slots_per_rank} H={od.hidden} cap={od.cap}")
-    gp = G.GpuPlan(dims_g).run(ids)
+    gp = G.GpuPlan(dims_g).run(ids, speeds=speeds)
     got = gp.fetch()
-    ref = O.plan(od, ids)
+    ref = O.plan(od, ids, speeds=speeds)
     G.assert_plan_equal(got, ref)
     buf, bs, y = G.run_rows(dims_g, gp, x, xs, y_exp, w)
     fatal = bool(ref.status[0] & O.ST_FATAL)
@@ -267,7 +267,7 @@ def test_round_trip_identity_experts():
 G_ROWS = 4099  # distinct expert-output rows, cycled over the buffer (prime)
 
 
-@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"] + W.configs.SWEEP_ORDER)
+@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"] + W.configs.EXTRA_ORDER)
 def test_prefill_full_size(name):
     """The full prefill and maxvio-sweep workloads in the launch configuration
     the benchmark times: the whole plan bit-exact; dispatched rows of three rank regions
@@ -277,12 +277,14 @@ def test_prefill_full_size(name):
     dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
     G.log(f"{name}: routing")
     ids, w = W.routing_for(wl)
-    ref = O.plan(od, ids)
-    gp = G.GpuPlan(dg).run(ids)
+    speeds = W.rank_speeds(wl)
+    ref = O.plan(od, ids, speeds=speeds)
+    gp = G.GpuPlan(dg).run(ids, speeds=speeds)
     got = gp.fetch()
     G.assert_plan_equal(got, ref)
-    assert ref.status[0] == 0 and ref.report["ir_after"] <= 1.01
-    G.log(f"{name}: plan bit-exact (IR {ref.report['ir_before']:.3f} -> {ref.report['ir_after']:.4f})")
+    assert ref.status[0] == 0 and ref.report["wir_after"] <= 1.01
+    G.log(f"{name}: plan bit-exact (IR {ref.report['ir_before']:.3f} -> {ref.report['ir_after']:.4f}, "
+          f"against speed targets {ref.report['wir_before']:.3f} -> {ref.report['wir_after']:.4f})")
 
     x, _ = W.token_rows(wl)
     d = G.dev()
@@ -349,3 +351,73 @@ def test_hand_examples_on_gpu(golden):
         assert np.array_equal(got[key].reshape(np.array(exp[key]).shape), np.array(exp[key])), key
     assert np.array_equal(got["pos"].ravel(), exp["pos"])
     G.assert_plan_equal(got, O.plan(O.make_dims(**dd, dtype_in="bf16", dtype_out="bf16"), ids))
+
+
+def test_hand_example_weighted_on_gpu():
+    """The hand-derived example with rank speeds [4, 4, 2, 1] through
+    mb_plan_weighted equals its stored values (and the oracle's)."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "hand_example_weighted.json")))
+    dd = dict(g["dims"])
+    dd["hidden"] = 8
+    ids = np.array(g["ids"], np.int32).reshape(dd["n_tokens"], dd["top_k"])
+    dg = mb.Dims.make(**dd, dtype_in="bf16", dtype_out="bf16")
+    got = G.GpuPlan(dg).run(ids, speeds=g["speeds"]).fetch()
+    for key in ("counts", "load_pre", "load_post", "rep_expert", "slot_quota", "cu_seqlens",
+                "row_src", "status"):
+        assert np.array_equal(got[key].reshape(np.array(g[key]).shape), np.array(g[key])), key
+    assert np.array_equal(got["pos"].ravel(), g["pos"])
+    G.assert_plan_equal(got, O.plan(O.make_dims(**dd, dtype_in="bf16", dtype_out="bf16"), ids,
+                                    speeds=np.array(g["speeds"], np.int32)))
+
+
+def _speed_cases():
+    rng = np.random.default_rng(77)
+    cases = []
+    for P in (1, 3, 8, 32, 64):
+        for R in (0, 1, 3):
+            eh = min(int(rng.choice([1, 5, 24, 40])), 1024 // P)  # E <= 1024
+            K = min(int(rng.choice([1, 4, 8])), P * eh)
+            S = int(rng.choice([5, 64, 301]))
+            kind = str(rng.choice(["narrow", "wide", "extreme"]))
+            cases.append((P, eh, K, R, S, kind))
+    return cases
+
+
+@pytest.mark.parametrize("P,eh,K,R,S,kind", _speed_cases())
+def test_weighted_shape_sweep(P, eh, K, R, S, kind):
+    """mb_plan_weighted against the oracle over shapes and speed spreads:
+    narrow (within 15 %), wide (up to 8x) and extreme (1 and 2^20 mixed,
+    where slow ranks get targets near zero)."""
+    E, N = P * eh, P * S
+    ids, w = W.routing(N, E, K, W.NOISE_NORMAL, 1.0, 0.8, 9000 + P * 31 + R * 7 + K)
+    rng = np.random.default_rng(P * 100 + R)
+    if kind == "narrow":
+        speeds = rng.integers(57000, 65537, P)
+    elif kind == "wide":
+        speeds = rng.integers(1000, 8001, P)
+    else:
+        speeds = np.where(rng.random(P) < 0.5, 1, mb.MAX_SPEED)
+    speeds = speeds.astype(np.int32)
+    cap = 2 * S * K if R > 0 else N * K
+    H = 64
+    dg = mb.Dims.make(N, K, E, P, R, H, cap=cap, dtype_in="f32", dtype_out="f32")
+    od = O.make_dims(N, K, E, P, R, H, cap=cap, dtype_in="f32", dtype_out="f32")
+    x = W.rows_f32(P * 1000 + S, W.TAG_X, H, n=N)
+    ye = W.rows_f32(P * 1000 + S, W.TAG_YEXP, H, n=P * cap)
+    _full_check(dg, od, ids, w, x, xs=None, y_exp=ye,
+                label=f"weighted P{P} Eh{eh} K{K} R{R} S{S} {kind}", speeds=speeds)
+
+
+def test_equal_speeds_match_mb_plan():
+    """mb_plan_weighted with equal speeds writes exactly what mb_plan writes."""
+    wl = W.get_workload("kimi_prefill").scaled(16384)
+    ids, _ = W.routing_for(wl)
+    dg = mb.Dims.for_workload(wl, cap=2 * wl.cap)
+    a = G.GpuPlan(dg).run(ids).fetch()
+    b = G.GpuPlan(dg).run(ids, speeds=[977] * wl.n_ranks).fetch()
+    for k in G.PLAN_FIELDS:
+        assert np.array_equal(a[k], b[k]), k

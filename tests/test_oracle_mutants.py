@@ -19,17 +19,30 @@ SRC = os.path.join(ROOT, "oracle", "mbref.c")
 # (name, original text, mutated text)
 MUTANTS = [
     ("busiest rank tie -> highest index",
-     "if (load[r] > load[rs]) rs = r;", "if (load[r] >= load[rs]) rs = r;"),
+     "if (load[r] - tau[r] > load[rs] - tau[rs]) rs = r;",
+     "if (load[r] - tau[r] >= load[rs] - tau[rs]) rs = r;"),
     ("heaviest expert tie -> highest id",
      "if (best < 0 || qh[e] > qh[best]) best = e;", "if (best < 0 || qh[e] >= qh[best]) best = e;"),
     ("destination tie -> highest index",
-     "if (dst < 0 || load[r] < load[dst]) dst = r;", "if (dst < 0 || load[r] <= load[dst]) dst = r;"),
+     "if (dst < 0 || tau[r] - load[r] > tau[dst] - load[dst]) dst = r;",
+     "if (dst < 0 || tau[r] - load[r] >= tau[dst] - load[dst]) dst = r;"),
     ("destination -> most loaded open rank",
-     "if (dst < 0 || load[r] < load[dst]) dst = r;", "if (dst < 0 || load[r] > load[dst]) dst = r;"),
+     "if (dst < 0 || tau[r] - load[r] > tau[dst] - load[dst]) dst = r;",
+     "if (dst < 0 || tau[r] - load[r] < tau[dst] - load[dst]) dst = r;"),
     ("move size capped at the busiest rank's excess",
-     "int64_t m = T - load[dst];", "int64_t m = T - load[dst];\n      if (load[rs] - T < m) m = load[rs] - T;"),
-    ("water level rounded down",
-     "const int64_t T = (N * K + P - 1) / P;", "const int64_t T = (N * K) / P - (N * K % P == 0 ? 1 : 0);"),
+     "int64_t m = tau[dst] - load[dst];",
+     "int64_t m = tau[dst] - load[dst];\n      if (load[rs] - tau[rs] < m) m = load[rs] - tau[rs];"),
+    ("water level one below the ceiling",
+     "tau[r] = (N * K * sr + sum_s - 1) / sum_s;", "tau[r] = (N * K * sr + sum_s - 1) / sum_s - 1;"),
+    ("busiest rank by load, not by excess over its target",
+     "if (load[r] - tau[r] > load[rs] - tau[rs]) rs = r;", "if (load[r] > load[rs]) rs = r;"),
+    ("destination by least load, not by deficit under its target",
+     "if (dst < 0 || tau[r] - load[r] > tau[dst] - load[dst]) dst = r;",
+     "if (dst < 0 || load[r] < load[dst]) dst = r;"),
+    ("weighted targets rounded down",
+     "tau[r] = (N * K * sr + sum_s - 1) / sum_s;", "tau[r] = (N * K * sr) / sum_s;"),
+    ("speeds ignored",
+     "const int64_t sr = speed ? speed[r] : 1;", "const int64_t sr = 1;"),
     ("highest free slot",
      "while (o->rep_expert[dst * R + j] >= 0) ++j;", "j = R - 1;\n      while (o->rep_expert[dst * R + j] >= 0) --j;"),
     ("no local preference (pass 1 off)",

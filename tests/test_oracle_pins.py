@@ -142,6 +142,72 @@ def test_hand_example_surplus_order():
 
 # ---- invariants on every workload -------------------------------------------
 
+def test_hand_example_weighted():
+    """P=4 ranks of speeds s = [4, 4, 2, 1], 2 home experts each, R=1, K=1,
+    16 tokens (4 per source rank), cap 6.
+
+    Targets tau_r = ceil(16 s_r / 11) = ceil([5.82, 5.82, 2.91, 1.45]) =
+    [6, 6, 3, 2]. Counts c = [5, 2, 2, 1, 1, 1, 3, 1] give L = [7, 3, 2, 4],
+    i.e. L - tau = [+1, -3, -1, +2].
+    Step 1: farthest above its target is rank 3 (+2; rank 0 has the larger
+    load but only +1); its heaviest expert is 6 (quota 3); open ranks are
+    1 (deficit 3) and 2 (deficit 1; it is the least loaded, but not the
+    farthest below target) -> rank 1; m = min(6 - 3, 3) = 3 -> loads
+    [7, 6, 2, 1].
+    Step 2: rank 0 (+1); heaviest expert 0 (quota 5); rank 1 has no free
+    slot, ranks 2 and 3 both lack 1 -> rank 2 (lower index);
+    m = min(3 - 2, 5) = 1 -> loads [6, 6, 3, 1]; every rank is at or below
+    its target; stop after 2 moves.
+    Routing: pass 1 keeps t0-t3 (e0, quota 4), t7 (e2), t10, t11, t15 home;
+    pass 2 sends t4 (e0) -> 2 (rank 0 is full), t5, t6 -> 0, t8, t9 -> 1,
+    t12-t14 (e6: home quota 0) -> the replica on rank 1.
+    Region of rank r at row 6r; home slots by id, then the replica slot.
+    Against the unrounded targets 16 s_r / 11 the largest ratio falls from
+    4 / 1.4545 = 2.75 to 6 / 5.8182 = 1.03125.
+    """
+    g = json.load(open(os.path.join(GOLDEN, "hand_example_weighted.json")))
+    d = O.make_dims(**g["dims"])
+    ids = np.array(g["ids"], np.int32).reshape(-1, 1)
+    p = O.plan(d, ids, speeds=np.array(g["speeds"], np.int32))
+    for key in ("counts", "load_pre", "load_post", "rep_expert", "slot_quota", "cu_seqlens",
+                "status", "row_src"):
+        assert np.array_equal(getattr(p, key), np.array(g[key])), key
+    assert np.array_equal(p.host.ravel(), g["host"])
+    assert np.array_equal(p.pos.ravel(), g["pos"])
+    assert p.report["water_level"] == max(g["targets"])
+    assert p.report["nonlocal_pairs"] == g["nonlocal_pairs"]
+    assert p.report["offhome_pairs"] == g["offhome_pairs"]
+    assert p.report["wir_before"] == pytest.approx(g["wir_before"])
+    assert p.report["wir_after"] == pytest.approx(g["wir_after"])
+    # the rounding of the targets matters: with cap 5 rank 0 and 1 overflow
+    d5 = O.make_dims(**dict(g["dims"], cap=5))
+    p5 = O.plan(d5, ids, speeds=np.array(g["speeds"], np.int32))
+    assert p5.flags == O.ST_CAPACITY and np.array_equal(p5.load_post, g["load_post"])
+
+
+def test_equal_speeds_are_the_water_level():
+    """Equal speeds (any value) give every rank the target T: the hand-derived
+    unweighted example comes out unchanged."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_example_fill.json")))
+    d = O.make_dims(**g["dims"])
+    ids = np.array(g["ids"], np.int32).reshape(-1, 1)
+    f = g["fill_host"]
+    for v in (1, 7, 1 << 20):
+        p = O.plan(d, ids, speeds=np.full(3, v, np.int32))
+        for key in ("load_post", "rep_expert", "slot_quota", "cu_seqlens", "status", "row_src"):
+            assert np.array_equal(getattr(p, key), np.array(f[key])), key
+        assert np.array_equal(p.pos.ravel(), f["pos"])
+        assert p.report["wir_after"] == pytest.approx(f["ir_after"])
+
+
+def test_speeds_rejected_out_of_range():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example_weighted.json")))
+    d = O.make_dims(**g["dims"])
+    ids = np.array(g["ids"], np.int32)
+    for bad in ([0, 4, 2, 1], [4, -1, 2, 1], [4, 4, 2, (1 << 20) + 1]):
+        assert O.plan_rc(d, ids, np.array(bad, np.int32)) == O.ERR_INVALID_ARG
+
+
 SMALL = ["tiny", "mixtral", "decode_drift"]
 
 

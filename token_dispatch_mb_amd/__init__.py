@@ -53,6 +53,8 @@ class Dims(ctypes.Structure):
     @classmethod
     def for_workload(cls, wl, cap=None, n_tokens=None) -> "Dims":
         n = wl.n_tokens if n_tokens is None else n_tokens
+        if cap is None and n_tokens is None:
+            cap = wl.cap
         return cls.make(n, wl.top_k, wl.n_experts, wl.n_ranks, wl.slots_per_rank, wl.hidden,
                         cap=cap, dtype_in=wl.dtype_in, dtype_out=wl.dtype_out)
 
@@ -87,6 +89,9 @@ _lib.mb_plan_workspace_bytes.restype = ctypes.c_size_t
 _lib.mb_plan.argtypes = [ctypes.POINTER(Dims), _vp, _vp, ctypes.c_size_t,
                          ctypes.POINTER(_PlanBufsC), _vp]
 _lib.mb_plan.restype = ctypes.c_int
+_lib.mb_plan_weighted.argtypes = [ctypes.POINTER(Dims), _vp, _i32p, _vp, ctypes.c_size_t,
+                                  ctypes.POINTER(_PlanBufsC), _vp]
+_lib.mb_plan_weighted.restype = ctypes.c_int
 _lib.mb_dispatch.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_PlanBufsC), _vp, _vp, _vp,
                              _vp, _vp]
 _lib.mb_dispatch.restype = ctypes.c_int
@@ -95,8 +100,9 @@ _lib.mb_combine.restype = ctypes.c_int
 _lib.mb_plan_status.argtypes = [ctypes.POINTER(_PlanBufsC), _vp, _i32p]
 _lib.mb_plan_status.restype = ctypes.c_int
 
-EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan", "mb_dispatch",
-           "mb_combine", "mb_plan_status")
+EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan",
+           "mb_plan_weighted", "mb_dispatch", "mb_combine", "mb_plan_status")
+MAX_SPEED = 1 << 20
 
 
 class MoebalError(RuntimeError):
@@ -161,13 +167,22 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, stream=None) -> None:
-    """mb_plan: enqueue the plan of one MoE layer call on `stream`."""
+def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, stream=None,
+         speeds=None) -> None:
+    """mb_plan: enqueue the plan of one MoE layer call on `stream`; with
+    ``speeds`` (P host ints), mb_plan_weighted."""
     assert ids.dtype == torch.int32 and ids.is_contiguous()
-    rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), ws.numel(),
-                      ctypes.byref(bufs.c_struct()), _stream(stream))
+    if speeds is None:
+        rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), ws.numel(),
+                          ctypes.byref(bufs.c_struct()), _stream(stream))
+        if rc != OK:
+            raise MoebalError("mb_plan", rc)
+        return
+    sp = (ctypes.c_int32 * len(speeds))(*[int(v) for v in speeds])
+    rc = _lib.mb_plan_weighted(ctypes.byref(dims), _ptr(ids), sp, _ptr(ws), ws.numel(),
+                               ctypes.byref(bufs.c_struct()), _stream(stream))
     if rc != OK:
-        raise MoebalError("mb_plan", rc)
+        raise MoebalError("mb_plan_weighted", rc)
 
 
 def dispatch(dims: Dims, bufs: PlanBuffers, x: torch.Tensor, buf: torch.Tensor,

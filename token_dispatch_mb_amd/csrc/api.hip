@@ -13,8 +13,6 @@ Geometry geometry(const mb_dims& d) {
   g.NS = g.Eh + d.slots_per_rank;
   g.nbps = (g.S + kTokensPerBlock - 1) / kTokensPerBlock;
   g.nblk = g.nbps * d.n_ranks;
-  // Water level T = ceil(N*K / P) (ISER-MoE, HALO-Q Objective 1).
-  g.T = (int32_t)(((int64_t)d.n_tokens * d.top_k + d.n_ranks - 1) / d.n_ranks);
   return g;
 }
 
@@ -92,7 +90,7 @@ const char* mb_strerror(int code) {
     case MB_ERR_HIP: return "HIP runtime error";
     case MB_ST_BAD_ID: return "status: an expert id outside [0, E)";
     case MB_ST_DUP_ID: return "status: a token lists one expert twice";
-    case MB_ST_UNBALANCED: return "status: placement stopped with a rank above the water level";
+    case MB_ST_UNBALANCED: return "status: placement stopped with a rank above its target";
     case MB_ST_CAPACITY: return "status: a rank needs more rows than cap";
     default: return "unknown code";
   }
@@ -104,13 +102,16 @@ size_t mb_plan_workspace_bytes(const mb_dims* dims) {
   return ws_layout(*dims, g).total;
 }
 
-int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws_bytes,
-            const mb_plan_bufs* out, hipStream_t stream) {
+static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
+                     void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out,
+                     hipStream_t stream) {
   int rc = validate(dims);
   if (rc != MB_OK) return rc;
   if (!plan_ptrs_ok(dims, out) || !ws_dev || (dims->n_tokens > 0 && !ids_dev) ||
       (dims->slots_per_rank > 0 && !out->rep_expert) || !aligned16(ws_dev))
     return MB_ERR_INVALID_ARG;
+  for (int r = 0; r < dims->n_ranks; ++r)
+    if (rank_speed[r] < 1 || rank_speed[r] > MB_MAX_SPEED) return MB_ERR_INVALID_ARG;
   const Geometry g = geometry(*dims);
   const WsLayout L = ws_layout(*dims, g);
   if (ws_bytes < L.total) return MB_ERR_WORKSPACE;
@@ -130,7 +131,8 @@ int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws
     return MB_ERR_HIP;
   if (launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_plan(*dims, g, *out, blockflags, expert_total, host_range, stream) != hipSuccess)
+  if (launch_plan(*dims, g, *out, rank_speed, blockflags, expert_total, host_range, stream) !=
+      hipSuccess)
     return MB_ERR_HIP;
   if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
@@ -139,6 +141,22 @@ int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws
       hipSuccess)
     return MB_ERR_HIP;
   return MB_OK;
+}
+
+int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws_bytes,
+            const mb_plan_bufs* out, hipStream_t stream) {
+  // Equal speeds: every target is the water level T = ceil(N*K / P)
+  // (ISER-MoE, HALO-Q Objective 1).
+  int32_t ones[kMaxRanks];
+  for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
+  return plan_impl(dims, ids_dev, ones, ws_dev, ws_bytes, out, stream);
+}
+
+int mb_plan_weighted(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
+                     void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out,
+                     hipStream_t stream) {
+  if (!rank_speed) return MB_ERR_INVALID_ARG;
+  return plan_impl(dims, ids_dev, rank_speed, ws_dev, ws_bytes, out, stream);
 }
 
 int mb_dispatch(const mb_dims* dims, const mb_plan_bufs* plan, const void* x_dev,

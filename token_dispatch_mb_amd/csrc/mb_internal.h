@@ -50,7 +50,6 @@ struct alignas(16) HostEntry {
 struct Geometry {
   int32_t S, Eh, NS;     // tokens per rank, home experts per rank, slots per rank
   int32_t nbps, nblk;    // routing blocks per source rank, in total
-  int32_t T;             // water level ceil(N*K/P)
 };
 
 struct WsLayout {
@@ -71,9 +70,10 @@ hipError_t launch_count(const mb_dims& d, const Geometry& g, const int32_t* ids,
 hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* blockcnt,
                        int32_t* blockoff, int32_t* counts, int32_t* expert_total,
                        hipStream_t st);
+// rank_speed: P host values (all 1 for the single water level).
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
-                       const int32_t* blockflags, const int32_t* expert_total,
-                       int2* host_range, hipStream_t st);
+                       const int32_t* rank_speed, const int32_t* blockflags,
+                       const int32_t* expert_total, int2* host_range, hipStream_t st);
 hipError_t launch_tables(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                          PairEntry* pair_tab, HostEntry* host_list, int2* host_range,
                          hipStream_t st);

@@ -3,9 +3,11 @@
 // One workgroup of 256 threads:
 //  1. routed pairs per expert c_e (summed over sources by k_scan);
 //  2. wave 0 runs the greedy with lane r = logical rank r (P <= 64): the
-//     busiest rank above the water level T gives a replica of its heaviest
-//     home expert to the least loaded rank below T that has a free slot and
-//     no copy yet, filling that rank up to T;
+//     rank farthest above its target tau_r gives a replica of its heaviest
+//     home expert to the rank farthest below its own target that has a free
+//     slot and no copy yet, filling that rank up to its target. With equal
+//     speeds every target is the water level T, the first rank is the
+//     busiest and the second the least loaded;
 //  3. all threads write slot quotas, cu_seqlens, loads and the status word.
 // The lookup tables that turn a pair's stable rank into its dispatch row are
 // built afterwards by k_tables (route.hip), one wave per expert.
@@ -20,7 +22,9 @@
 // (surplus routes onto the hosts' spare quotas); Zepp summary §4.1 (R replica
 // slots per GPU); MoonEP, "What MoonEP enforces and how" (S*K rows per rank,
 // planner-made cu_seqlens) and "Implementation details" (home experts, then
-// prefetch slots, in one numbering).
+// prefetch slots, in one numbering); ViBE summary, Methodology, Variability-
+// Informed Expert Placement (token target per GPU in proportion to its
+// speed, experts to the GPU farthest below its target).
 #include "mb_internal.h"
 #include "wave.h"
 
@@ -28,7 +32,8 @@ namespace mb {
 namespace {
 
 struct PlanArgs {
-  int N, K, E, P, R, cap, Eh, NS, nblk, T;
+  int N, K, E, P, R, cap, Eh, NS, nblk;
+  int32_t speed[kMaxRanks];  // rank speeds (all 1: the single water level)
   const int32_t* expert_total;
   const int32_t* blockflags;
   int32_t* load_pre;
@@ -49,11 +54,12 @@ struct PlanSmem {
   int32_t* repM;    // [P*R] quota of replica slot
   int32_t* loadv;   // [64] load after planning
   int32_t* lpre;    // [64] load before planning
-  int32_t* misc;    // [4] moves, unbalanced
+  int32_t* tau;     // [64] target of each rank
+  int32_t* misc;    // [4] moves, unbalanced, max load, largest target
 };
 
 __host__ __device__ inline size_t plan_smem_bytes(int E, int P, int R, int NS) {
-  return sizeof(int32_t) * (2 * (size_t)E + 2 * (size_t)P * R + 64 + 64 + 4);
+  return sizeof(int32_t) * (2 * (size_t)E + 2 * (size_t)P * R + 64 + 64 + 64 + 4);
 }
 
 __device__ inline PlanSmem carve(uint8_t* base, int E, int P, int R, int NS) {
@@ -71,6 +77,8 @@ __device__ inline PlanSmem carve(uint8_t* base, int E, int P, int R, int NS) {
   p += 64;
   m.lpre = p;
   p += 64;
+  m.tau = p;
+  p += 64;
   m.misc = p;
   return m;
 }
@@ -83,15 +91,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Greedy placement, run by the 64 lanes of wave 0 (lane = rank).
 //
-// A move gives its destination min(T - load, remaining home quota) pairs, so
-// a rank that receives a replica of an expert either ends at T or exhausts
-// that expert's home quota, and a rank at or below T never sheds. Hence, for
-// an expert with home quota left, every holder other than its home is at T:
-// no open rank (load below T, slot free) holds it, and the destination of a
-// move is the least loaded open rank whatever expert the busiest rank gives.
-// A step is then two independent wave reductions over the loads (busiest
-// rank, least loaded open rank) plus reads of the busiest rank's heaviest
-// expert, which each rank lane keeps up to date in registers.
+// Each lane works on x = load - tau, its rank's distance above (x > 0) or
+// below (x < 0) its target. A move gives its destination min(-x, remaining
+// home quota) pairs, so a rank that receives a replica of an expert either
+// ends at its target or exhausts that expert's home quota, and a rank at or
+// below its target never sheds. Hence, for an expert with home quota left,
+// every holder other than its home is at its target: no open rank (x < 0,
+// slot free) holds it, and the destination of a move is the open rank with
+// the smallest x whatever expert the busiest rank gives. A step is then two
+// independent wave reductions over x (largest; smallest among open ranks)
+// plus reads of the busiest rank's heaviest expert, which each rank lane
+// keeps up to date in registers.
 //
 // EHM >= Eh: registers per lane for the home quotas of its rank.
 //
@@ -103,8 +113,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int EHM>
 __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
-  const int P = a.P, R = a.R, Eh = a.Eh, T = a.T;
+  const int P = a.P, R = a.R, Eh = a.Eh;
   const bool rank_lane = lane < P;
+  const int tau = rank_lane ? m.tau[lane] : 0;
   int q[EHM];
   int load = 0;
 #pragma unroll
@@ -135,20 +146,21 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
       }
     const int bq = v[0], bj = ix[0];
 
-    const bool open_lane = rank_lane && used < R && load < T;
-    int lmax, lmin;
-    wave_max_min_i32(rank_lane ? load : INT32_MIN, open_lane ? load : INT32_MAX, lmax, lmin);
-    if (lmax <= T) break;
-    if (lmin == INT32_MAX) {  // no open rank
+    const int x = load - tau;
+    const bool open_lane = rank_lane && used < R && x < 0;
+    int xmax, xmin;
+    wave_max_min_i32(rank_lane ? x : INT32_MIN, open_lane ? x : INT32_MAX, xmax, xmin);
+    if (xmax <= 0) break;
+    if (xmin == INT32_MAX) {  // no open rank
       unbalanced = 1;
       break;
     }
-    const int rs = lowest_lane(ballot64(rank_lane && load == lmax));
-    const int d = lowest_lane(ballot64(open_lane && load == lmin));
+    const int rs = lowest_lane(ballot64(rank_lane && x == xmax));
+    const int d = lowest_lane(ballot64(open_lane && x == xmin));
     const int qmax = __builtin_amdgcn_readlane(bq, rs);
     const int jb = __builtin_amdgcn_readlane(bj, rs);
     const int slot = __builtin_amdgcn_readlane(used, d);  // slots fill in index order
-    const int mv = min(T - lmin, qmax);
+    const int mv = min(-xmin, qmax);
     const int mi = moves & 63;
     rec_e = lane == mi ? rs * Eh + jb : rec_e;
     rec_m = lane == mi ? mv : rec_m;
@@ -185,24 +197,26 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
 // wave reduction per step.
 __device__ void greedy_lds(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
-  const int P = a.P, R = a.R, Eh = a.Eh, T = a.T;
+  const int P = a.P, R = a.R, Eh = a.Eh;
   const bool rank_lane = lane < P;
+  const int tau = rank_lane ? m.tau[lane] : 0;
   int load = 0;
   if (rank_lane)
     for (int i = 0; i < Eh; ++i) load += m.c[lane * Eh + i];
   const int lpre = load;
   int used = 0, moves = 0, unbalanced = 0;
   for (;;) {
-    const bool open_lane = rank_lane && used < R && load < T;
-    const int lmax = wave_max_i32(rank_lane ? load : INT32_MIN);
-    const int lmin = wave_min_i32(open_lane ? load : INT32_MAX);
-    if (lmax <= T) break;
-    if (lmin == INT32_MAX) {
+    const int x = load - tau;
+    const bool open_lane = rank_lane && used < R && x < 0;
+    const int xmax = wave_max_i32(rank_lane ? x : INT32_MIN);
+    const int xmin = wave_min_i32(open_lane ? x : INT32_MAX);
+    if (xmax <= 0) break;
+    if (xmin == INT32_MAX) {
       unbalanced = 1;
       break;
     }
-    const int rs = lowest_lane(ballot64(rank_lane && load == lmax));
-    const int d = lowest_lane(ballot64(open_lane && load == lmin));
+    const int rs = lowest_lane(ballot64(rank_lane && x == xmax));
+    const int d = lowest_lane(ballot64(open_lane && x == xmin));
     int myq = 0, myj = INT32_MAX;
     for (int j = lane; j < Eh; j += 64) {
       const int qq = m.qh[rs * Eh + j];
@@ -215,7 +229,7 @@ __device__ void greedy_lds(const PlanArgs& a, PlanSmem& m) {
     const int jb = wave_min_i32(myq == qmax ? myj : INT32_MAX);
     const int e = rs * Eh + jb;
     const int slot = __builtin_amdgcn_readlane(used, d);
-    const int mv = min(T - lmin, qmax);
+    const int mv = min(-xmin, qmax);
     if (lane == 0) {
       m.qh[e] = qmax - mv;
       m.repE[d * R + slot] = e;
@@ -245,6 +259,19 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   const int E = a.E, P = a.P, R = a.R, Eh = a.Eh, NS = a.NS;
   PlanSmem m = carve(smem, E, P, R, NS);
 
+  // Targets (ViBE, token target in proportion to speed), exact in integers:
+  // tau_r = ceil(N*K * s_r / sum s); equal speeds give T = ceil(N*K / P).
+  if (tid < 64) {
+    const bool rank_lane = tid < P;
+    const int s = rank_lane ? a.speed[tid] : 0;
+    const int sum = __builtin_amdgcn_readlane(wave_inclusive_sum(s), 63);
+    const long long nk = (long long)a.N * a.K;
+    const int tau = rank_lane ? (int)((nk * s + sum - 1) / sum) : 0;
+    m.tau[tid] = tau;
+    const int tmax = wave_max_i32(tau);
+    if (tid == 0) m.misc[3] = tmax;
+  }
+
   // Status bits of the routing decisions.
   int fl = 0;
   for (int i = tid; i < a.nblk; i += kPlanThreads) fl |= a.blockflags[i];
@@ -253,7 +280,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   if (bad || dup) {
     if (tid == 0) {
       a.status[0] = (bad ? MB_ST_BAD_ID : 0) | (dup ? MB_ST_DUP_ID : 0);
-      a.status[1] = a.T;
+      a.status[1] = m.misc[3];
       a.status[2] = 0;
       a.status[3] = 0;
     }
@@ -335,7 +362,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   const bool over_cap = max_load > a.cap;
   if (tid == 0) {
     a.status[0] = (m.misc[1] ? MB_ST_UNBALANCED : 0) | (over_cap ? MB_ST_CAPACITY : 0);
-    a.status[1] = a.T;
+    a.status[1] = m.misc[3];
     a.status[2] = max_load;
     a.status[3] = m.misc[0];
   }
@@ -344,8 +371,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
 }  // namespace
 
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
-                       const int32_t* blockflags, const int32_t* expert_total,
-                       int2* host_range, hipStream_t st) {
+                       const int32_t* rank_speed, const int32_t* blockflags,
+                       const int32_t* expert_total, int2* host_range, hipStream_t st) {
   PlanArgs a;
   a.N = d.n_tokens;
   a.K = d.top_k;
@@ -356,7 +383,7 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.Eh = g.Eh;
   a.NS = g.NS;
   a.nblk = g.nblk;
-  a.T = g.T;
+  for (int r = 0; r < kMaxRanks; ++r) a.speed[r] = r < d.n_ranks ? rank_speed[r] : 0;
   a.expert_total = expert_total;
   a.blockflags = blockflags;
   a.load_pre = o.load_pre;

@@ -28,6 +28,14 @@ Sizes, and the statistic each workload is shaped to hit:
   beta is where the routing crosses the target (to 1e-4, by bisection at
   seed 6000; ``workload/tune.py``). Two replica slots per rank: with one, the
   planner cannot hold every rank to S * K at maxvio 10 and 20.
+* vibe_dsv3_prefill: the dsv3_prefill routing on 32 ranks of unequal speed.
+  Each rank's relative latency is 1 + 0.07 u (u uniform in [0, 1): up to 7 %
+  kernel time variation under balanced load, ViBE Challenge 2) and rank 7 is
+  degraded to 1.13 (the 13 % "skewed variability" case of ViBE's
+  sensitivity study); speed = round(65536 / latency). Targets follow speed,
+  so the fastest ranks take more than S * K rows: regions are 36864 rows
+  (S * K * 9 / 8), and two replica slots per rank (with one, the planner
+  stops short of the targets).
 """
 from __future__ import annotations
 
@@ -52,6 +60,11 @@ class Workload:
     calls: int = 1
     note: str = ""
     targets: dict = field(default_factory=dict)
+    cap_rows: int = 0  # rows per rank region; 0 = S * K
+    # synthetic rank speeds (see ``workload.rank_speeds``); none by default
+    speed_spread: float = 0.0
+    slow_rank: int = -1
+    slow_factor: float = 1.0
 
     @property
     def tokens_per_rank(self) -> int:
@@ -59,8 +72,13 @@ class Workload:
 
     @property
     def cap(self) -> int:
-        """Rows per rank region of the dispatch buffer: S * K."""
-        return self.tokens_per_rank * self.top_k
+        """Rows per rank region of the dispatch buffer: S * K unless set."""
+        return self.cap_rows or self.tokens_per_rank * self.top_k
+
+    @property
+    def weighted(self) -> bool:
+        """Planned with per-rank speeds."""
+        return self.speed_spread > 0 or self.slow_rank >= 0
 
     def seed_for(self, call: int) -> int:
         return self.seed + call
@@ -69,6 +87,7 @@ class Workload:
         """Same routing model with fewer tokens (a bounded sample)."""
         d = dict(self.__dict__)
         d["n_tokens"] = n_tokens
+        d["cap_rows"] = self.cap_rows * n_tokens // self.n_tokens
         d["name"] = f"{self.name}@N={n_tokens}"
         return Workload(**d)
 
@@ -121,8 +140,18 @@ for _name, (_target, _beta) in MAXVIO_SWEEP.items():
         targets={"maxvio": _target},
     )
 
+WORKLOADS["vibe_dsv3_prefill"] = Workload(
+    name="vibe_dsv3_prefill", n_tokens=131072, n_experts=256, top_k=8, n_ranks=32,
+    slots_per_rank=2, hidden=7168, dtype_in="bf16", dtype_out="bf16", noise=0,
+    zipf_s=1.0, beta=0.42, seed=3027, cap_rows=36864,
+    speed_spread=0.07, slow_rank=7, slow_factor=1.13,
+    note="dsv3_prefill routing on 32 ranks of unequal speed (relative latency 1 + 0.07 u, "
+         "rank 7 at 1.13), targets in proportion to speed, 2 slots, 36864 rows per region",
+)
+
 ORDER = ["tiny", "mixtral", "dsv3_prefill", "kimi_prefill", "decode_drift"]
 SWEEP_ORDER = list(MAXVIO_SWEEP)
+EXTRA_ORDER = SWEEP_ORDER + ["vibe_dsv3_prefill"]
 
 
 def get_workload(name: str) -> Workload:
@@ -130,4 +159,4 @@ def get_workload(name: str) -> Workload:
         return WORKLOADS[name]
     except KeyError:
         raise KeyError(f"unknown workload {name!r}; known: "
-                       f"{', '.join(ORDER + SWEEP_ORDER)}") from None
+                       f"{', '.join(ORDER + EXTRA_ORDER)}") from None
