@@ -10,6 +10,12 @@ seeded synthetic routing and rows, resident in HBM before timing starts.
 Expert outputs are the dispatched rows (identity experts), written once
 before timing into a buffer of their own.
 
+A workload planned with drift-gated replanning (drift_decode) steps through
+its sequence of calls, one call per step, from a fresh drift state when the
+timed steps begin; the line then also reports which calls replanned, their
+plan time against the kept calls' and against replanning every call, and
+the rank imbalance each way.
+
 Prints one JSON line. `value` is dispatch + combine algorithmic bytes per
 step divided by the whole step time (plan included). `roofline` refers to the
 kernel with the larger share of the step (HIP events on the launch stream);
@@ -72,6 +78,38 @@ def measured_traffic(kernel: str, workload: str):
         return None
     m = re.search(rf"^traffic_bytes_per_launch\.{kernel}:\s*([0-9.eE+]+)", text, re.M)
     return float(m.group(1)) if m else None
+
+
+def _drift_report(steps, plan_ms, plan_call, bufs, drift, mean_load, mb, torch, np):
+    """Untimed replays of the timed sequence from a fresh state: which calls
+    replanned and the imbalance after each call, then every call planned
+    without the gate (its plan time by HIP events, and its imbalance)."""
+    drift[1].zero_()
+    replanned, ir_gated = [], []
+    for i in range(steps):
+        plan_call(i)
+        st = mb.plan_status(bufs)
+        replanned.append(bool(st[0] & mb.ST_REPLANNED))
+        ir_gated.append(float(st[2]) / mean_load)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    ir_always = []
+    for i in range(steps):
+        ev[i][0].record()
+        plan_call(i, gated=False)
+        ev[i][1].record()
+        ir_always.append(float(mb.plan_status(bufs)[2]) / mean_load)
+    always_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    rp = np.array(replanned)
+    return {
+        "replanned_calls": [i for i in range(steps) if replanned[i]],
+        "plan_us_replanned": round(float(plan_ms[rp].mean()) * 1e3, 2) if rp.any() else None,
+        "plan_us_kept": round(float(plan_ms[~rp].mean()) * 1e3, 2) if (~rp).any() else None,
+        "plan_us_every_call_replanned": round(float(always_ms.mean()) * 1e3, 2),
+        "ir_after_mean_gated": round(float(np.mean(ir_gated)), 5),
+        "ir_after_max_gated": round(float(np.max(ir_gated)), 5),
+        "ir_after_mean_every_call_replanned": round(float(np.mean(ir_always)), 5),
+        "header": mb.drift_header(drift[1]),
+    }
 
 
 def _speed_ratio(load, speeds, wl):
@@ -158,7 +196,8 @@ def _cpu_model() -> str:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; a drift-gated workload: its call count)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
@@ -195,6 +234,8 @@ def main() -> int:
     wl = W.get_workload(args.workload)
     dims = mb.Dims.for_workload(wl)
     log(f"workload {wl.name}: {wl.note}")
+    if args.steps is None:
+        args.steps = wl.calls if wl.drift else 20
 
     ids, w = W.routing_for(wl)
     x, xs = W.token_rows(wl)
@@ -217,6 +258,23 @@ def main() -> int:
     # single water level). For comparison, the equal-target plan's largest
     # ratio of load to the speed-proportional share, outside the timing.
     speeds = W.rank_speeds(wl)
+    # A drift-gated workload: the routing of every call of its sequence, and
+    # a drift state (zero-filled = fresh) for the layer.
+    drift = None
+    if wl.drift:
+        ids_all = torch.stack([torch.from_numpy(W.routing_for(wl, c)[0])
+                               for c in range(wl.calls)]).to(dev)
+        drift = (mb.DriftParams(*wl.drift), mb.alloc_drift_state(dims, dev))
+        log(f"drift gate {wl.drift}: {wl.calls} calls of routing resident")
+
+    def plan_call(i, gated=True):
+        if drift is None:
+            mb.plan(dims, ids_d, ws, bufs, speeds=speeds)
+        elif gated:
+            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, drift=drift)
+        else:
+            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds)
+
     wir_equal = None
     if speeds is not None:
         mb.plan(dims, ids_d, ws, bufs)
@@ -233,10 +291,10 @@ def main() -> int:
     status = mb.plan_status(bufs)
     log(f"status {status.tolist()} (flags, T, max load, moves)")
 
-    def step(ev=None):
+    def step(i, ev=None):
         if ev is not None:
             ev[0].record()
-        mb.plan(dims, ids_d, ws, bufs, speeds=speeds)
+        plan_call(i)
         if ev is not None:
             ev[1].record()
         mb.dispatch(dims, bufs, x_d, buf, xs_d, bs)
@@ -246,8 +304,10 @@ def main() -> int:
         if ev is not None:
             ev[3].record()
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
+    if drift is not None:
+        drift[1].zero_()  # the timed steps run the sequence from its first call
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
 
@@ -255,7 +315,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(i, evs[i])
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
 
@@ -282,6 +342,11 @@ def main() -> int:
         samp = torch.arange(0, wl.n_tokens, max(1, wl.n_tokens // 256), device=dev)
         err = (y[samp].float() - x_d[samp].float() * w_d[samp].sum(1, keepdim=True)).abs().max()
         log(f"identity-expert check: max |y - x * sum(w)| = {float(err):.3e}")
+
+    drift_report = None
+    if drift is not None:
+        drift_report = _drift_report(args.steps, plan_ms, plan_call, bufs, drift, mean_load, mb,
+                                     torch, np)
 
     out = {
         "metric": METRIC,
@@ -317,6 +382,7 @@ def main() -> int:
         "speed_targets": None if speeds is None else {
             "max_load_over_share": round(float(_speed_ratio(bufs.load_post.cpu().numpy(), speeds, wl)), 5),
             "same_with_equal_targets": round(wir_equal, 5)},
+        "drift_gate": drift_report,
         "wall_s_timed": round(t_wall, 4),
         "roofline": {
             "kernel": dominant,

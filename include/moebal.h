@@ -94,6 +94,37 @@ enum mb_status_flag {
 /* Largest rank speed accepted by mb_plan_weighted. */
 #define MB_MAX_SPEED (1 << 20)
 
+/* status[0] bit of mb_plan_drift: this call ran the greedy placement
+ * (informational, never fatal). */
+#define MB_ST_REPLANNED 16
+
+/* Largest reference window of mb_plan_drift, in calls. */
+#define MB_MAX_WINDOW 4096
+
+/* Drift gate of mb_plan_drift [ViBE, Drift-Aware Recalibration]. */
+typedef struct mb_drift_params {
+  int32_t delta_num;   /* replan when d > delta_num / delta_den, where  */
+  int32_t delta_den;   /*   d = 1 - cos(current counts, reference)      */
+  int32_t window;      /* reference = count vectors of up to `window` calls
+                          since the last replan, in [1, MB_MAX_WINDOW] */
+  int32_t check_every; /* calls between two checks (>= 1) */
+} mb_drift_params;
+
+/* First bytes of a drift state buffer (device memory, caller-owned); the
+ * rest holds the reference sum int64[E], then the kept placement: replica
+ * experts int32[P*R] and their slots in placement order int32[P*R]. A
+ * zero-filled buffer is a fresh state. */
+typedef struct mb_drift_header {
+  int32_t have_plan;  /* a placement is kept */
+  int32_t countdown;  /* calls until the next check */
+  int32_t nwin;       /* count vectors in the reference */
+  int32_t n_moves;    /* replicas of the kept placement */
+  int64_t calls;      /* calls planned with this state */
+  int64_t replans;    /* of which ran the greedy */
+  double last_d;      /* distance found at the last check */
+  int64_t reserved[3];
+} mb_drift_header;
+
 /* Problem sizes of one MoE layer call. */
 typedef struct mb_dims {
   int32_t n_tokens;       /* N tokens; token t originates on rank t / (N/P) */
@@ -189,6 +220,35 @@ int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws
 int mb_plan_weighted(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
                      void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out,
                      hipStream_t stream);
+
+/* Bytes of a drift state buffer for these sizes (0 outside the limits).
+ * Pure host function. */
+size_t mb_drift_state_bytes(const mb_dims* dims);
+
+/*
+ * One call of a layer planned with drift-gated replanning [ViBE, Drift-Aware
+ * Recalibration], on `state` (mb_drift_state_bytes(dims) bytes of device
+ * memory, 16-byte aligned, zero-filled before the layer's first call, then
+ * passed to every call of that layer with the same dims and params; calls
+ * on one state must be ordered on one stream).
+ * On the first call, and when a check finds d > delta (checks run every
+ * check_every calls), the greedy of mb_plan (or of mb_plan_weighted when
+ * rank_speed, a P-entry host array, is not NULL) places replicas; the
+ * placement is kept in the state, the reference restarts from this call's
+ * counts, and status[0] gets MB_ST_REPLANNED. Otherwise the kept replicas,
+ * in the order they were placed, each take min(target - host load,
+ * remaining home quota) pairs while the expert's home rank is above its
+ * target and the host below its own (none otherwise), the plan is
+ * MB_ST_UNBALANCED if any rank stays above its target, and this call's
+ * counts join the reference while it holds fewer than `window` vectors.
+ * d = 1 - r.c / (|r| |c|) over the expert counts c and the reference sum r,
+ * with exact integer sums, then one division and two square roots in
+ * double. A call with BAD_ID or DUP_ID leaves the state unchanged.
+ * Outputs and everything else as mb_plan.
+ */
+int mb_plan_drift(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
+                  const mb_drift_params* params, void* state_dev, void* ws_dev,
+                  size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream);
 
 /*
  * Dispatch [MoonEP, "What MoonEP enforces and how": tokens written into

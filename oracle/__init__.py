@@ -27,6 +27,7 @@ ELT_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1}
 
 ST_BAD_ID, ST_DUP_ID, ST_UNBALANCED, ST_CAPACITY = 1, 2, 4, 8
 ST_FATAL = ST_BAD_ID | ST_DUP_ID | ST_CAPACITY
+ST_REPLANNED = 16
 
 MOVE_FILL_HOST, MOVE_EXCESS_ONLY = 0, 1
 
@@ -57,6 +58,35 @@ class Report(ctypes.Structure):
                 ("wir_before", ctypes.c_double), ("wir_after", ctypes.c_double)]
 
 
+class DriftParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("delta_num", "delta_den", "window", "check_every")]
+
+
+class _DriftStateC(ctypes.Structure):
+    _fields_ = [("have_plan", ctypes.c_int32), ("countdown", ctypes.c_int32),
+                ("nwin", ctypes.c_int32), ("n_moves", ctypes.c_int32),
+                ("calls", ctypes.c_int64), ("replans", ctypes.c_int64),
+                ("last_d", ctypes.c_double),
+                ("wsum", ctypes.POINTER(ctypes.c_int64)), ("rep", _i32p), ("order", _i32p)]
+
+
+class DriftState:
+    """State of one layer's drift-gated planning (host memory)."""
+
+    def __init__(self, n_experts: int, n_ranks: int, slots_per_rank: int):
+        self.wsum = np.zeros(n_experts, np.int64)
+        self.rep = np.full(n_ranks * slots_per_rank, -1, np.int32)
+        self.order = np.full(n_ranks * slots_per_rank, -1, np.int32)
+        self.c = _DriftStateC(0, 0, 0, 0, 0, 0, 0.0,
+                              self.wsum.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                              self.rep.ctypes.data_as(_i32p), self.order.ctypes.data_as(_i32p))
+
+    def __getattr__(self, name):
+        if name in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans", "last_d"):
+            return getattr(self.c, name)
+        raise AttributeError(name)
+
+
 _lib = None
 
 
@@ -73,6 +103,10 @@ def lib() -> ctypes.CDLL:
         L.mbref_plan_weighted.argtypes = [ctypes.POINTER(Dims), vp, vp, ctypes.c_int32,
                                           ctypes.POINTER(PlanOut), ctypes.POINTER(Report)]
         L.mbref_plan_weighted.restype = ctypes.c_int
+        L.mbref_plan_drift.argtypes = [ctypes.POINTER(Dims), vp, vp, ctypes.POINTER(DriftParams),
+                                       ctypes.POINTER(_DriftStateC), ctypes.POINTER(PlanOut),
+                                       ctypes.POINTER(Report)]
+        L.mbref_plan_drift.restype = ctypes.c_int
         L.mbref_dispatch.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp]
         L.mbref_dispatch.restype = ctypes.c_int
         L.mbref_dispatch_window.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp,
@@ -129,9 +163,10 @@ def _ptr(a: np.ndarray):
 
 
 def plan(dims: Dims, ids: np.ndarray, move_rule: int = MOVE_FILL_HOST,
-         speeds: np.ndarray | None = None) -> Plan:
+         speeds: np.ndarray | None = None, drift: tuple | None = None) -> Plan:
     """Steps O0-O4 and O7. ``speeds`` (int32 [P]) gives per-rank targets in
-    proportion to rank speed in place of the single water level."""
+    proportion to rank speed in place of the single water level. ``drift`` =
+    (DriftParams, DriftState) plans one call of a drift-gated sequence."""
     N, K, E, P, R = dims.n_tokens, dims.top_k, dims.n_experts, dims.n_ranks, dims.slots_per_rank
     ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(N, K)
     eh = E // P if P > 0 else 0
@@ -145,7 +180,13 @@ def plan(dims: Dims, ids: np.ndarray, move_rule: int = MOVE_FILL_HOST,
     }
     po = PlanOut(**{k: v.ctypes.data_as(_i32p) for k, v in a.items()})
     rep = Report()
-    if speeds is None:
+    if drift is not None:
+        prm, st = drift
+        sp = None if speeds is None else np.ascontiguousarray(speeds, dtype=np.int32)
+        rc = lib().mbref_plan_drift(ctypes.byref(dims), _ptr(ids),
+                                    _ptr(sp) if sp is not None else None, ctypes.byref(prm),
+                                    ctypes.byref(st.c), ctypes.byref(po), ctypes.byref(rep))
+    elif speeds is None:
         rc = lib().mbref_plan(ctypes.byref(dims), _ptr(ids), move_rule, ctypes.byref(po),
                               ctypes.byref(rep))
     else:
@@ -176,6 +217,21 @@ def plan_rc(dims: Dims, ids: np.ndarray, speeds: np.ndarray | None = None) -> in
     sp = np.ascontiguousarray(speeds, dtype=np.int32)
     return lib().mbref_plan_weighted(ctypes.byref(dims), _ptr(ids), _ptr(sp), 0,
                                      ctypes.byref(po), None)
+
+
+def plan_drift_rc(dims: Dims, ids: np.ndarray, params: DriftParams, state: DriftState) -> int:
+    """Return code of mbref_plan_drift alone, for invalid parameters."""
+    N = max(dims.n_tokens, 0)
+    K = max(dims.top_k, 0)
+    P = max(dims.n_ranks, 1)
+    E = max(dims.n_experts, 1)
+    R = max(dims.slots_per_rank, 0)
+    big = max(N * K, P * max(dims.cap, 1), P * E, P * (E + R + 1), 16)
+    bufs = [np.zeros(big, np.int32) for _ in range(10)]
+    po = PlanOut(*[b.ctypes.data_as(_i32p) for b in bufs])
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    return lib().mbref_plan_drift(ctypes.byref(dims), _ptr(ids), None, ctypes.byref(params),
+                                  ctypes.byref(state.c), ctypes.byref(po), None)
 
 
 def row_bytes_in(dims: Dims) -> int:

@@ -83,13 +83,30 @@ static int valid_dims(const mbref_dims* d) {
   return 1;
 }
 
+/* A placement kept from an earlier call: replica experts per slot and the
+ * slots in the order their replicas were placed. */
+typedef struct keep_t {
+  const int32_t* rep;
+  const int32_t* order;
+  int64_t n_moves;
+} keep_t;
+
+static int plan_core(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
+                     int32_t move_rule, const keep_t* keep, int32_t* order_out,
+                     mbref_plan_out* o, mbref_report* rep);
+
 int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
                mbref_plan_out* o, mbref_report* rep) {
-  return mbref_plan_weighted(dm, ids, NULL, move_rule, o, rep);
+  return plan_core(dm, ids, NULL, move_rule, NULL, NULL, o, rep);
 }
 
-int mbref_plan_weighted(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
-                        int32_t move_rule, mbref_plan_out* o, mbref_report* rep) {
+
+/* Steps O0-O4 and O7. With `keep`, step O2 reuses that placement instead of
+ * running the greedy; otherwise the greedy's slots are written, in move
+ * order, to order_out (if not NULL). */
+static int plan_core(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
+                     int32_t move_rule, const keep_t* keep, int32_t* order_out,
+                     mbref_plan_out* o, mbref_report* rep) {
   if (!dm || !o || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
   if (move_rule != MBREF_MOVE_FILL_HOST && move_rule != MBREF_MOVE_EXCESS_ONLY)
     return MBREF_ERR_INVALID_ARG;
@@ -185,7 +202,32 @@ int mbref_plan_weighted(const mbref_dims* dm, const int32_t* ids, const int32_t*
   }
   int64_t moves = 0;
   int unbalanced = 0;
-  for (;;) {
+  if (keep) {
+    /* [ViBE] Drift-Aware Recalibration keeps the placement while the load
+     * has not drifted: the kept replicas, in the order they were placed,
+     * each take min(target - load of its host, remaining home quota) pairs
+     * while its home rank is above its target and its host below its own,
+     * else none. */
+    for (int64_t i = 0; i < P * R; ++i) o->rep_expert[i] = keep->rep[i];
+    for (int64_t i = 0; i < keep->n_moves; ++i) {
+      const int64_t slot = keep->order[i], dst = slot / R;
+      const int64_t e = keep->rep[slot], h = e / Eh;
+      int64_t m = 0;
+      if (load[h] > tau[h] && load[dst] < tau[dst]) {
+        m = tau[dst] - load[dst];
+        if (qh[e] < m) m = qh[e];
+      }
+      rq[slot] = m;
+      is_host[e * P + dst] = 1;
+      qh[e] -= m;
+      load[h] -= m;
+      load[dst] += m;
+    }
+    moves = keep->n_moves;
+    for (int64_t r = 0; r < P; ++r)
+      if (load[r] > tau[r]) unbalanced = 1;
+  }
+  for (; !keep;) {
     int64_t rs = 0; /* busiest rank (farthest above its target), lowest index on ties */
     for (int64_t r = 1; r < P; ++r)
       if (load[r] - tau[r] > load[rs] - tau[rs]) rs = r;
@@ -219,6 +261,7 @@ int mbref_plan_weighted(const mbref_dims* dm, const int32_t* ids, const int32_t*
       while (o->rep_expert[dst * R + j] >= 0) ++j;
       o->rep_expert[dst * R + j] = (int32_t)best;
       rq[dst * R + j] = m;
+      if (order_out) order_out[moves] = (int32_t)(dst * R + j);
       is_host[best * P + dst] = 1;
       qh[best] -= m;
       load[rs] -= m;
@@ -353,6 +396,86 @@ int mbref_plan_weighted(const mbref_dims* dm, const int32_t* ids, const int32_t*
 done:
   free(c); free(L); free(load); free(qh); free(rq); free(is_host); free(tried);
   free(Q); free(used); free(slot_of); free(rows); free(cu); free(fill); free(tau);
+  return rc;
+}
+
+int mbref_plan_weighted(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
+                        int32_t move_rule, mbref_plan_out* o, mbref_report* rep) {
+  return plan_core(dm, ids, speed, move_rule, NULL, NULL, o, rep);
+}
+
+/* [ViBE] Drift-Aware Recalibration: d = 1 - w.w^ / (|w| |w^|). The window's
+ * sum stands for its mean (same direction); the three sums are exact
+ * integers, then one division and two square roots in double. */
+static double cosine_distance(const int64_t* c, const int64_t* ws, int64_t E) {
+  unsigned __int128 dot = 0, n1 = 0, n2 = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    dot += (unsigned __int128)(uint64_t)c[e] * (uint64_t)ws[e];
+    n1 += (unsigned __int128)(uint64_t)c[e] * (uint64_t)c[e];
+    n2 += (unsigned __int128)(uint64_t)ws[e] * (uint64_t)ws[e];
+  }
+  if (n1 == 0 || n2 == 0) return n1 == n2 ? 0.0 : 1.0;
+  return 1.0 - (double)dot / (sqrt((double)n1) * sqrt((double)n2));
+}
+
+int mbref_plan_drift(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
+                     const mbref_drift_params* prm, mbref_drift_state* st,
+                     mbref_plan_out* o, mbref_report* rep) {
+  if (!dm || !o || !prm || !st || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
+  if (prm->delta_den < 1 || prm->delta_num < 0 || prm->delta_num > prm->delta_den ||
+      prm->window < 1 || prm->window > MBREF_MAX_WINDOW || prm->check_every < 1)
+    return MBREF_ERR_INVALID_ARG;
+  const int64_t N = dm->n_tokens, K = dm->top_k, E = dm->n_experts;
+  const int64_t P = dm->n_ranks, R = dm->slots_per_rank;
+  /* Routing decisions that are not a valid input leave the state alone. */
+  for (int64_t t = 0; t < N; ++t)
+    for (int64_t k = 0; k < K; ++k) {
+      const int32_t e = ids[t * K + k];
+      int bad = e < 0 || e >= E;
+      for (int64_t k2 = 0; k2 < k; ++k2) bad |= ids[t * K + k2] == e;
+      if (bad) return plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, NULL, NULL, o, rep);
+    }
+  int64_t* c = calloc((size_t)E, sizeof(int64_t));
+  int32_t* order = calloc((size_t)(P * R + 1), sizeof(int32_t));
+  if (!c || !order) {
+    free(c);
+    free(order);
+    return MBREF_ERR_NOMEM;
+  }
+  for (int64_t i = 0; i < N * K; ++i) c[ids[i]] += 1;
+  /* Replan on the first call, then check every check_every calls. */
+  int replan = !st->have_plan;
+  if (!replan && --st->countdown == 0) {
+    st->countdown = prm->check_every;
+    st->last_d = cosine_distance(c, st->wsum, E);
+    if (st->last_d > (double)prm->delta_num / (double)prm->delta_den) replan = 1;
+  }
+  int rc;
+  if (replan) {
+    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, NULL, order, o, rep);
+    if (rc == MBREF_OK) {
+      for (int64_t i = 0; i < P * R; ++i) st->rep[i] = o->rep_expert[i];
+      for (int64_t i = 0; i < P * R; ++i) st->order[i] = i < o->status[3] ? order[i] : -1;
+      st->n_moves = o->status[3];
+      st->have_plan = 1;
+      st->countdown = prm->check_every;
+      /* the reference restarts from the load seen at the recalibration */
+      for (int64_t e = 0; e < E; ++e) st->wsum[e] = c[e];
+      st->nwin = 1;
+      st->replans += 1;
+      o->status[0] |= MBREF_ST_REPLANNED;
+    }
+  } else {
+    const keep_t keep = {st->rep, st->order, st->n_moves};
+    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, &keep, NULL, o, rep);
+    if (rc == MBREF_OK && st->nwin < prm->window) {
+      for (int64_t e = 0; e < E; ++e) st->wsum[e] += c[e];
+      st->nwin += 1;
+    }
+  }
+  if (rc == MBREF_OK) st->calls += 1;
+  free(c);
+  free(order);
   return rc;
 }
 

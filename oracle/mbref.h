@@ -58,6 +58,35 @@ enum { MBREF_MOVE_FILL_HOST = 0, MBREF_MOVE_EXCESS_ONLY = 1 };
 /* Largest rank speed accepted by mbref_plan_weighted. */
 #define MBREF_MAX_SPEED (1 << 20)
 
+/* status[0] bit of mbref_plan_drift: this call ran the greedy (no fatal
+ * meaning). */
+#define MBREF_ST_REPLANNED 16
+
+/* Largest reference window of mbref_plan_drift (calls). */
+#define MBREF_MAX_WINDOW 4096
+
+/* Drift gate: replan when d = 1 - cos(current counts, reference) exceeds
+ * delta_num / delta_den, checked every check_every calls; the reference is
+ * the sum of the count vectors of up to `window` calls since the last
+ * replan. */
+typedef struct mbref_drift_params {
+  int32_t delta_num, delta_den, window, check_every;
+} mbref_drift_params;
+
+/* State carried between the calls of one layer; zero-filled (and arrays of
+ * E, P*R, P*R entries) before the first call. */
+typedef struct mbref_drift_state {
+  int32_t have_plan;  /* a placement is kept */
+  int32_t countdown;  /* calls until the next check */
+  int32_t nwin;       /* count vectors in the reference */
+  int32_t n_moves;    /* replicas of the kept placement */
+  int64_t calls, replans;
+  double last_d;      /* distance at the last check */
+  int64_t* wsum;      /* [E] sum of the reference's count vectors */
+  int32_t* rep;       /* [P*R] kept replica experts */
+  int32_t* order;     /* [P*R] kept slots in placement order, -1 after */
+} mbref_drift_state;
+
 typedef struct mbref_dims {
   int32_t n_tokens;       /* N */
   int32_t top_k;          /* K */
@@ -112,6 +141,13 @@ int mbref_plan(const mbref_dims* dims, const int32_t* ids, int32_t move_rule,
 int mbref_plan_weighted(const mbref_dims* dims, const int32_t* ids,
                         const int32_t* speed, int32_t move_rule,
                         mbref_plan_out* out, mbref_report* report);
+
+/* Drift-gated planning of one layer's successive calls: the greedy runs on
+ * the first call and whenever a check finds the counts drifted; otherwise
+ * the kept placement gets new quotas (see mbref.c). */
+int mbref_plan_drift(const mbref_dims* dims, const int32_t* ids, const int32_t* speed,
+                     const mbref_drift_params* params, mbref_drift_state* state,
+                     mbref_plan_out* out, mbref_report* report);
 
 /* Step O5: buf[pos[t][k]] = x[t] (and the fp8 scale row). Rows of buf that
  * no pair maps to are left untouched. Returns 1 if status is fatal (nothing

@@ -37,10 +37,10 @@ class GpuPlan:
         self.bufs = mb.PlanBuffers.allocate(dims, self.device)
         self.ws = mb.alloc_workspace(dims, self.device)
 
-    def run(self, ids: np.ndarray | torch.Tensor, stream=None, speeds=None):
+    def run(self, ids: np.ndarray | torch.Tensor, stream=None, speeds=None, drift=None):
         ids_d = ids if isinstance(ids, torch.Tensor) else torch.from_numpy(
             np.ascontiguousarray(ids, np.int32)).to(self.device)
-        mb.plan(self.dims, ids_d, self.ws, self.bufs, stream, speeds=speeds)
+        mb.plan(self.dims, ids_d, self.ws, self.bufs, stream, speeds=speeds, drift=drift)
         return self
 
     def fetch(self) -> dict:

@@ -267,7 +267,8 @@ def test_round_trip_identity_experts():
 G_ROWS = 4099  # distinct expert-output rows, cycled over the buffer (prime)
 
 
-@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"] + W.configs.EXTRA_ORDER)
+@pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill", "vibe_dsv3_prefill"]
+                         + W.configs.SWEEP_ORDER)
 def test_prefill_full_size(name):
     """The full prefill and maxvio-sweep workloads in the launch configuration
     the benchmark times: the whole plan bit-exact; dispatched rows of three rank regions
@@ -421,3 +422,137 @@ def test_equal_speeds_match_mb_plan():
     b = G.GpuPlan(dg).run(ids, speeds=[977] * wl.n_ranks).fetch()
     for k in G.PLAN_FIELDS:
         assert np.array_equal(a[k], b[k]), k
+
+
+# ---- drift-gated replanning ------------------------------------------------------
+
+def _gpu_drift_state(dg):
+    return mb.alloc_drift_state(dg, G.dev())
+
+
+def _assert_state_equal(state_d, st, E, label):
+    h = mb.drift_header(state_d)
+    for key in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans"):
+        assert h[key] == getattr(st, key), (label, key, h[key], getattr(st, key))
+    # the decision is taken in double on both sides from exact integer sums
+    assert h["last_d"] == st.last_d, (label, "last_d", h["last_d"], st.last_d)
+    wsum = state_d[64:64 + 8 * E].cpu().numpy().view(np.int64)
+    assert np.array_equal(wsum, st.wsum), (label, "reference")
+
+
+def test_hand_example_drift_on_gpu():
+    """The hand-derived drift sequence through mb_plan_drift: every call's
+    plan and the state after it equal the stored values and the oracle's."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "hand_example_drift.json")))
+    dd = dict(g["dims"])
+    dd["hidden"] = 8
+    dg = mb.Dims.make(**dd, dtype_in="bf16", dtype_out="bf16")
+    od = O.make_dims(**dd, dtype_in="bf16", dtype_out="bf16")
+    gprm, oprm = mb.DriftParams(**g["params"]), O.DriftParams(**g["params"])
+    state = _gpu_drift_state(dg)
+    st = O.DriftState(od.n_experts, od.n_ranks, od.slots_per_rank)
+    gp = G.GpuPlan(dg)
+    for i, call in enumerate(g["calls"]):
+        ids = np.array(call["ids"], np.int32).reshape(-1, 1)
+        got = gp.run(ids, drift=(gprm, state)).fetch()
+        for key in ("status", "load_post", "rep_expert", "slot_quota"):
+            assert np.array_equal(got[key].reshape(np.array(call[key]).shape),
+                                  np.array(call[key])), (i, key)
+        ref = O.plan(od, ids, drift=(oprm, st))
+        G.assert_plan_equal(got, ref)
+        _assert_state_equal(state, st, od.n_experts, f"call {i}")
+
+
+def test_drift_replay_needs_home_above_target_on_gpu():
+    dg = mb.Dims.make(12, 1, 3, 3, 1, 8, cap=12, dtype_in="bf16", dtype_out="bf16")
+    state = _gpu_drift_state(dg)
+    prm = mb.DriftParams(1, 1, 4, 1)
+    gp = G.GpuPlan(dg)
+    c0 = np.array([0] * 6 + [1] * 3 + [2] * 3, np.int32).reshape(-1, 1)
+    c1 = np.array([0] * 4 + [1] * 2 + [2] * 6, np.int32).reshape(-1, 1)
+    a = gp.run(c0, drift=(prm, state)).fetch()
+    assert a["status"][0] == mb.ST_REPLANNED and np.array_equal(a["load_post"], [4, 4, 4])
+    b = gp.run(c1, drift=(prm, state)).fetch()
+    assert b["status"][0] == mb.ST_UNBALANCED and np.array_equal(b["load_post"], [4, 2, 6])
+
+
+@pytest.mark.parametrize("H", [1, 10])
+def test_drift_decode_sequence(H):
+    """The 60-pass drift workload through mb_plan_drift and the oracle in
+    lockstep: every call's plan bit-exact, the state (counters, reference,
+    distance) equal after every call; dispatch and combine on three kept
+    calls. Rows are 128 wide here (the plan does not depend on H)."""
+    wl = W.get_workload("drift_decode")
+    num, den, win, _ = wl.drift
+    dg = mb.Dims.for_workload(wl)
+    dg.hidden = 128
+    od = O.dims_for(wl)
+    od.hidden = 128
+    state = _gpu_drift_state(dg)
+    st = O.DriftState(wl.n_experts, wl.n_ranks, wl.slots_per_rank)
+    gprm, oprm = mb.DriftParams(num, den, win, H), O.DriftParams(num, den, win, H)
+    gp = G.GpuPlan(dg)
+    replans = []
+    for call in range(wl.calls):
+        ids, w = W.routing_for(wl, call)
+        got = gp.run(ids, drift=(gprm, state)).fetch()
+        ref = O.plan(od, ids, drift=(oprm, st))
+        G.assert_plan_equal(got, ref)
+        _assert_state_equal(state, st, wl.n_experts, f"call {call}")
+        if ref.flags & O.ST_REPLANNED:
+            replans.append(call)
+        if call in (7, 33, 59):
+            assert not ref.flags & O.ST_REPLANNED
+            x, xs, _ = W.rows_fp8(wl.seed_for(call), W.TAG_X, 128, n=wl.n_tokens)
+            ye = _y_exp_rows(wl.seed_for(call), od, od.n_ranks * od.cap)
+            buf, bs, y = G.run_rows(dg, gp, x, xs, ye, w)
+            ref_buf, ref_bs, _ = O.dispatch(od, ref, x, xs)
+            used = ref.row_src >= 0
+            assert np.array_equal(buf[used], ref_buf[used]) and np.array_equal(bs[used], ref_bs[used])
+            y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, ye)
+            G.assert_combine_close(y, y_ref, mag, "bf16")
+    G.log(f"drift_decode H={H}: replans at {replans}")
+    first = {1: [0, 25, 50], 10: [0, 30, 50]}[H]
+    assert replans == first
+
+
+def _drift_cases():
+    rng = np.random.default_rng(31)
+    cases = []
+    for P in (2, 8, 33, 64):
+        for R in (0, 1, 2, 5):
+            eh = min(int(rng.choice([1, 3, 16, 40])), 1024 // P)
+            K = min(int(rng.choice([1, 2, 8])), P * eh)
+            S = int(rng.choice([4, 50, 200]))
+            H = int(rng.choice([1, 2, 5]))
+            delta = (int(rng.choice([0, 1, 3])), 100)
+            cases.append((P, eh, K, R, S, H, delta))
+    return cases
+
+
+@pytest.mark.parametrize("P,eh,K,R,S,H,delta", _drift_cases())
+def test_drift_sequences_sweep(P, eh, K, R, S, H, delta):
+    """Short sequences (12 calls, popularity changing every 4) over shapes,
+    check intervals and thresholds; some with rank speeds."""
+    E, N = P * eh, P * S
+    cap = 2 * S * K if R > 0 else N * K
+    dg = mb.Dims.make(N, K, E, P, R, 16, cap=cap, dtype_in="bf16", dtype_out="bf16")
+    od = O.make_dims(N, K, E, P, R, 16, cap=cap, dtype_in="bf16", dtype_out="bf16")
+    speeds = None
+    if (P + R) % 2:
+        speeds = np.random.default_rng(P * 7 + R).integers(1000, 3000, P).astype(np.int32)
+    state = _gpu_drift_state(dg)
+    st = O.DriftState(E, P, R)
+    gprm, oprm = mb.DriftParams(delta[0], delta[1], 3, H), O.DriftParams(delta[0], delta[1], 3, H)
+    gp = G.GpuPlan(dg)
+    for call in range(12):
+        ids, _ = W.routing(N, E, K, W.NOISE_GUMBEL, 1.1, 0.9, 12000 + P * 100 + call,
+                           pop_seed=13000 + P * 100 + call // 4)
+        got = gp.run(ids, speeds=speeds, drift=(gprm, state)).fetch()
+        ref = O.plan(od, ids, speeds=speeds, drift=(oprm, st))
+        G.assert_plan_equal(got, ref)
+        _assert_state_equal(state, st, E, f"P{P} R{R} call {call}")

@@ -62,6 +62,18 @@ MUTANTS = [
     ("dispatch copies the next token",
      "memcpy((char*)buf_win + (p - row0) * rb, (const char*)x + t * rb, (size_t)rb);",
      "memcpy((char*)buf_win + (p - row0) * rb, (const char*)x + ((t + 1) % N) * rb, (size_t)rb);"),
+    ("drift reference not accumulated",
+     "for (int64_t e = 0; e < E; ++e) st->wsum[e] += c[e];", "for (int64_t e = 0; e < 0; ++e) st->wsum[e] += c[e];"),
+    ("drift reference not restarted at a replan",
+     "for (int64_t e = 0; e < E; ++e) st->wsum[e] = c[e];", "for (int64_t e = 0; e < E; ++e) st->wsum[e] += c[e];"),
+    ("drift threshold inclusive",
+     "if (st->last_d > (double)prm->delta_num", "if (st->last_d >= (double)prm->delta_num"),
+    ("drift check on every call",
+     "if (!replan && --st->countdown == 0) {", "if (!replan && (--st->countdown, 1)) {"),
+    ("drift distance without the norms' square roots",
+     "(sqrt((double)n1) * sqrt((double)n2))", "((double)n1 + (double)n2)"),
+    ("kept replica takes pairs whatever its home's load",
+     "if (load[h] > tau[h] && load[dst] < tau[dst]) {", "if (load[dst] < tau[dst]) {"),
     ("duplicate ids not flagged",
      "if (ids[t * K + k2] == e) flags |= MBREF_ST_DUP_ID;", "if (0) flags |= MBREF_ST_DUP_ID;"),
 ]

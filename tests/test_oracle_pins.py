@@ -208,6 +208,130 @@ def test_speeds_rejected_out_of_range():
         assert O.plan_rc(d, ids, np.array(bad, np.int32)) == O.ERR_INVALID_ARG
 
 
+def test_hand_example_drift():
+    """Drift-gated replanning: P=2 ranks, 2 home experts each, R=1, K=1,
+    8 tokens, T = 4; replan when d > 1/2, checked every call, reference of
+    up to 2 calls.
+
+    Call 0 (c = [4, 1, 1, 2], L = [5, 3]): the first call runs the greedy:
+    expert 0 goes to rank 1 with min(4 - 3, 4) = 1 pair -> loads [4, 4];
+    the kept placement is slot 1 (rank 1) holding expert 0; reference
+    r = [4, 1, 1, 2].
+    Call 1 (c = [2, 0, 3, 3], L = [2, 6]): c.r = 17, |c|^2 = 22, |r|^2 = 22,
+    d = 1 - 17/22 = 5/22 < 1/2 -> keep; the kept replica takes nothing (its
+    home rank 0 is not above T) -> loads [2, 6], UNBALANCED, where a fresh
+    greedy would have reached [4, 4]; r = [6, 1, 4, 5] (2 calls).
+    Call 2 (c = [5, 1, 0, 2], L = [6, 2]): c.r = 41, |c|^2 = 30, |r|^2 = 78,
+    d = 1 - 41/sqrt(2340) = 0.152 -> keep; the replica takes
+    min(4 - 2, 5) = 2 -> [4, 4]; the window is full, r stays.
+    Call 3 (all tokens to expert 1): c.r = 8, |c|^2 = 64, d = 1 -
+    8/sqrt(4992) = 0.887 -> replan: expert 1 goes to rank 1 with
+    min(4 - 0, 8) = 4 pairs; the reference restarts at [0, 8, 0, 0].
+    (Had the reference not accumulated call 1, call 2 would have seen
+    d = 1 - 25/sqrt(660) = 0.027 against r = [4, 1, 1, 2] as well, and kept;
+    had it not restarted at call 3, the window would still hold [6, 1, 4, 5].)
+    """
+    g = json.load(open(os.path.join(GOLDEN, "hand_example_drift.json")))
+    d = O.make_dims(**g["dims"])
+    prm = O.DriftParams(**g["params"])
+    st = O.DriftState(d.n_experts, d.n_ranks, d.slots_per_rank)
+    for i, call in enumerate(g["calls"]):
+        ids = np.array(call["ids"], np.int32).reshape(-1, 1)
+        p = O.plan(d, ids, drift=(prm, st))
+        for key in ("status", "load_post", "rep_expert", "slot_quota"):
+            assert np.array_equal(getattr(p, key), np.array(call[key])), (i, key)
+        C.check_layout(p, ids, d.n_ranks, d.n_experts, d.slots_per_rank, d.cap)
+        exp = call["state"]
+        for key in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans"):
+            assert getattr(st, key) == exp[key], (i, key)
+        assert np.array_equal(st.wsum, exp["wsum"]), i
+        if "last_d" in exp:
+            assert st.last_d == pytest.approx(exp["last_d"], rel=1e-14), i
+        if "rep" in exp:
+            assert np.array_equal(st.rep, exp["rep"]) and np.array_equal(st.order, exp["order"])
+        if "fresh_load_post" in call:
+            assert np.array_equal(O.plan(d, ids).load_post, call["fresh_load_post"])
+
+
+def test_drift_replay_needs_home_above_target():
+    """A kept replica takes pairs only while its expert's home rank is above
+    its target. P=3 ranks of one home expert, R=1, K=1, 12 tokens, T = 4,
+    no replan after the first call (delta = 1).
+
+    Call 0 (c = [6, 3, 3]): expert 0 goes to rank 1 (least loaded, lower
+    index of the tie) with min(4 - 3, 6) = 1 pair, then to rank 2 with
+    min(4 - 3, 5) = 1 -> loads [4, 4, 4]; kept slots in order: 1, 2.
+    Call 1 (c = [4, 2, 6]): rank 0 is at T, so neither replica takes
+    anything even though rank 1 is below T -> loads [4, 2, 6], UNBALANCED.
+    """
+    d = O.make_dims(12, 1, 3, 3, 1, 4, cap=12)
+    st = O.DriftState(3, 3, 1)
+    prm = O.DriftParams(1, 1, 4, 1)
+    c0 = np.array([0] * 6 + [1] * 3 + [2] * 3, np.int32).reshape(-1, 1)
+    p0 = O.plan(d, c0, drift=(prm, st))
+    assert p0.flags == O.ST_REPLANNED and np.array_equal(p0.load_post, [4, 4, 4])
+    assert np.array_equal(p0.rep_expert.ravel(), [-1, 0, 0])
+    assert np.array_equal(st.order, [1, 2, -1])
+    c1 = np.array([0] * 4 + [1] * 2 + [2] * 6, np.int32).reshape(-1, 1)
+    p1 = O.plan(d, c1, drift=(prm, st))
+    assert p1.flags == O.ST_UNBALANCED
+    assert np.array_equal(p1.load_post, [4, 2, 6])
+    assert np.array_equal(p1.slot_quota, [[4, 0], [2, 0], [6, 0]])
+
+
+@pytest.mark.parametrize("H", [1, 3, 4])
+def test_drift_replans_every_check_when_counts_are_orthogonal(H):
+    """Each call sends every token to one expert, a different one each call:
+    d = 1 at every check, so the greedy runs on the first call and at every
+    H-th call after it; with delta = 1 (d never exceeds it) only the first
+    call replans; with delta = 0 every check replans."""
+    d = O.make_dims(32, 1, 8, 2, 1, 4, cap=32)
+    seq = [np.full((32, 1), e % 8, np.int32) for e in range(13)]
+    for num, den, expect in ((1, 20, [i for i in range(13) if i % H == 0]), (1, 1, [0]),
+                             (0, 1, [i for i in range(13) if i % H == 0])):
+        st = O.DriftState(8, 2, 1)
+        prm = O.DriftParams(num, den, 100, H)
+        got = [i for i, ids in enumerate(seq)
+               if O.plan(d, ids, drift=(prm, st)).flags & O.ST_REPLANNED]
+        assert got == expect, (num, den)
+        assert st.replans == len(expect) and st.calls == 13
+
+
+def test_drift_identical_calls_never_replan_and_match_mb_plan():
+    """The same routing every call: d = 0 (to rounding) at every check, the
+    placement is kept, and replaying it gives exactly the greedy's plan."""
+    wl = W.get_workload("decode_drift")
+    ids, _ = W.routing_for(wl, 3)
+    d = O.dims_for(wl)
+    ref = O.plan(d, ids)
+    st = O.DriftState(wl.n_experts, wl.n_ranks, wl.slots_per_rank)
+    prm = O.DriftParams(1, 1000, 8, 1)
+    for i in range(5):
+        p = O.plan(d, ids, drift=(prm, st))
+        assert (p.flags & ~O.ST_REPLANNED) == ref.flags
+        for key in ("load_post", "rep_expert", "slot_quota", "cu_seqlens", "pos", "row_src"):
+            assert np.array_equal(getattr(p, key), getattr(ref, key)), (i, key)
+        assert abs(st.last_d) <= 1e-15
+    assert st.replans == 1 and st.nwin == 5
+
+
+def test_drift_rejects_bad_params_and_keeps_state_on_bad_ids():
+    d = O.make_dims(8, 1, 4, 2, 1, 4, cap=8)
+    ids = np.zeros((8, 1), np.int32)
+    for prm in ((1, 0, 2, 1), (-1, 2, 2, 1), (3, 2, 2, 1), (1, 2, 0, 1), (1, 2, 2, 0),
+                (1, 2, 4097, 1)):
+        st = O.DriftState(4, 2, 1)
+        assert O.plan_drift_rc(d, ids, O.DriftParams(*prm), st) == O.ERR_INVALID_ARG, prm
+    st = O.DriftState(4, 2, 1)
+    prm = O.DriftParams(1, 2, 2, 1)
+    O.plan(d, ids, drift=(prm, st))
+    bad = ids.copy()
+    bad[3] = 9
+    p = O.plan(d, bad, drift=(prm, st))
+    assert p.flags == O.ST_BAD_ID
+    assert st.calls == 1 and st.replans == 1 and st.nwin == 1
+
+
 SMALL = ["tiny", "mixtral", "decode_drift"]
 
 

@@ -100,10 +100,11 @@ def test_fp8_rows_scales_and_dequant():
 
 
 def test_workloads_recipe():
-    for name in W.configs.ORDER + W.configs.SWEEP_ORDER:
+    for name in W.configs.ORDER + W.configs.EXTRA_ORDER:
         wl = W.get_workload(name)
         assert wl.n_tokens % wl.n_ranks == 0 and wl.n_experts % wl.n_ranks == 0
-        assert wl.cap == wl.tokens_per_rank * wl.top_k
+        assert wl.cap == (wl.cap_rows or wl.tokens_per_rank * wl.top_k)
+        assert wl.cap >= wl.tokens_per_rank * wl.top_k
 
 
 @pytest.mark.parametrize("name", ["dsv3_prefill", "kimi_prefill"])

@@ -92,6 +92,19 @@ _lib.mb_plan.restype = ctypes.c_int
 _lib.mb_plan_weighted.argtypes = [ctypes.POINTER(Dims), _vp, _i32p, _vp, ctypes.c_size_t,
                                   ctypes.POINTER(_PlanBufsC), _vp]
 _lib.mb_plan_weighted.restype = ctypes.c_int
+
+
+class DriftParams(ctypes.Structure):
+    """mb_drift_params: replan when d > delta_num / delta_den, checked every
+    check_every calls, reference of up to `window` calls."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("delta_num", "delta_den", "window", "check_every")]
+
+
+_lib.mb_drift_state_bytes.argtypes = [ctypes.POINTER(Dims)]
+_lib.mb_drift_state_bytes.restype = ctypes.c_size_t
+_lib.mb_plan_drift.argtypes = [ctypes.POINTER(Dims), _vp, _i32p, ctypes.POINTER(DriftParams), _vp,
+                               _vp, ctypes.c_size_t, ctypes.POINTER(_PlanBufsC), _vp]
+_lib.mb_plan_drift.restype = ctypes.c_int
 _lib.mb_dispatch.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_PlanBufsC), _vp, _vp, _vp,
                              _vp, _vp]
 _lib.mb_dispatch.restype = ctypes.c_int
@@ -101,7 +114,10 @@ _lib.mb_plan_status.argtypes = [ctypes.POINTER(_PlanBufsC), _vp, _i32p]
 _lib.mb_plan_status.restype = ctypes.c_int
 
 EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan",
-           "mb_plan_weighted", "mb_dispatch", "mb_combine", "mb_plan_status")
+           "mb_plan_weighted", "mb_drift_state_bytes", "mb_plan_drift", "mb_dispatch",
+           "mb_combine", "mb_plan_status")
+ST_REPLANNED = 16
+MAX_WINDOW = 4096
 MAX_SPEED = 1 << 20
 
 
@@ -168,10 +184,20 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
 
 
 def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, stream=None,
-         speeds=None) -> None:
+         speeds=None, drift=None) -> None:
     """mb_plan: enqueue the plan of one MoE layer call on `stream`; with
-    ``speeds`` (P host ints), mb_plan_weighted."""
+    ``speeds`` (P host ints), mb_plan_weighted; with ``drift`` =
+    (DriftParams, state tensor), mb_plan_drift."""
     assert ids.dtype == torch.int32 and ids.is_contiguous()
+    if drift is not None:
+        prm, state = drift
+        sp = None if speeds is None else (ctypes.c_int32 * len(speeds))(*[int(v) for v in speeds])
+        rc = _lib.mb_plan_drift(ctypes.byref(dims), _ptr(ids), sp, ctypes.byref(prm), _ptr(state),
+                                _ptr(ws), ws.numel(), ctypes.byref(bufs.c_struct()),
+                                _stream(stream))
+        if rc != OK:
+            raise MoebalError("mb_plan_drift", rc)
+        return
     if speeds is None:
         rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), ws.numel(),
                           ctypes.byref(bufs.c_struct()), _stream(stream))
@@ -205,6 +231,26 @@ def combine(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, w: torch.Tensor,
                          _ptr(y), _stream(stream))
     if rc != OK:
         raise MoebalError("mb_combine", rc)
+
+
+def alloc_drift_state(dims: Dims, device) -> torch.Tensor:
+    """A zero-filled (fresh) drift state buffer for one layer."""
+    n = _lib.mb_drift_state_bytes(ctypes.byref(dims))
+    if n == 0:
+        raise MoebalError("mb_drift_state_bytes", ERR_INVALID_ARG)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def drift_header(state: torch.Tensor) -> dict:
+    """The mb_drift_header fields of a state buffer (copies to the host)."""
+    import numpy as np
+
+    b = state[:64].cpu().numpy().tobytes()
+    i32 = np.frombuffer(b[:16], np.int32)
+    i64 = np.frombuffer(b[16:32], np.int64)
+    return {"have_plan": int(i32[0]), "countdown": int(i32[1]), "nwin": int(i32[2]),
+            "n_moves": int(i32[3]), "calls": int(i64[0]), "replans": int(i64[1]),
+            "last_d": float(np.frombuffer(b[32:40], np.float64)[0])}
 
 
 def plan_status(bufs: PlanBuffers, stream=None):

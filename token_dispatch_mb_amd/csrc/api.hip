@@ -18,6 +18,12 @@ Geometry geometry(const mb_dims& d) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+size_t drift_state_bytes(const mb_dims& d) {
+  const size_t PR = (size_t)d.n_ranks * d.slots_per_rank;
+  return align256(sizeof(mb_drift_header) + sizeof(int64_t) * d.n_experts +
+                  2 * sizeof(int32_t) * PR);
+}
+
 WsLayout ws_layout(const mb_dims& d, const Geometry& g) {
   WsLayout L;
   size_t off = 0;
@@ -103,8 +109,8 @@ size_t mb_plan_workspace_bytes(const mb_dims* dims) {
 }
 
 static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
-                     void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out,
-                     hipStream_t stream) {
+                     const mb_drift_params* drift, void* drift_state, void* ws_dev,
+                     size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream) {
   int rc = validate(dims);
   if (rc != MB_OK) return rc;
   if (!plan_ptrs_ok(dims, out) || !ws_dev || (dims->n_tokens > 0 && !ids_dev) ||
@@ -131,8 +137,8 @@ static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t*
     return MB_ERR_HIP;
   if (launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_plan(*dims, g, *out, rank_speed, blockflags, expert_total, host_range, stream) !=
-      hipSuccess)
+  if (launch_plan(*dims, g, *out, rank_speed, drift, drift_state, blockflags, expert_total,
+                  host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
@@ -149,14 +155,32 @@ int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws
   // (ISER-MoE, HALO-Q Objective 1).
   int32_t ones[kMaxRanks];
   for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
-  return plan_impl(dims, ids_dev, ones, ws_dev, ws_bytes, out, stream);
+  return plan_impl(dims, ids_dev, ones, nullptr, nullptr, ws_dev, ws_bytes, out, stream);
 }
 
 int mb_plan_weighted(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
                      void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out,
                      hipStream_t stream) {
   if (!rank_speed) return MB_ERR_INVALID_ARG;
-  return plan_impl(dims, ids_dev, rank_speed, ws_dev, ws_bytes, out, stream);
+  return plan_impl(dims, ids_dev, rank_speed, nullptr, nullptr, ws_dev, ws_bytes, out, stream);
+}
+
+size_t mb_drift_state_bytes(const mb_dims* dims) {
+  if (validate(dims) != MB_OK) return 0;
+  return drift_state_bytes(*dims);
+}
+
+int mb_plan_drift(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
+                  const mb_drift_params* params, void* state_dev, void* ws_dev,
+                  size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream) {
+  if (!params || !state_dev || !aligned16(state_dev)) return MB_ERR_INVALID_ARG;
+  if (params->delta_den < 1 || params->delta_num < 0 || params->delta_num > params->delta_den ||
+      params->window < 1 || params->window > MB_MAX_WINDOW || params->check_every < 1)
+    return MB_ERR_INVALID_ARG;
+  int32_t ones[kMaxRanks];
+  for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
+  return plan_impl(dims, ids_dev, rank_speed ? rank_speed : ones, params, state_dev, ws_dev,
+                   ws_bytes, out, stream);
 }
 
 int mb_dispatch(const mb_dims* dims, const mb_plan_bufs* plan, const void* x_dev,

@@ -34,6 +34,9 @@ namespace {
 struct PlanArgs {
   int N, K, E, P, R, cap, Eh, NS, nblk;
   int32_t speed[kMaxRanks];  // rank speeds (all 1: the single water level)
+  // drift-gated replanning: state buffer (nullptr: run the greedy every call)
+  uint8_t* drift_state;
+  int delta_num, delta_den, window, check_every;
   const int32_t* expert_total;
   const int32_t* blockflags;
   int32_t* load_pre;
@@ -47,24 +50,33 @@ struct PlanArgs {
 
 constexpr int kPlanThreads = 256;
 
+typedef unsigned __int128 u128;
+
 struct PlanSmem {
+  u128* red;        // [64*3] per-lane partial sums of the drift check
+  double* dmisc;    // [2] distance of this call's check
   int32_t* c;       // [E] routed pairs per expert
   int32_t* qh;      // [E] remaining home quota
   int32_t* repE;    // [P*R] expert of replica slot, -1 empty
   int32_t* repM;    // [P*R] quota of replica slot
+  int32_t* order;   // [P*R] replica slots in placement order
   int32_t* loadv;   // [64] load after planning
   int32_t* lpre;    // [64] load before planning
   int32_t* tau;     // [64] target of each rank
-  int32_t* misc;    // [4] moves, unbalanced, max load, largest target
+  int32_t* misc;    // [8] moves, unbalanced, max load, largest target,
+                    //     replan, checked, next countdown, window size
 };
 
 __host__ __device__ inline size_t plan_smem_bytes(int E, int P, int R, int NS) {
-  return sizeof(int32_t) * (2 * (size_t)E + 2 * (size_t)P * R + 64 + 64 + 64 + 4);
+  return sizeof(u128) * 64 * 3 + 2 * sizeof(double) +
+         sizeof(int32_t) * (2 * (size_t)E + 3 * (size_t)P * R + 64 + 64 + 64 + 8);
 }
 
 __device__ inline PlanSmem carve(uint8_t* base, int E, int P, int R, int NS) {
   PlanSmem m;
-  int32_t* p = reinterpret_cast<int32_t*>(base);
+  m.red = reinterpret_cast<u128*>(base);
+  m.dmisc = reinterpret_cast<double*>(base + sizeof(u128) * 64 * 3);
+  int32_t* p = reinterpret_cast<int32_t*>(base + sizeof(u128) * 64 * 3 + 2 * sizeof(double));
   m.c = p;
   p += E;
   m.qh = p;
@@ -72,6 +84,8 @@ __device__ inline PlanSmem carve(uint8_t* base, int E, int P, int R, int NS) {
   m.repE = p;
   p += P * R;
   m.repM = p;
+  p += P * R;
+  m.order = p;
   p += P * R;
   m.loadv = p;
   p += 64;
@@ -173,11 +187,13 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     if ((moves & 63) == 0) {
       m.repE[rec_i] = rec_e;
       m.repM[rec_i] = rec_m;
+      m.order[moves - 64 + lane] = rec_i;
     }
   }
   if (lane < (moves & 63)) {
     m.repE[rec_i] = rec_e;
     m.repM[rec_i] = rec_m;
+    m.order[(moves & ~63) + lane] = rec_i;
   }
   if (rank_lane) {
 #pragma unroll
@@ -234,6 +250,7 @@ __device__ void greedy_lds(const PlanArgs& a, PlanSmem& m) {
       m.qh[e] = qmax - mv;
       m.repE[d * R + slot] = e;
       m.repM[d * R + slot] = mv;
+      m.order[moves] = d * R + slot;
     }
     if (lane == rs) load -= mv;
     if (lane == d) {
@@ -250,6 +267,182 @@ __device__ void greedy_lds(const PlanArgs& a, PlanSmem& m) {
   if (lane == 0) {
     m.misc[0] = moves;
     m.misc[1] = unbalanced;
+  }
+}
+
+static_assert(sizeof(mb_drift_header) == 64, "drift header layout");
+
+struct DriftView {
+  mb_drift_header* hdr;
+  int64_t* wsum;   // [E] reference sum
+  int32_t* rep;    // [P*R] kept replica experts
+  int32_t* order;  // [P*R] kept slots in placement order
+};
+
+__device__ inline DriftView drift_view(const PlanArgs& a) {
+  DriftView v;
+  v.hdr = reinterpret_cast<mb_drift_header*>(a.drift_state);
+  v.wsum = reinterpret_cast<int64_t*>(a.drift_state + sizeof(mb_drift_header));
+  v.rep = reinterpret_cast<int32_t*>(v.wsum + a.E);
+  v.order = v.rep + a.P * a.R;
+  return v;
+}
+
+// d = 1 - c.r / (|c| |r|) from exact integer sums (ViBE summary, Drift-Aware
+// Recalibration); the window's sum r has the direction of its mean.
+__device__ double cosine_distance(u128 dot, u128 n1, u128 n2) {
+#pragma clang fp contract(off)
+  if (n1 == 0 || n2 == 0) return n1 == n2 ? 0.0 : 1.0;
+  return 1.0 - (double)dot / (__builtin_sqrt((double)n1) * __builtin_sqrt((double)n2));
+}
+
+// Wave 0: whether this call runs the greedy. The first call does; after
+// that a check every check_every calls compares the counts with the
+// reference and replans when d exceeds delta_num / delta_den.
+__device__ void drift_decide(const PlanArgs& a, PlanSmem& m) {
+  const int lane = threadIdx.x;
+  const DriftView v = drift_view(a);
+  const int have = v.hdr->have_plan;
+  int countdown = v.hdr->countdown;
+  const int nwin = v.hdr->nwin;
+  double d = v.hdr->last_d;
+  int replan = !have, checked = 0;
+  if (!replan && --countdown == 0) {
+    countdown = a.check_every;
+    checked = 1;
+    u128 dot = 0, n1 = 0, n2 = 0;
+    for (int e = lane; e < a.E; e += 64) {
+      const uint64_t c = (uint32_t)m.c[e], w = (uint64_t)v.wsum[e];
+      dot += (u128)c * w;
+      n1 += (u128)c * c;
+      n2 += (u128)w * w;
+    }
+    m.red[lane] = dot;
+    m.red[64 + lane] = n1;
+    m.red[128 + lane] = n2;
+    wave_lds_sync();
+    for (int w = 32; w >= 1; w >>= 1) {  // pairwise tree over the lanes
+      if (lane < w) {
+        m.red[lane] += m.red[lane + w];
+        m.red[64 + lane] += m.red[64 + lane + w];
+        m.red[128 + lane] += m.red[128 + lane + w];
+      }
+      wave_lds_sync();
+    }
+    if (lane == 0) m.dmisc[0] = cosine_distance(m.red[0], m.red[64], m.red[128]);
+    wave_lds_sync();
+    d = m.dmisc[0];
+    replan = d > (double)a.delta_num / (double)a.delta_den;
+  }
+  if (replan) countdown = a.check_every;
+  if (lane == 0) {
+    m.misc[4] = replan;
+    m.misc[5] = checked;
+    m.misc[6] = countdown;
+    m.misc[7] = nwin;
+    m.dmisc[0] = d;
+  }
+  wave_lds_sync();
+}
+
+// Wave 0, no replan: the kept replicas, in the order they were placed, each
+// take min(target - host load, remaining home quota) pairs while the
+// expert's home rank is above its target and the host below its own. Loads
+// stay in lane registers (lane = rank); a chunk of up to 64 moves is read
+// one move per lane, each lane also holding its move's expert's remaining
+// home quota, then stepped through in order (a move lowers the quota on
+// every lane of the same expert).
+__device__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
+  const int lane = threadIdx.x;
+  const int P = a.P, R = a.R, Eh = a.Eh;
+  const DriftView v = drift_view(a);
+  // (a state written by this kernel for the same sizes always passes these
+  // range checks; they only keep a foreign buffer inside the arrays)
+  const int n_moves = min(max(v.hdr->n_moves, 0), P * R);
+  for (int i = lane; i < P * R; i += 64) {
+    m.repE[i] = v.rep[i];
+    m.order[i] = v.order[i];
+  }
+  const bool rank_lane = lane < P;
+  const int tau = rank_lane ? m.tau[lane] : 0;
+  int load = 0;
+  if (rank_lane)
+    for (int i = 0; i < Eh; ++i) load += m.c[lane * Eh + i];
+  const int lpre = load;
+  wave_lds_sync();
+  for (int base = 0; base < n_moves; base += 64) {
+    const int i = base + lane;
+    int slot = 0, e = 0, dst = 0, h = 0;
+    bool ok = false;
+    if (i < n_moves) {
+      slot = m.order[i];
+      ok = (unsigned)slot < (unsigned)(P * R);
+      e = ok ? m.repE[slot] : 0;
+      ok = ok && (unsigned)e < (unsigned)a.E;
+      dst = ok ? slot / R : 0;
+      h = ok ? e / Eh : 0;
+      e = ok ? e : 0;
+    }
+    int q = ok ? m.qh[e] : 0;  // remaining home quota of this lane's expert
+    int mine = 0;
+    const int cnt = min(64, n_moves - base);
+    for (int j = 0; j < cnt; ++j) {
+      const int sd = __builtin_amdgcn_readlane(dst, j);
+      const int se = __builtin_amdgcn_readlane(e, j);
+      const int sh = __builtin_amdgcn_readlane(h, j);
+      const int ld = __builtin_amdgcn_readlane(load, sd);
+      const int lh = __builtin_amdgcn_readlane(load, sh);
+      const int td = __builtin_amdgcn_readlane(tau, sd);
+      const int th = __builtin_amdgcn_readlane(tau, sh);
+      const int qe = __builtin_amdgcn_readlane(q, j);
+      const bool okj = __builtin_amdgcn_readlane((int)ok, j) != 0;
+      const int mv = (okj && lh > th && ld < td) ? min(td - ld, qe) : 0;
+      mine = lane == j ? mv : mine;
+      q -= (ok && e == se) ? mv : 0;
+      load += (lane == sd ? mv : 0) - (lane == sh ? mv : 0);
+    }
+    if (i < n_moves && ok) {
+      m.repM[slot] = mine;
+      m.qh[e] = q;  // lanes of one expert hold the same final quota
+    }
+    wave_lds_sync();
+  }
+  const int unbalanced = ballot64(rank_lane && load > tau) != 0;
+  if (rank_lane) {
+    m.loadv[lane] = load;
+    m.lpre[lane] = lpre;
+  }
+  if (lane == 0) {
+    m.misc[0] = n_moves;
+    m.misc[1] = unbalanced;
+  }
+}
+
+// All threads, after the placement: the state for the layer's next call.
+__device__ void drift_update(const PlanArgs& a, PlanSmem& m) {
+  const int tid = threadIdx.x;
+  const DriftView v = drift_view(a);
+  const int replan = m.misc[4], moves = m.misc[0], nwin = m.misc[7];
+  const int PR = a.P * a.R;
+  if (replan) {
+    for (int e = tid; e < a.E; e += kPlanThreads) v.wsum[e] = m.c[e];
+    for (int i = tid; i < PR; i += kPlanThreads) {
+      v.rep[i] = m.repE[i];
+      v.order[i] = i < moves ? m.order[i] : -1;
+    }
+  } else if (nwin < a.window) {
+    for (int e = tid; e < a.E; e += kPlanThreads) v.wsum[e] += m.c[e];
+  }
+  if (tid == 0) {
+    mb_drift_header h = *v.hdr;
+    h.have_plan = 1;
+    h.countdown = m.misc[6];
+    h.nwin = replan ? 1 : min(nwin + 1, a.window);
+    if (replan) h.n_moves = moves;
+    h.calls += 1;
+    h.replans += replan;
+    h.last_d = m.dmisc[0];
+    *v.hdr = h;
   }
 }
 
@@ -299,8 +492,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   }
   __syncthreads();
 
+  const bool drift = a.drift_state != nullptr;
   if (tid < 64) {
-    if (Eh <= 4)
+    if (drift) drift_decide(a, m);
+    if (drift && !m.misc[4])
+      replay_kept(a, m);
+    else if (Eh <= 4)
       greedy_regs<4>(a, m);
     else if (Eh <= 8)
       greedy_regs<8>(a, m);
@@ -312,6 +509,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       greedy_lds(a, m);
   }
   __syncthreads();
+  if (drift) {
+    drift_update(a, m);
+    __syncthreads();
+  }
 
   // Slot quotas, cu_seqlens and loads, one thread per rank.
   for (int r = tid; r < P; r += kPlanThreads) {
@@ -361,7 +562,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   }
   const bool over_cap = max_load > a.cap;
   if (tid == 0) {
-    a.status[0] = (m.misc[1] ? MB_ST_UNBALANCED : 0) | (over_cap ? MB_ST_CAPACITY : 0);
+    a.status[0] = (m.misc[1] ? MB_ST_UNBALANCED : 0) | (over_cap ? MB_ST_CAPACITY : 0) |
+                  (drift && m.misc[4] ? MB_ST_REPLANNED : 0);
     a.status[1] = m.misc[3];
     a.status[2] = max_load;
     a.status[3] = m.misc[0];
@@ -371,7 +573,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
 }  // namespace
 
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
-                       const int32_t* rank_speed, const int32_t* blockflags,
+                       const int32_t* rank_speed, const mb_drift_params* drift,
+                       void* drift_state, const int32_t* blockflags,
                        const int32_t* expert_total, int2* host_range, hipStream_t st) {
   PlanArgs a;
   a.N = d.n_tokens;
@@ -384,6 +587,11 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.NS = g.NS;
   a.nblk = g.nblk;
   for (int r = 0; r < kMaxRanks; ++r) a.speed[r] = r < d.n_ranks ? rank_speed[r] : 0;
+  a.drift_state = static_cast<uint8_t*>(drift_state);
+  a.delta_num = drift ? drift->delta_num : 0;
+  a.delta_den = drift ? drift->delta_den : 1;
+  a.window = drift ? drift->window : 1;
+  a.check_every = drift ? drift->check_every : 1;
   a.expert_total = expert_total;
   a.blockflags = blockflags;
   a.load_pre = o.load_pre;

@@ -36,6 +36,15 @@ Sizes, and the statistic each workload is shaped to hit:
   so the fastest ranks take more than S * K rows: regions are 36864 rows
   (S * K * 9 / 8), and two replica slots per rank (with one, the planner
   stops short of the targets).
+* drift_decode: one layer of the decode workload followed over 60 passes
+  (ViBE, Drift-Aware Recalibration: a layer's load is tracked across forward
+  passes). Routing noise is fresh every pass; the popularity permutation
+  holds for 25 passes, then changes (a shift of the serving workload, as in
+  ViBE's dynamic-workload experiments). Planned with ViBE's defaults:
+  replan when d > 0.05, reference over up to 100 passes, a check every 10.
+  Regions hold 8 S K rows: until the check after a shift, the kept placement
+  sends a rank up to 7.2 times its share, and a smaller region would make
+  those calls fail with CAPACITY.
 """
 from __future__ import annotations
 
@@ -65,6 +74,13 @@ class Workload:
     speed_spread: float = 0.0
     slow_rank: int = -1
     slow_factor: float = 1.0
+    # popularity regimes of a sequence of passes over one layer: the
+    # permutation stays fixed for `regime` calls, then changes (0: a fresh
+    # permutation every call, from the call's own seed)
+    regime: int = 0
+    # drift gate (delta_num, delta_den, window, check_every) of a workload
+    # planned with drift-gated replanning; empty: replan every call
+    drift: tuple = ()
 
     @property
     def tokens_per_rank(self) -> int:
@@ -82,6 +98,12 @@ class Workload:
 
     def seed_for(self, call: int) -> int:
         return self.seed + call
+
+    def pop_seed_for(self, call: int) -> int:
+        """Seed of the popularity permutation of a call."""
+        if self.regime <= 0:
+            return self.seed_for(call)
+        return self.seed + 100000 + call // self.regime
 
     def scaled(self, n_tokens: int) -> "Workload":
         """Same routing model with fewer tokens (a bounded sample)."""
@@ -149,9 +171,19 @@ WORKLOADS["vibe_dsv3_prefill"] = Workload(
          "rank 7 at 1.13), targets in proportion to speed, 2 slots, 36864 rows per region",
 )
 
+WORKLOADS["drift_decode"] = Workload(
+    name="drift_decode", n_tokens=8192, n_experts=256, top_k=8, n_ranks=64, slots_per_rank=1,
+    hidden=7168, dtype_in="fp8", dtype_out="bf16", noise=1, zipf_s=1.1, beta=1.0, seed=8000,
+    calls=60, regime=25, drift=(1, 20, 100, 10), cap_rows=8192,
+    note="one decode layer over 60 passes (64 ranks x 128 tokens, 256 experts, top-8, 1 slot, "
+         "fp8 H=7168): fresh routing noise every pass, popularity changing at passes 25 and 50; "
+         "drift gate d > 0.05, reference window 100, a check every 10 passes; "
+         "regions of 8192 rows (8 S K)",
+)
+
 ORDER = ["tiny", "mixtral", "dsv3_prefill", "kimi_prefill", "decode_drift"]
 SWEEP_ORDER = list(MAXVIO_SWEEP)
-EXTRA_ORDER = SWEEP_ORDER + ["vibe_dsv3_prefill"]
+EXTRA_ORDER = SWEEP_ORDER + ["vibe_dsv3_prefill", "drift_decode"]
 
 
 def get_workload(name: str) -> Workload:

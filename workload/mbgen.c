@@ -121,17 +121,19 @@ void mbgen_log_popularity(uint64_t seed, int32_t n_experts, double zipf_s,
 
 /*
  * Routing decisions for n_tokens tokens: ids[t*K + k], w[t*K + k].
- * noise_kind: 0 = N(0,1), 1 = Gumbel(0,1). Returns 0, or -1 on bad sizes.
+ * noise_kind: 0 = N(0,1), 1 = Gumbel(0,1). The popularity permutation comes
+ * from pop_seed and the per-token noise from noise_seed. Returns 0, or -1
+ * on bad sizes.
  */
-int mbgen_routing(int32_t n_tokens, int32_t n_experts, int32_t top_k,
-                  int32_t noise_kind, double zipf_s, double beta,
-                  uint64_t seed, int32_t* ids, float* w) {
+int mbgen_routing_ex(int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                     int32_t noise_kind, double zipf_s, double beta,
+                     uint64_t pop_seed, uint64_t noise_seed, int32_t* ids, float* w) {
   if (n_tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts ||
       top_k > 256 || (noise_kind != 0 && noise_kind != 1))
     return -1;
   double* lnp = (double*)malloc(sizeof(double) * (size_t)n_experts);
-  mbgen_log_popularity(seed, n_experts, zipf_s, lnp);
-  const uint64_t key = stream_key(seed, MBGEN_TAG_NOISE);
+  mbgen_log_popularity(pop_seed, n_experts, zipf_s, lnp);
+  const uint64_t key = stream_key(noise_seed, MBGEN_TAG_NOISE);
 #pragma omp parallel for schedule(static)
   for (int32_t t = 0; t < n_tokens; ++t) {
     double best_l[256];
@@ -164,6 +166,14 @@ int mbgen_routing(int32_t n_tokens, int32_t n_experts, int32_t top_k,
   }
   free(lnp);
   return 0;
+}
+
+/* One seed for both the popularity permutation and the noise. */
+int mbgen_routing(int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                  int32_t noise_kind, double zipf_s, double beta,
+                  uint64_t seed, int32_t* ids, float* w) {
+  return mbgen_routing_ex(n_tokens, n_experts, top_k, noise_kind, zipf_s, beta, seed, seed,
+                          ids, w);
 }
 
 /* ---- row formats ------------------------------------------------------ */
