@@ -200,6 +200,8 @@ def main() -> int:
                     help="timed steps (default 20; a drift-gated workload: its call count)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--repair", action="store_true",
+                    help="plan with the quota repair after placement (mb_plan_ex)")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="leave out the CPU oracle leg (for profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -269,11 +271,12 @@ def main() -> int:
 
     def plan_call(i, gated=True):
         if drift is None:
-            mb.plan(dims, ids_d, ws, bufs, speeds=speeds)
+            mb.plan(dims, ids_d, ws, bufs, speeds=speeds, repair=args.repair)
         elif gated:
-            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, drift=drift)
+            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, drift=drift,
+                    repair=args.repair)
         else:
-            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds)
+            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, repair=args.repair)
 
     wir_equal = None
     if speeds is not None:
@@ -282,7 +285,7 @@ def main() -> int:
 
     # Expert outputs: the dispatched rows (identity experts), or for fp8
     # rows a generated bf16 buffer.
-    mb.plan(dims, ids_d, ws, bufs, speeds=speeds)
+    mb.plan(dims, ids_d, ws, bufs, speeds=speeds, repair=args.repair)
     if wl.dtype_in == wl.dtype_out:
         mb.dispatch(dims, bufs, x_d, y_exp, xs_d, bs)
     else:
@@ -338,6 +341,9 @@ def main() -> int:
     # combined row is sum_k w_k x_t).
     status = mb.plan_status(bufs)
     mean_load = wl.n_tokens * wl.top_k / wl.n_ranks
+    # pairs served on a rank other than the one their token originates on
+    src = torch.arange(wl.n_tokens, device=dev).unsqueeze(1) // wl.tokens_per_rank
+    nonlocal_pairs = int((bufs.pos.view(wl.n_tokens, wl.top_k) // wl.cap != src).sum())
     if wl.dtype_in == wl.dtype_out:
         samp = torch.arange(0, wl.n_tokens, max(1, wl.n_tokens // 256), device=dev)
         err = (y[samp].float() - x_d[samp].float() * w_d[samp].sum(1, keepdim=True)).abs().max()
@@ -378,7 +384,8 @@ def main() -> int:
         "algorithmic_bytes": {"dispatch": ab["dispatch"], "combine": ab["combine"]},
         "plan_status": {"flags": int(status[0]), "water_level": int(status[1]),
                         "max_load": int(status[2]), "moves": int(status[3]),
-                        "ir_after": round(float(status[2]) / mean_load, 5)},
+                        "ir_after": round(float(status[2]) / mean_load, 5),
+                        "nonlocal_pairs": nonlocal_pairs, "quota_repair": bool(args.repair)},
         "speed_targets": None if speeds is None else {
             "max_load_over_share": round(float(_speed_ratio(bufs.load_post.cpu().numpy(), speeds, wl)), 5),
             "same_with_equal_targets": round(wir_equal, 5)},

@@ -250,6 +250,35 @@ int mb_plan_drift(const mb_dims* dims, const int32_t* ids_dev, const int32_t* ra
                   const mb_drift_params* params, void* state_dev, void* ws_dev,
                   size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream);
 
+/* Options of mb_plan_ex; a zero-filled struct gives mb_plan. */
+typedef struct mb_plan_options {
+  const int32_t* rank_speed;   /* [P] host speeds as in mb_plan_weighted, or NULL (equal) */
+  const mb_drift_params* drift; /* drift gate as in mb_plan_drift, or NULL */
+  void* drift_state;           /* its device state; NULL exactly when drift is NULL */
+  int32_t quota_repair;        /* non-zero: quota repair between placement and routing */
+} mb_plan_options;
+
+/*
+ * mb_plan with any of rank speeds, the drift gate and the quota repair
+ * [ISER HALO-Q stage 4: a circle-method tournament over disjoint rank pairs
+ * cancels opposite token flows]. The repair runs after the placement (fresh
+ * or kept): n = P rounded up to even players, n - 1 rounds; in round r,
+ * player 0 stays at position 0, player 1 + (p - 1 + r) mod (n - 1) sits at
+ * position p >= 1, and positions k and n-1-k meet (player P is a bye). For
+ * a pair a < b, over the experts both hold (a's replica slots in order whose
+ * expert b also holds, then b's replica slots in order whose expert is
+ * homed on a), with d the rank's own pairs of the expert and Q its quota,
+ * x_ab = min((d_a - Q_a)^+, (Q_b - d_b)^+) and x_ba = min((d_b - Q_b)^+,
+ * (Q_a - d_a)^+); m = min(sum x_ab, sum x_ba) units of quota move from b to
+ * a over the x_ab experts and from a to b over the x_ba experts, in that
+ * order, each taking at most its own x. Rank loads and expert totals are
+ * unchanged and 2m more pairs are served where they originate.
+ * Error behaviour as mb_plan, mb_plan_weighted and mb_plan_drift; drift and
+ * drift_state must be both set or both NULL.
+ */
+int mb_plan_ex(const mb_dims* dims, const int32_t* ids_dev, const mb_plan_options* opt,
+               void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream);
+
 /*
  * Dispatch [MoonEP, "What MoonEP enforces and how": tokens written into
  * fixed-shape expert-grouped buffers]: buf[pos[t][k]] = x[t] for every pair.

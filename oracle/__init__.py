@@ -87,6 +87,11 @@ class DriftState:
         raise AttributeError(name)
 
 
+class _PlanOptionsC(ctypes.Structure):
+    _fields_ = [("rank_speed", ctypes.c_void_p), ("drift", ctypes.POINTER(DriftParams)),
+                ("drift_state", ctypes.POINTER(_DriftStateC)), ("quota_repair", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -107,6 +112,11 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(_DriftStateC), ctypes.POINTER(PlanOut),
                                        ctypes.POINTER(Report)]
         L.mbref_plan_drift.restype = ctypes.c_int
+        L.mbref_plan_ex.argtypes = [ctypes.POINTER(Dims), vp, ctypes.POINTER(_PlanOptionsC),
+                                    ctypes.POINTER(PlanOut), ctypes.POINTER(Report)]
+        L.mbref_plan_ex.restype = ctypes.c_int
+        L.mbref_circle_schedule.argtypes = [ctypes.c_int32, vp]
+        L.mbref_circle_schedule.restype = None
         L.mbref_dispatch.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp]
         L.mbref_dispatch.restype = ctypes.c_int
         L.mbref_dispatch_window.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp,
@@ -163,10 +173,12 @@ def _ptr(a: np.ndarray):
 
 
 def plan(dims: Dims, ids: np.ndarray, move_rule: int = MOVE_FILL_HOST,
-         speeds: np.ndarray | None = None, drift: tuple | None = None) -> Plan:
+         speeds: np.ndarray | None = None, drift: tuple | None = None,
+         repair: bool = False) -> Plan:
     """Steps O0-O4 and O7. ``speeds`` (int32 [P]) gives per-rank targets in
     proportion to rank speed in place of the single water level. ``drift`` =
-    (DriftParams, DriftState) plans one call of a drift-gated sequence."""
+    (DriftParams, DriftState) plans one call of a drift-gated sequence.
+    ``repair`` runs the quota repair between placement and assignment."""
     N, K, E, P, R = dims.n_tokens, dims.top_k, dims.n_experts, dims.n_ranks, dims.slots_per_rank
     ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(N, K)
     eh = E // P if P > 0 else 0
@@ -180,7 +192,14 @@ def plan(dims: Dims, ids: np.ndarray, move_rule: int = MOVE_FILL_HOST,
     }
     po = PlanOut(**{k: v.ctypes.data_as(_i32p) for k, v in a.items()})
     rep = Report()
-    if drift is not None:
+    if repair:
+        sp = None if speeds is None else np.ascontiguousarray(speeds, dtype=np.int32)
+        opt = _PlanOptionsC(sp.ctypes.data if sp is not None else None,
+                            ctypes.pointer(drift[0]) if drift else None,
+                            ctypes.pointer(drift[1].c) if drift else None, 1)
+        rc = lib().mbref_plan_ex(ctypes.byref(dims), _ptr(ids), ctypes.byref(opt),
+                                 ctypes.byref(po), ctypes.byref(rep))
+    elif drift is not None:
         prm, st = drift
         sp = None if speeds is None else np.ascontiguousarray(speeds, dtype=np.int32)
         rc = lib().mbref_plan_drift(ctypes.byref(dims), _ptr(ids),
@@ -232,6 +251,16 @@ def plan_drift_rc(dims: Dims, ids: np.ndarray, params: DriftParams, state: Drift
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     return lib().mbref_plan_drift(ctypes.byref(dims), _ptr(ids), None, ctypes.byref(params),
                                   ctypes.byref(state.c), ctypes.byref(po), None)
+
+
+def circle_schedule(n_ranks: int) -> np.ndarray:
+    """[rounds, pairs, 2] ranks met in each round of the quota repair's
+    tournament (index n_ranks = the bye of an odd count)."""
+    n = n_ranks + (n_ranks & 1)
+    out = np.zeros((max(n - 1, 0), n // 2, 2), np.int32)
+    if n >= 2:
+        lib().mbref_circle_schedule(n_ranks, _ptr(out))
+    return out
 
 
 def row_bytes_in(dims: Dims) -> int:

@@ -92,20 +92,120 @@ typedef struct keep_t {
 } keep_t;
 
 static int plan_core(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
-                     int32_t move_rule, const keep_t* keep, int32_t* order_out,
+                     int32_t move_rule, const keep_t* keep, int32_t* order_out, int repair,
                      mbref_plan_out* o, mbref_report* rep);
 
 int mbref_plan(const mbref_dims* dm, const int32_t* ids, int32_t move_rule,
                mbref_plan_out* o, mbref_report* rep) {
-  return plan_core(dm, ids, NULL, move_rule, NULL, NULL, o, rep);
+  return plan_core(dm, ids, NULL, move_rule, NULL, NULL, 0, o, rep);
 }
 
 
+/* Round `round` of the circle method for n (even) players: player 0 stays,
+ * the others rotate one place per round; position k meets position n-1-k. */
+static void circle_pair(int64_t n, int64_t round, int64_t k, int64_t* a, int64_t* b) {
+  const int64_t pa = k, pb = n - 1 - k;
+  *a = pa == 0 ? 0 : 1 + (pa - 1 + round) % (n - 1);
+  *b = pb == 0 ? 0 : 1 + (pb - 1 + round) % (n - 1);
+}
+
+void mbref_circle_schedule(int32_t P, int32_t* pairs) {
+  const int64_t n = P + (P & 1);
+  for (int64_t r = 0; r + 1 < n; ++r)
+    for (int64_t k = 0; k < n / 2; ++k) {
+      int64_t a, b;
+      circle_pair(n, r, k, &a, &b);
+      pairs[(r * (n / 2) + k) * 2] = (int32_t)a;
+      pairs[(r * (n / 2) + k) * 2 + 1] = (int32_t)b;
+    }
+}
+
+/* Quota of expert e on rank r (home quota or replica slot), or NULL if r
+ * does not hold e. */
+static int64_t* quota_at(int64_t e, int64_t r, int64_t Eh, int64_t R, const int32_t* rep_expert,
+                         int64_t* qh, int64_t* rq) {
+  if (e / Eh == r) return &qh[e];
+  for (int64_t j = 0; j < R; ++j)
+    if (rep_expert[r * R + j] == e) return &rq[r * R + j];
+  return NULL;
+}
+
+/* [ISER] HALO-Q stage 4, quota repair: a circle-method tournament over
+ * disjoint rank pairs cancels opposite token flows. For a pair a < b and an
+ * expert e both hold, a sends x_ab(e) = min((d[a][e] - Q[e][a])^+,
+ * (Q[e][b] - d[b][e])^+) of its own pairs of e that b's quota could give
+ * back to a; likewise x_ba(e). With m = min(sum_e x_ab(e), sum_e x_ba(e)),
+ * m units of quota move from b to a over the experts of x_ab (and m from a
+ * to b over those of x_ba): both ranks keep their loads, every expert keeps
+ * its total, and 2m pairs become local. The experts both hold are taken in
+ * the order of a's replica slots (experts homed on b or also replicated on
+ * b), then b's replica slots (experts homed on a). One tournament: n - 1
+ * rounds of n/2 pairs, n = P rounded up to even (the extra player is a
+ * bye). */
+static void quota_repair(int64_t P, int64_t E, int64_t R, const int32_t* counts,
+                         const int32_t* rep_expert, int64_t* qh, int64_t* rq) {
+  const int64_t Eh = E / P, n = P + (P & 1);
+  int64_t* common = calloc((size_t)(2 * R + 1), sizeof(int64_t));
+  if (!common) return;
+  for (int64_t round = 0; round + 1 < n; ++round)
+    for (int64_t k = 0; k < n / 2; ++k) {
+      int64_t a, b;
+      circle_pair(n, round, k, &a, &b);
+      if (a >= P || b >= P) continue; /* bye */
+      if (a > b) {
+        const int64_t t = a;
+        a = b;
+        b = t;
+      }
+      int64_t nc = 0;
+      for (int64_t j = 0; j < R; ++j) {
+        const int64_t e = rep_expert[a * R + j];
+        if (e >= 0 && quota_at(e, b, Eh, R, rep_expert, qh, rq)) common[nc++] = e;
+      }
+      for (int64_t j = 0; j < R; ++j) {
+        const int64_t e = rep_expert[b * R + j];
+        if (e >= 0 && e / Eh == a) common[nc++] = e;
+      }
+      int64_t fab = 0, fba = 0;
+      for (int64_t i = 0; i < nc; ++i) {
+        const int64_t e = common[i];
+        const int64_t qa = *quota_at(e, a, Eh, R, rep_expert, qh, rq);
+        const int64_t qb = *quota_at(e, b, Eh, R, rep_expert, qh, rq);
+        const int64_t da = counts[a * E + e], db = counts[b * E + e];
+        const int64_t ua = da > qa ? da - qa : 0, sb = qb > db ? qb - db : 0;
+        const int64_t ub = db > qb ? db - qb : 0, sa = qa > da ? qa - da : 0;
+        fab += ua < sb ? ua : sb;
+        fba += ub < sa ? ub : sa;
+      }
+      int64_t left_ab = fab < fba ? fab : fba, left_ba = left_ab;
+      for (int64_t i = 0; i < nc; ++i) {
+        const int64_t e = common[i];
+        int64_t* qa = quota_at(e, a, Eh, R, rep_expert, qh, rq);
+        int64_t* qb = quota_at(e, b, Eh, R, rep_expert, qh, rq);
+        const int64_t da = counts[a * E + e], db = counts[b * E + e];
+        const int64_t ua = da > *qa ? da - *qa : 0, sb = *qb > db ? *qb - db : 0;
+        const int64_t ub = db > *qb ? db - *qb : 0, sa = *qa > da ? *qa - da : 0;
+        int64_t t = ua < sb ? ua : sb;
+        if (t > left_ab) t = left_ab;
+        *qa += t;
+        *qb -= t;
+        left_ab -= t;
+        t = ub < sa ? ub : sa;
+        if (t > left_ba) t = left_ba;
+        *qb += t;
+        *qa -= t;
+        left_ba -= t;
+      }
+    }
+  free(common);
+}
+
 /* Steps O0-O4 and O7. With `keep`, step O2 reuses that placement instead of
  * running the greedy; otherwise the greedy's slots are written, in move
- * order, to order_out (if not NULL). */
+ * order, to order_out (if not NULL). With `repair`, the quota repair runs
+ * between placement and assignment. */
 static int plan_core(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
-                     int32_t move_rule, const keep_t* keep, int32_t* order_out,
+                     int32_t move_rule, const keep_t* keep, int32_t* order_out, int repair,
                      mbref_plan_out* o, mbref_report* rep) {
   if (!dm || !o || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
   if (move_rule != MBREF_MOVE_FILL_HOST && move_rule != MBREF_MOVE_EXCESS_ONLY)
@@ -276,6 +376,8 @@ static int plan_core(const mbref_dims* dm, const int32_t* ids, const int32_t* sp
     }
   }
 
+  if (repair) quota_repair(P, E, R, o->counts, o->rep_expert, qh, rq);
+
   /* Quotas per (expert, host) and the local slot of each (host, expert):
    * home experts first by id, then replica slots ([MoonEP] [E+B,H,H']). */
   for (int64_t i = 0; i < E * P; ++i) slot_of[i] = -1;
@@ -401,7 +503,7 @@ done:
 
 int mbref_plan_weighted(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
                         int32_t move_rule, mbref_plan_out* o, mbref_report* rep) {
-  return plan_core(dm, ids, speed, move_rule, NULL, NULL, o, rep);
+  return plan_core(dm, ids, speed, move_rule, NULL, NULL, 0, o, rep);
 }
 
 /* [ViBE] Drift-Aware Recalibration: d = 1 - w.w^ / (|w| |w^|). The window's
@@ -418,9 +520,9 @@ static double cosine_distance(const int64_t* c, const int64_t* ws, int64_t E) {
   return 1.0 - (double)dot / (sqrt((double)n1) * sqrt((double)n2));
 }
 
-int mbref_plan_drift(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
-                     const mbref_drift_params* prm, mbref_drift_state* st,
-                     mbref_plan_out* o, mbref_report* rep) {
+static int plan_drift_core(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
+                           const mbref_drift_params* prm, mbref_drift_state* st, int repair,
+                           mbref_plan_out* o, mbref_report* rep) {
   if (!dm || !o || !prm || !st || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
   if (prm->delta_den < 1 || prm->delta_num < 0 || prm->delta_num > prm->delta_den ||
       prm->window < 1 || prm->window > MBREF_MAX_WINDOW || prm->check_every < 1)
@@ -433,7 +535,7 @@ int mbref_plan_drift(const mbref_dims* dm, const int32_t* ids, const int32_t* sp
       const int32_t e = ids[t * K + k];
       int bad = e < 0 || e >= E;
       for (int64_t k2 = 0; k2 < k; ++k2) bad |= ids[t * K + k2] == e;
-      if (bad) return plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, NULL, NULL, o, rep);
+      if (bad) return plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, NULL, NULL, 0, o, rep);
     }
   int64_t* c = calloc((size_t)E, sizeof(int64_t));
   int32_t* order = calloc((size_t)(P * R + 1), sizeof(int32_t));
@@ -452,7 +554,7 @@ int mbref_plan_drift(const mbref_dims* dm, const int32_t* ids, const int32_t* sp
   }
   int rc;
   if (replan) {
-    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, NULL, order, o, rep);
+    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, NULL, order, repair, o, rep);
     if (rc == MBREF_OK) {
       for (int64_t i = 0; i < P * R; ++i) st->rep[i] = o->rep_expert[i];
       for (int64_t i = 0; i < P * R; ++i) st->order[i] = i < o->status[3] ? order[i] : -1;
@@ -467,7 +569,7 @@ int mbref_plan_drift(const mbref_dims* dm, const int32_t* ids, const int32_t* sp
     }
   } else {
     const keep_t keep = {st->rep, st->order, st->n_moves};
-    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, &keep, NULL, o, rep);
+    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, &keep, NULL, repair, o, rep);
     if (rc == MBREF_OK && st->nwin < prm->window) {
       for (int64_t e = 0; e < E; ++e) st->wsum[e] += c[e];
       st->nwin += 1;
@@ -477,6 +579,24 @@ int mbref_plan_drift(const mbref_dims* dm, const int32_t* ids, const int32_t* sp
   free(c);
   free(order);
   return rc;
+}
+
+int mbref_plan_drift(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
+                     const mbref_drift_params* prm, mbref_drift_state* st,
+                     mbref_plan_out* o, mbref_report* rep) {
+  return plan_drift_core(dm, ids, speed, prm, st, 0, o, rep);
+}
+
+int mbref_plan_ex(const mbref_dims* dm, const int32_t* ids, const mbref_plan_options* opt,
+                  mbref_plan_out* o, mbref_report* rep) {
+  if (!opt) return MBREF_ERR_INVALID_ARG;
+  if (opt->drift || opt->drift_state) {
+    if (!opt->drift || !opt->drift_state) return MBREF_ERR_INVALID_ARG;
+    return plan_drift_core(dm, ids, opt->rank_speed, opt->drift, opt->drift_state,
+                           opt->quota_repair != 0, o, rep);
+  }
+  return plan_core(dm, ids, opt->rank_speed, MBREF_MOVE_FILL_HOST, NULL, NULL,
+                   opt->quota_repair != 0, o, rep);
 }
 
 /* O5 — dispatch: the row of token t is copied to every row pos[t][k]

@@ -149,6 +149,23 @@ int mbref_plan_drift(const mbref_dims* dims, const int32_t* ids, const int32_t* 
                      const mbref_drift_params* params, mbref_drift_state* state,
                      mbref_plan_out* out, mbref_report* report);
 
+/* Everything at once: rank speeds (NULL = equal), a drift gate (both NULL
+ * = none) and the quota repair (non-zero = on, after placement). */
+typedef struct mbref_plan_options {
+  const int32_t* rank_speed;
+  const mbref_drift_params* drift;
+  mbref_drift_state* drift_state;
+  int32_t quota_repair;
+} mbref_plan_options;
+
+int mbref_plan_ex(const mbref_dims* dims, const int32_t* ids, const mbref_plan_options* opt,
+                  mbref_plan_out* out, mbref_report* report);
+
+/* The circle-method schedule of the quota repair: for n = P rounded up to
+ * even, (n - 1) rounds of n/2 pairs, written as pairs[(round*n/2 + k)*2 + {0,1}];
+ * index P is the bye of an odd P. */
+void mbref_circle_schedule(int32_t P, int32_t* pairs);
+
 /* Step O5: buf[pos[t][k]] = x[t] (and the fp8 scale row). Rows of buf that
  * no pair maps to are left untouched. Returns 1 if status is fatal (nothing
  * written), 0 otherwise. */

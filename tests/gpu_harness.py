@@ -37,10 +37,12 @@ class GpuPlan:
         self.bufs = mb.PlanBuffers.allocate(dims, self.device)
         self.ws = mb.alloc_workspace(dims, self.device)
 
-    def run(self, ids: np.ndarray | torch.Tensor, stream=None, speeds=None, drift=None):
+    def run(self, ids: np.ndarray | torch.Tensor, stream=None, speeds=None, drift=None,
+            repair=False):
         ids_d = ids if isinstance(ids, torch.Tensor) else torch.from_numpy(
             np.ascontiguousarray(ids, np.int32)).to(self.device)
-        mb.plan(self.dims, ids_d, self.ws, self.bufs, stream, speeds=speeds, drift=drift)
+        mb.plan(self.dims, ids_d, self.ws, self.bufs, stream, speeds=speeds, drift=drift,
+                repair=repair)
         return self
 
     def fetch(self) -> dict:

@@ -556,3 +556,84 @@ def test_drift_sequences_sweep(P, eh, K, R, S, H, delta):
         ref = O.plan(od, ids, speeds=speeds, drift=(oprm, st))
         G.assert_plan_equal(got, ref)
         _assert_state_equal(state, st, E, f"P{P} R{R} call {call}")
+
+
+# ---- quota repair ------------------------------------------------------------------
+
+def test_hand_example_repair_on_gpu():
+    """The hand-derived repair example through mb_plan_ex: quotas repaired as
+    stored, and the whole plan equal to the oracle's."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "hand_example_repair.json")))
+    dd = dict(g["dims"])
+    dd["hidden"] = 8
+    ids = np.array(g["ids"], np.int32).reshape(-1, 1)
+    dg = mb.Dims.make(**dd, dtype_in="bf16", dtype_out="bf16")
+    od = O.make_dims(**dd, dtype_in="bf16", dtype_out="bf16")
+    got = G.GpuPlan(dg).run(ids, repair=True).fetch()
+    assert np.array_equal(got["slot_quota"].reshape(2, 5), g["slot_quota_repaired"])
+    G.assert_plan_equal(got, O.plan(od, ids, repair=True))
+    plain = G.GpuPlan(dg).run(ids).fetch()
+    assert np.array_equal(plain["slot_quota"].reshape(2, 5), g["slot_quota_placed"])
+
+
+def test_repair_pattern_sweep():
+    """40 pattern inputs (2 to 64 ranks, 2 to 4 slots) with the repair: every
+    plan bit-exact; rows dispatched and combined on every fifth case."""
+    from tests.crafted import repair_cases, repair_pattern_ids
+
+    for n, (P, pairs, R, seed) in enumerate(repair_cases()):
+        ids = repair_pattern_ids(P, pairs, seed)
+        N, E, H = 8 * P, 3 * P, 64
+        dg = mb.Dims.make(N, 1, E, P, R, H, cap=16, dtype_in="f32", dtype_out="f32")
+        od = O.make_dims(N, 1, E, P, R, H, cap=16, dtype_in="f32", dtype_out="f32")
+        G.log(f"repair pattern P={P} pairs={len(pairs)} R={R} seed={seed}")
+        gp = G.GpuPlan(dg).run(ids, repair=True)
+        ref = O.plan(od, ids, repair=True)
+        G.assert_plan_equal(gp.fetch(), ref)
+        if n % 5 == 0:
+            w = np.ones((N, 1), np.float32)
+            x = W.rows_f32(seed, W.TAG_X, H, n=N)
+            ye = W.rows_f32(seed, W.TAG_YEXP, H, n=P * 16)
+            buf, _, y = G.run_rows(dg, gp, x, None, ye, w)
+            ref_buf, _, _ = O.dispatch(od, ref, x, None)
+            used = ref.row_src >= 0
+            assert np.array_equal(buf[used], ref_buf[used])
+            y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, ye)
+            G.assert_combine_close(y, y_ref, mag, "f32")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "decode_drift", "kimi_prefill"])
+def test_repair_on_workloads_gpu(name):
+    wl = W.get_workload(name)
+    ids, _ = W.routing_for(wl)
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    G.assert_plan_equal(G.GpuPlan(dg).run(ids, repair=True).fetch(), O.plan(od, ids, repair=True))
+
+
+def test_repair_with_speeds_and_drift():
+    """All three options at once over a 10-call sequence of pattern inputs
+    whose planted pairs change every 3 calls, in lockstep with the oracle."""
+    from tests.crafted import repair_pattern_ids
+
+    P, R = 13, 3
+    N, E = 8 * P, 3 * P
+    dg = mb.Dims.make(N, 1, E, P, R, 8, cap=24, dtype_in="bf16", dtype_out="bf16")
+    od = O.make_dims(N, 1, E, P, R, 8, cap=24, dtype_in="bf16", dtype_out="bf16")
+    speeds = np.random.default_rng(3).integers(900, 1100, P).astype(np.int32)
+    state = mb.alloc_drift_state(dg, G.dev())
+    st = O.DriftState(E, P, R)
+    gprm, oprm = mb.DriftParams(1, 10, 4, 2), O.DriftParams(1, 10, 4, 2)
+    gp = G.GpuPlan(dg)
+    for call in range(10):
+        rng = np.random.default_rng(call // 3)
+        perm = rng.permutation(P)
+        pairs = [(int(perm[2 * i]), int(perm[2 * i + 1])) for i in range(3)]
+        ids = repair_pattern_ids(P, pairs, call)
+        got = gp.run(ids, speeds=speeds, drift=(gprm, state), repair=True).fetch()
+        ref = O.plan(od, ids, speeds=speeds, drift=(oprm, st), repair=True)
+        G.assert_plan_equal(got, ref)
+        _assert_state_equal(state, st, E, f"call {call}")

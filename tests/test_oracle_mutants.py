@@ -74,6 +74,17 @@ MUTANTS = [
      "(sqrt((double)n1) * sqrt((double)n2))", "((double)n1 + (double)n2)"),
     ("kept replica takes pairs whatever its home's load",
      "if (load[h] > tau[h] && load[dst] < tau[dst]) {", "if (load[dst] < tau[dst]) {"),
+    ("repair moves quota one way only",
+     "        *qb += t;\n        *qa -= t;\n        left_ba -= t;", "        left_ba -= t;"),
+    ("repair cancels the larger flow",
+     "int64_t left_ab = fab < fba ? fab : fba, left_ba = left_ab;",
+     "int64_t left_ab = fab > fba ? fab : fba, left_ba = left_ab;"),
+    ("circle method without rotation",
+     "*a = pa == 0 ? 0 : 1 + (pa - 1 + round) % (n - 1);", "*a = pa == 0 ? 0 : 1 + (pa - 1) % (n - 1);"),
+    ("repair misses replicas of a's home experts on b",
+     "if (e >= 0 && e / Eh == a) common[nc++] = e;", "if (0) common[nc++] = e;"),
+    ("repair skips pairs with the last rank",
+     "if (a >= P || b >= P) continue; /* bye */", "if (a >= P - 1 || b >= P - 1) continue;"),
     ("duplicate ids not flagged",
      "if (ids[t * K + k2] == e) flags |= MBREF_ST_DUP_ID;", "if (0) flags |= MBREF_ST_DUP_ID;"),
 ]

@@ -332,6 +332,145 @@ def test_drift_rejects_bad_params_and_keeps_state_on_bad_ids():
     assert st.calls == 1 and st.replans == 1 and st.nwin == 1
 
 
+def test_hand_example_repair():
+    """Quota repair: P=2 ranks of 3 home experts, R=2, K=1, 16 tokens, T = 8.
+
+    Sources: rank 0 sends e0 x3, e1, e2 x2, e3, e4; rank 1 sends e0 x2,
+    e1 x4, e2 x2, so c = [5, 5, 4, 1, 1, 0] and L = [14, 2].
+    Placement: rank 0 gives e0 (quota 5; ties with e1, lower id) to rank 1,
+    m = min(8 - 2, 5) = 5 -> loads [9, 7]; then e1 (5) to rank 1's second
+    slot, m = min(8 - 7, 5) = 1 -> loads [8, 8]. Quotas: e0 0 at home, 5 on
+    rank 1; e1 4 at home, 1 on rank 1.
+    Routing without repair: rank 0's 3 pairs of e0 go to rank 1 (rank 1
+    keeps its own 2), rank 1's pairs of e1 beyond its quota (3) go to
+    rank 0, rank 1's e2 pairs (2) and rank 0's e3, e4 (2) cross too:
+    10 non-local pairs.
+    Repair, the only pair (0, 1): both hold e0 and e1 (b's slots, homed on
+    a). x_01(e0) = min(3 - 0, 5 - 2) = 3, x_10(e1) = min(4 - 1, 4 - 1) = 3,
+    m = 3: e0's quota 3 moves to rank 0 (0 -> 3, 5 -> 2), e1's 3 to rank 1
+    (4 -> 1, 1 -> 4). Loads stay [8, 8]; 6 pairs become local: 4 remain
+    (e2 from rank 1, e3 and e4 from rank 0 have a single host), which is
+    the least any routing with these hosts and loads can reach.
+    """
+    g = json.load(open(os.path.join(GOLDEN, "hand_example_repair.json")))
+    d = O.make_dims(**g["dims"])
+    ids = np.array(g["ids"], np.int32).reshape(-1, 1)
+    a = O.plan(d, ids)
+    b = O.plan(d, ids, repair=True)
+    for p, q, nl in ((a, "slot_quota_placed", "nonlocal_placed"),
+                     (b, "slot_quota_repaired", "nonlocal_repaired")):
+        assert np.array_equal(p.status, g["status"])
+        assert np.array_equal(p.rep_expert, g["rep_expert"])
+        assert np.array_equal(p.load_post, g["load_post"])
+        assert np.array_equal(p.slot_quota, g[q]), q
+        assert p.report["nonlocal_pairs"] == g[nl], nl
+        C.check_layout(p, ids, d.n_ranks, d.n_experts, d.slots_per_rank, d.cap)
+    assert _routing_lp_optimum(b, d) == g["nonlocal_best"]
+
+
+def _routing_lp_optimum(p, d) -> int:
+    """Zepp eq. (1) with a_ij = [i != j] over the plan's hosts, each rank's
+    load fixed at the plan's (the quotas free): a transportation problem,
+    solved by scipy's LP (its constraint matrix is totally unimodular, so
+    the optimum is integral)."""
+    from scipy.optimize import linprog
+
+    P, E = d.n_ranks, d.n_experts
+    eh = E // P
+    hosts = [[e // eh] + [r for r in range(P) for j in range(d.slots_per_rank)
+                          if p.rep_expert[r, j] == e] for e in range(E)]
+    dm = p.counts
+    var = [(i, e, j) for i in range(P) for e in range(E) if dm[i, e] > 0 for j in hosts[e]]
+    if not var:
+        return 0
+    cost = np.array([0.0 if i == j else 1.0 for (i, e, j) in var])
+    rows, rhs = [], []
+    for i in range(P):
+        for e in range(E):
+            if dm[i, e] > 0:
+                rows.append(np.array([1.0 if (v[0], v[1]) == (i, e) else 0.0 for v in var]))
+                rhs.append(dm[i, e])
+    for j in range(P):
+        rows.append(np.array([1.0 if v[2] == j else 0.0 for v in var]))
+        rhs.append(p.load_post[j])
+    res = linprog(cost, A_eq=np.array(rows), b_eq=np.array(rhs, float), bounds=(0, None),
+                  method="highs")
+    assert res.status == 0
+    return int(round(res.fun))
+
+
+@pytest.mark.parametrize("P", list(range(1, 18)))
+def test_circle_schedule(P):
+    """The repair's tournament: n - 1 rounds (n = P rounded up to even) of
+    disjoint pairs in which every two ranks meet exactly once (the round-
+    robin of the circle method); an odd P leaves one rank a bye per round."""
+    sch = O.circle_schedule(P)
+    n = P + (P & 1)
+    assert sch.shape == (max(n - 1, 0), n // 2, 2)
+    met = set()
+    for rnd in sch:
+        seen = rnd.ravel().tolist()
+        assert len(set(seen)) == len(seen) == n  # disjoint, everyone plays
+        for a, b in rnd:
+            if a < P and b < P:
+                key = (min(a, b), max(a, b))
+                assert key not in met
+                met.add(key)
+    assert len(met) == P * (P - 1) // 2
+
+
+def _repair_checks(d, ids, speeds=None):
+    a = O.plan(d, ids, speeds=speeds)
+    b = O.plan(d, ids, speeds=speeds, repair=True)
+    assert b.flags == a.flags and np.array_equal(b.rep_expert, a.rep_expert)
+    assert np.array_equal(b.load_post, a.load_post)  # loads never change
+    Q = C.quotas_matrix(b, d.n_experts, d.n_ranks)
+    assert np.array_equal(Q.sum(1), a.counts.sum(0))  # nor expert totals
+    assert np.all(Q >= 0)
+    if not b.flags & O.ST_CAPACITY:
+        C.check_layout(b, ids, d.n_ranks, d.n_experts, d.slots_per_rank, d.cap)
+    # routing stays optimal for the repaired quotas, and never gets worse
+    assert b.report["nonlocal_pairs"] == C.transport_nonlocal_optimum(b.counts, Q)
+    assert b.report["nonlocal_pairs"] <= a.report["nonlocal_pairs"]
+    return a, b
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "decode_drift"])
+def test_repair_on_workloads(name):
+    """On the workloads (tokens routed independently of their rank) the
+    greedy leaves no opposite flows on experts two ranks share: the repair
+    changes nothing, and the routing is already the best these hosts and
+    loads allow (tiny, mixtral)."""
+    wl, ids, w, d, _ = _plan_workload(name)
+    a, b = _repair_checks(d, ids)
+    assert np.array_equal(a.slot_quota, b.slot_quota)
+    if name != "decode_drift":
+        assert a.report["nonlocal_pairs"] == _routing_lp_optimum(a, d)
+
+
+def test_repair_on_pattern_inputs():
+    """Inputs built so that rank pairs hold opposite flows: the repair cancels
+    them and never moves a load. Against the routing optimum over the plan's
+    hosts and loads (scipy LP, cases up to 8 ranks) it never goes below it,
+    and reaches it when a single pattern pair is planted; with several, the
+    greedy can interleave their replicas into cycles over three or more
+    ranks, which pairwise cancellation cannot undo."""
+    from tests.crafted import repair_cases, repair_pattern_ids
+
+    fired = 0
+    for P, pairs, R, seed in repair_cases():
+        ids = repair_pattern_ids(P, pairs, seed)
+        d = O.make_dims(8 * P, 1, 3 * P, P, R, 16, cap=16)
+        a, b = _repair_checks(d, ids)
+        fired += b.report["nonlocal_pairs"] < a.report["nonlocal_pairs"]
+        if P <= 8:
+            opt = _routing_lp_optimum(b, d)
+            assert b.report["nonlocal_pairs"] >= opt
+            if len(pairs) == 1:
+                assert b.report["nonlocal_pairs"] == opt
+    assert fired >= 20
+
+
 SMALL = ["tiny", "mixtral", "decode_drift"]
 
 
@@ -672,6 +811,43 @@ def test_exhaustive_placements_tiny():
                 own[e].append(r)
     assert greedy >= _min_max_load(c, own, P) >= best >= int(p.status[1])
     print(f"tiny: greedy max load {greedy}, best over all placements {best}")
+
+
+def test_exhaustive_locality_tiny():
+    """pi8's locality half: over all 13^4 single-slot placements of the tiny
+    workload that can reach max load T, the fewest non-local pairs any
+    routing with loads <= T achieves (scipy LP per placement: a
+    transportation problem, so integral). The greedy (with or without the
+    quota repair) is feasible, so it cannot beat that; the gap is reported."""
+    from scipy.optimize import linprog
+
+    wl, ids, w, d, p = _plan_workload("tiny")
+    P, E = wl.n_ranks, wl.n_experts
+    eh, T, dm = E // P, int(p.status[1]), p.counts
+    c = dm.sum(0)
+    home = [[e // eh] for e in range(E)]
+    best = None
+    for pl in itertools.product(*[[-1] + [e for e in range(E) if e // eh != r] for r in range(P)]):
+        hosts = [list(h) for h in home]
+        for r, e in enumerate(pl):
+            if e >= 0:
+                hosts[e].append(r)
+        if _min_max_load(c, hosts, P) > T:
+            continue
+        var = [(i, e, j) for i in range(P) for e in range(E) if dm[i, e] > 0 for j in hosts[e]]
+        cost = [0.0 if i == j else 1.0 for (i, e, j) in var]
+        a_eq = [[1.0 if (v[0], v[1]) == (i, e) else 0.0 for v in var]
+                for i in range(P) for e in range(E) if dm[i, e] > 0]
+        b_eq = [dm[i, e] for i in range(P) for e in range(E) if dm[i, e] > 0]
+        a_ub = [[1.0 if v[2] == j else 0.0 for v in var] for j in range(P)]
+        res = linprog(cost, A_ub=a_ub, b_ub=[T] * P, A_eq=a_eq, b_eq=b_eq, bounds=(0, None),
+                      method="highs")
+        if res.status == 0 and (best is None or res.fun < best):
+            best = int(round(res.fun))
+    greedy = p.report["nonlocal_pairs"]
+    repaired = O.plan(d, ids, repair=True).report["nonlocal_pairs"]
+    assert p.flags == 0 and greedy >= best and repaired >= best
+    print(f"tiny: non-local pairs greedy {greedy}, repaired {repaired}, best over placements {best}")
 
 
 # ---- report formulas -------------------------------------------------------------

@@ -100,6 +100,14 @@ class DriftParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("delta_num", "delta_den", "window", "check_every")]
 
 
+class _PlanOptionsC(ctypes.Structure):
+    _fields_ = [("rank_speed", _i32p), ("drift", ctypes.POINTER(DriftParams)),
+                ("drift_state", _vp), ("quota_repair", ctypes.c_int32)]
+
+
+_lib.mb_plan_ex.argtypes = [ctypes.POINTER(Dims), _vp, ctypes.POINTER(_PlanOptionsC), _vp,
+                            ctypes.c_size_t, ctypes.POINTER(_PlanBufsC), _vp]
+_lib.mb_plan_ex.restype = ctypes.c_int
 _lib.mb_drift_state_bytes.argtypes = [ctypes.POINTER(Dims)]
 _lib.mb_drift_state_bytes.restype = ctypes.c_size_t
 _lib.mb_plan_drift.argtypes = [ctypes.POINTER(Dims), _vp, _i32p, ctypes.POINTER(DriftParams), _vp,
@@ -114,8 +122,8 @@ _lib.mb_plan_status.argtypes = [ctypes.POINTER(_PlanBufsC), _vp, _i32p]
 _lib.mb_plan_status.restype = ctypes.c_int
 
 EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan",
-           "mb_plan_weighted", "mb_drift_state_bytes", "mb_plan_drift", "mb_dispatch",
-           "mb_combine", "mb_plan_status")
+           "mb_plan_weighted", "mb_drift_state_bytes", "mb_plan_drift", "mb_plan_ex",
+           "mb_dispatch", "mb_combine", "mb_plan_status")
 ST_REPLANNED = 16
 MAX_WINDOW = 4096
 MAX_SPEED = 1 << 20
@@ -184,11 +192,22 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
 
 
 def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, stream=None,
-         speeds=None, drift=None) -> None:
+         speeds=None, drift=None, repair: bool = False) -> None:
     """mb_plan: enqueue the plan of one MoE layer call on `stream`; with
     ``speeds`` (P host ints), mb_plan_weighted; with ``drift`` =
-    (DriftParams, state tensor), mb_plan_drift."""
+    (DriftParams, state tensor), mb_plan_drift; with ``repair``, mb_plan_ex
+    (any of the three options)."""
     assert ids.dtype == torch.int32 and ids.is_contiguous()
+    if repair:
+        sp = None if speeds is None else (ctypes.c_int32 * len(speeds))(*[int(v) for v in speeds])
+        opt = _PlanOptionsC(ctypes.cast(sp, _i32p) if sp is not None else None,
+                            ctypes.pointer(drift[0]) if drift else None,
+                            _ptr(drift[1]) if drift else None, 1)
+        rc = _lib.mb_plan_ex(ctypes.byref(dims), _ptr(ids), ctypes.byref(opt), _ptr(ws),
+                             ws.numel(), ctypes.byref(bufs.c_struct()), _stream(stream))
+        if rc != OK:
+            raise MoebalError("mb_plan_ex", rc)
+        return
     if drift is not None:
         prm, state = drift
         sp = None if speeds is None else (ctypes.c_int32 * len(speeds))(*[int(v) for v in speeds])

@@ -109,7 +109,7 @@ size_t mb_plan_workspace_bytes(const mb_dims* dims) {
 }
 
 static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
-                     const mb_drift_params* drift, void* drift_state, void* ws_dev,
+                     const mb_drift_params* drift, void* drift_state, int repair, void* ws_dev,
                      size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream) {
   int rc = validate(dims);
   if (rc != MB_OK) return rc;
@@ -137,8 +137,8 @@ static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t*
     return MB_ERR_HIP;
   if (launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_plan(*dims, g, *out, rank_speed, drift, drift_state, blockflags, expert_total,
-                  host_range, stream) != hipSuccess)
+  if (launch_plan(*dims, g, *out, rank_speed, drift, drift_state, repair, blockflags,
+                  expert_total, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
@@ -155,14 +155,15 @@ int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws
   // (ISER-MoE, HALO-Q Objective 1).
   int32_t ones[kMaxRanks];
   for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
-  return plan_impl(dims, ids_dev, ones, nullptr, nullptr, ws_dev, ws_bytes, out, stream);
+  return plan_impl(dims, ids_dev, ones, nullptr, nullptr, 0, ws_dev, ws_bytes, out, stream);
 }
 
 int mb_plan_weighted(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
                      void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out,
                      hipStream_t stream) {
   if (!rank_speed) return MB_ERR_INVALID_ARG;
-  return plan_impl(dims, ids_dev, rank_speed, nullptr, nullptr, ws_dev, ws_bytes, out, stream);
+  return plan_impl(dims, ids_dev, rank_speed, nullptr, nullptr, 0, ws_dev, ws_bytes, out,
+                   stream);
 }
 
 size_t mb_drift_state_bytes(const mb_dims* dims) {
@@ -170,17 +171,29 @@ size_t mb_drift_state_bytes(const mb_dims* dims) {
   return drift_state_bytes(*dims);
 }
 
+int mb_plan_ex(const mb_dims* dims, const int32_t* ids_dev, const mb_plan_options* opt,
+               void* ws_dev, size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream) {
+  if (!opt) return MB_ERR_INVALID_ARG;
+  const mb_drift_params* prm = opt->drift;
+  if ((prm != nullptr) != (opt->drift_state != nullptr)) return MB_ERR_INVALID_ARG;
+  if (prm) {
+    if (!aligned16(opt->drift_state)) return MB_ERR_INVALID_ARG;
+    if (prm->delta_den < 1 || prm->delta_num < 0 || prm->delta_num > prm->delta_den ||
+        prm->window < 1 || prm->window > MB_MAX_WINDOW || prm->check_every < 1)
+      return MB_ERR_INVALID_ARG;
+  }
+  int32_t ones[kMaxRanks];
+  for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
+  return plan_impl(dims, ids_dev, opt->rank_speed ? opt->rank_speed : ones, prm,
+                   opt->drift_state, opt->quota_repair != 0, ws_dev, ws_bytes, out, stream);
+}
+
 int mb_plan_drift(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
                   const mb_drift_params* params, void* state_dev, void* ws_dev,
                   size_t ws_bytes, const mb_plan_bufs* out, hipStream_t stream) {
-  if (!params || !state_dev || !aligned16(state_dev)) return MB_ERR_INVALID_ARG;
-  if (params->delta_den < 1 || params->delta_num < 0 || params->delta_num > params->delta_den ||
-      params->window < 1 || params->window > MB_MAX_WINDOW || params->check_every < 1)
-    return MB_ERR_INVALID_ARG;
-  int32_t ones[kMaxRanks];
-  for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
-  return plan_impl(dims, ids_dev, rank_speed ? rank_speed : ones, params, state_dev, ws_dev,
-                   ws_bytes, out, stream);
+  if (!params || !state_dev) return MB_ERR_INVALID_ARG;
+  const mb_plan_options opt = {rank_speed, params, state_dev, 0};
+  return mb_plan_ex(dims, ids_dev, &opt, ws_dev, ws_bytes, out, stream);
 }
 
 int mb_dispatch(const mb_dims* dims, const mb_plan_bufs* plan, const void* x_dev,

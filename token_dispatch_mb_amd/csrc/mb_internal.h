@@ -71,10 +71,11 @@ hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* block
                        int32_t* blockoff, int32_t* counts, int32_t* expert_total,
                        hipStream_t st);
 // rank_speed: P host values (all 1 for the single water level);
-// drift/drift_state: drift-gated replanning, or both nullptr.
+// drift/drift_state: drift-gated replanning, or both nullptr; repair: the
+// quota repair after placement.
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
-                       void* drift_state, const int32_t* blockflags,
+                       void* drift_state, int repair, const int32_t* blockflags,
                        const int32_t* expert_total, int2* host_range, hipStream_t st);
 
 // Bytes of a drift state buffer: header, int64 reference [E], kept replicas

@@ -37,6 +37,8 @@ struct PlanArgs {
   // drift-gated replanning: state buffer (nullptr: run the greedy every call)
   uint8_t* drift_state;
   int delta_num, delta_den, window, check_every;
+  int repair;                 // quota repair after placement
+  const int32_t* counts;      // [P][E] pairs per (source rank, expert), from k_scan
   const int32_t* expert_total;
   const int32_t* blockflags;
   int32_t* load_pre;
@@ -54,12 +56,18 @@ typedef unsigned __int128 u128;
 
 struct PlanSmem {
   u128* red;        // [64*3] per-lane partial sums of the drift check
+  uint64_t* hold;   // [E] ranks holding a replica of expert e
   double* dmisc;    // [2] distance of this call's check
   int32_t* c;       // [E] routed pairs per expert
   int32_t* qh;      // [E] remaining home quota
   int32_t* repE;    // [P*R] expert of replica slot, -1 empty
   int32_t* repM;    // [P*R] quota of replica slot
   int32_t* order;   // [P*R] replica slots in placement order
+  int32_t* dRep;    // [P*R] own pairs of the slot's rank for its expert (repair)
+  int32_t* dHome;   // [P*R] own pairs of the slot expert's home rank (repair)
+  int32_t* homeOf;  // [P*R] home rank of the slot's expert (repair)
+  int32_t* xab;     // [P*R] this round's flows of each slot's entry (repair)
+  int32_t* xba;
   int32_t* loadv;   // [64] load after planning
   int32_t* lpre;    // [64] load before planning
   int32_t* tau;     // [64] target of each rank
@@ -68,15 +76,16 @@ struct PlanSmem {
 };
 
 __host__ __device__ inline size_t plan_smem_bytes(int E, int P, int R, int NS) {
-  return sizeof(u128) * 64 * 3 + 2 * sizeof(double) +
-         sizeof(int32_t) * (2 * (size_t)E + 3 * (size_t)P * R + 64 + 64 + 64 + 8);
+  return sizeof(u128) * 64 * 3 + sizeof(uint64_t) * (size_t)E + 2 * sizeof(double) +
+         sizeof(int32_t) * (2 * (size_t)E + 8 * (size_t)P * R + 64 + 64 + 64 + 8);
 }
 
 __device__ inline PlanSmem carve(uint8_t* base, int E, int P, int R, int NS) {
   PlanSmem m;
   m.red = reinterpret_cast<u128*>(base);
-  m.dmisc = reinterpret_cast<double*>(base + sizeof(u128) * 64 * 3);
-  int32_t* p = reinterpret_cast<int32_t*>(base + sizeof(u128) * 64 * 3 + 2 * sizeof(double));
+  m.hold = reinterpret_cast<uint64_t*>(base + sizeof(u128) * 64 * 3);
+  m.dmisc = reinterpret_cast<double*>(m.hold + E);
+  int32_t* p = reinterpret_cast<int32_t*>(m.dmisc + 2);
   m.c = p;
   p += E;
   m.qh = p;
@@ -86,6 +95,16 @@ __device__ inline PlanSmem carve(uint8_t* base, int E, int P, int R, int NS) {
   m.repM = p;
   p += P * R;
   m.order = p;
+  p += P * R;
+  m.dRep = p;
+  p += P * R;
+  m.dHome = p;
+  p += P * R;
+  m.homeOf = p;
+  p += P * R;
+  m.xab = p;
+  p += P * R;
+  m.xba = p;
   p += P * R;
   m.loadv = p;
   p += 64;
@@ -360,7 +379,8 @@ __device__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
   // range checks; they only keep a foreign buffer inside the arrays)
   const int n_moves = min(max(v.hdr->n_moves, 0), P * R);
   for (int i = lane; i < P * R; i += 64) {
-    m.repE[i] = v.rep[i];
+    const int e = v.rep[i];
+    m.repE[i] = (unsigned)e < (unsigned)a.E ? e : -1;
     m.order[i] = v.order[i];
   }
   const bool rank_lane = lane < P;
@@ -415,6 +435,232 @@ __device__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
   if (lane == 0) {
     m.misc[0] = n_moves;
     m.misc[1] = unbalanced;
+  }
+}
+
+// Wave 0, after the placement: ISER-MoE HALO-Q stage 4, quota repair. A
+// circle-method tournament (n = P rounded up to even players, n - 1 rounds;
+// player 0 stays at position 0, the others rotate one position per round;
+// positions k and n-1-k meet) pairs ranks disjointly. For a pair a < b and
+// each expert both hold, taken in ascending replica-slot order (a's slots
+// whose expert b also holds, then b's slots whose expert is homed on a),
+// x_ab = min((d_a - Q_a)^+, (Q_b - d_b)^+) of a's own pairs could come back to
+// a, and x_ba likewise; m = min(sum x_ab, sum x_ba) units of quota move
+// b -> a over the x_ab experts and a -> b over the x_ba experts, each expert
+// taking min(x, what is left of m) in that order. Loads and expert totals do
+// not change. Each replica slot is an entry handled by one lane: in every
+// round it finds its holder's partner, whether its expert is one the pair
+// holds in common, and its two quota cells; the entries of a pair read each
+// other's x from LDS for the pair's totals and running sums. Different
+// entries have different cells, so the entries of a round act at once.
+__device__ void quota_repair(const PlanArgs& a, PlanSmem& m) {
+  const int lane = threadIdx.x;
+  const int P = a.P, R = a.R, Eh = a.Eh, E = a.E, PR = P * R;
+  // Per slot: home of its expert, own demands of its holder and of that
+  // home; per expert: the ranks holding a replica.
+  for (int e = lane; e < E; e += 64) m.hold[e] = 0;
+  wave_lds_sync();
+  for (int i = lane; i < PR; i += 64) {
+    const int e = m.repE[i];
+    const int h = e >= 0 ? e / Eh : -1;
+    m.homeOf[i] = h;
+    m.dRep[i] = e >= 0 ? a.counts[(size_t)(i / R) * E + e] : 0;
+    m.dHome[i] = e >= 0 ? a.counts[(size_t)h * E + e] : 0;
+    if (e >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&m.hold[e]), 1ull << (i / R));
+  }
+  wave_lds_sync();
+  // A quota cell c >= 0 is home quota qh[c]; c < 0 is replica quota
+  // repM[-1 - c]. (Indices, not pointers, keep the accesses in LDS.)
+  auto qget = [&](int c) { return c >= 0 ? m.qh[c] : m.repM[-1 - c]; };
+  auto qadd = [&](int c, int v) {
+    if (c >= 0)
+      m.qh[c] += v;
+    else
+      m.repM[-1 - c] += v;
+  };
+  // Quotas change only where a pair cancels flows in both directions: if no
+  // pair of ranks has a flow each way on the experts it shares under the
+  // placement's quotas, no round changes anything. fwd[a] / back[a] mark the
+  // ranks b > a with which rank a has a flow a -> b / b -> a.
+  {
+    uint64_t* fwd = reinterpret_cast<uint64_t*>(m.red);  // the drift sums are done
+    uint64_t* back = fwd + 64;
+    fwd[lane] = back[lane] = 0;
+    wave_lds_sync();
+    auto mark = [&](int ra, int rb, int xab, int xba) {
+      if (xab > 0) atomicOr(reinterpret_cast<unsigned long long*>(&fwd[ra]), 1ull << rb);
+      if (xba > 0) atomicOr(reinterpret_cast<unsigned long long*>(&back[ra]), 1ull << rb);
+    };
+    for (int i = lane; i < PR; i += 64) {
+      const int e = m.repE[i];
+      if (e < 0) continue;
+      const int r = i / R, h = m.homeOf[i];
+      const int Qr = m.repM[i], Qh = m.qh[e], dr = m.dRep[i], dh = m.dHome[i];
+      const int xr = min(max(dr - Qr, 0), max(Qh - dh, 0));  // holder's pairs home could take
+      const int xh = min(max(dh - Qh, 0), max(Qr - dr, 0));  // home's pairs the holder could take
+      if (r < h)
+        mark(r, h, xr, xh);
+      else
+        mark(h, r, xh, xr);
+      // pairs of holders of the same expert (r below the other holder)
+      for (uint64_t o = m.hold[e] & ~((2ull << r) - 1); o; o &= o - 1) {
+        const int q = __builtin_ctzll(o);
+        for (int j = 0; j < R; ++j)
+          if (m.repE[q * R + j] == e) {
+            const int Qq = m.repM[q * R + j], dq = m.dRep[q * R + j];
+            mark(r, q, min(max(dr - Qr, 0), max(Qq - dq, 0)),
+                 min(max(dq - Qq, 0), max(Qr - dr, 0)));
+          }
+      }
+    }
+    wave_lds_sync();
+    if (ballot64((fwd[lane] & back[lane]) != 0) == 0) return;
+  }
+  const int n = P + (P & 1);
+  // Entry of slot i in a round: cells of ranks a < b, their own demands, the pair.
+  auto entry = [&](int i, int round, int& ca, int& cb, int& da, int& db, int& lo,
+                   int& hi) -> bool {
+    const int e = m.repE[i];
+    if (e < 0) return false;
+    const int r = i / R, h = m.homeOf[i];
+    // position of r this round, then the player at the opposite position
+    int pos = 0;
+    if (r > 0) {
+      pos = r - 1 - round;
+      pos += pos < 0 ? n - 1 : 0;
+      pos += 1;
+    }
+    const int ppos = n - 1 - pos;
+    int q = 0;
+    if (ppos > 0) {
+      q = ppos - 1 + round;
+      q -= q >= n - 1 ? n - 1 : 0;
+      q += 1;
+    }
+    if (q >= P) return false;  // bye
+    if (h == q) {              // the partner is e's home
+      if (r < q) {
+        ca = -1 - i, cb = e, da = m.dRep[i], db = m.dHome[i], lo = r, hi = q;
+      } else {
+        ca = e, cb = -1 - i, da = m.dHome[i], db = m.dRep[i], lo = q, hi = r;
+      }
+      return true;
+    }
+    if (r < q && ((m.hold[e] >> q) & 1))  // the partner holds e in a slot
+      for (int j = 0; j < R; ++j)
+        if (m.repE[q * R + j] == e) {
+          ca = -1 - i, cb = -1 - (q * R + j), da = m.dRep[i], db = m.dRep[q * R + j];
+          lo = r, hi = q;
+          return true;
+        }
+    return false;
+  };
+  if (PR <= 64) {
+    // One slot per lane: everything but the quotas stays in registers.
+    const int i = lane;
+    const int e = i < PR ? m.repE[i] : -1;
+    const int r = i < PR ? i / R : 0, h = i < PR ? m.homeOf[i] : -1;
+    const int dr = i < PR ? m.dRep[i] : 0, dh = i < PR ? m.dHome[i] : 0;
+    const uint64_t hold = e >= 0 ? m.hold[e] : 0;
+    for (int round = 0; round + 1 < n; ++round) {
+      int ca = 0, cb = 0, da = 0, db = 0, lo = 0, hi = 0;
+      bool on = false;
+      if (e >= 0) {
+        int pos = 0;
+        if (r > 0) {
+          pos = r - 1 - round;
+          pos += pos < 0 ? n - 1 : 0;
+          pos += 1;
+        }
+        const int ppos = n - 1 - pos;
+        int q = 0;
+        if (ppos > 0) {
+          q = ppos - 1 + round;
+          q -= q >= n - 1 ? n - 1 : 0;
+          q += 1;
+        }
+        if (q < P && h == q) {
+          on = true;
+          if (r < q) {
+            ca = -1 - i, cb = e, da = dr, db = dh, lo = r, hi = q;
+          } else {
+            ca = e, cb = -1 - i, da = dh, db = dr, lo = q, hi = r;
+          }
+        } else if (q < P && r < q && ((hold >> q) & 1)) {
+          for (int j = 0; j < R; ++j)
+            if (m.repE[q * R + j] == e) {
+              on = true;
+              ca = -1 - i, cb = -1 - (q * R + j), da = dr, db = m.dRep[q * R + j];
+              lo = r, hi = q;
+            }
+        }
+      }
+      if (ballot64(on) == 0) continue;  // no pair of this round holds an expert in common
+      int xab = 0, xba = 0;
+      if (on) {
+        const int Qa = qget(ca), Qb = qget(cb);
+        xab = min(max(da - Qa, 0), max(Qb - db, 0));
+        xba = min(max(db - Qb, 0), max(Qa - da, 0));
+      }
+      if (i < PR) {
+        m.xab[i] = xab;
+        m.xba[i] = xba;
+      }
+      if (ballot64(xab != 0 || xba != 0) == 0) continue;  // no flow to cancel
+      wave_lds_sync();
+      if (xab != 0 || xba != 0) {
+        int fab = 0, fba = 0, pab = 0, pba = 0;  // pair totals; sums before this slot
+        for (int s2 = 0; s2 < 2 * R; ++s2) {
+          const int j = s2 < R ? lo * R + s2 : hi * R + (s2 - R);
+          const int x1 = m.xab[j], x2 = m.xba[j];
+          fab += x1;
+          fba += x2;
+          pab += j < i ? x1 : 0;
+          pba += j < i ? x2 : 0;
+        }
+        const int mm = min(fab, fba);
+        const int t = min(xab, max(mm - pab, 0)) - min(xba, max(mm - pba, 0));
+        qadd(ca, t);
+        qadd(cb, -t);
+      }
+      wave_lds_sync();
+    }
+    return;
+  }
+  for (int round = 0; round + 1 < n; ++round) {
+    int any = 0;
+    for (int i = lane; i < PR; i += 64) {
+      int ca, cb, da, db, lo, hi, xab = 0, xba = 0;
+      if (entry(i, round, ca, cb, da, db, lo, hi)) {
+        const int Qa = qget(ca), Qb = qget(cb);
+        xab = min(max(da - Qa, 0), max(Qb - db, 0));
+        xba = min(max(db - Qb, 0), max(Qa - da, 0));
+        any |= (xab | xba) != 0;
+      }
+      m.xab[i] = xab;
+      m.xba[i] = xba;
+    }
+    if (ballot64(any) == 0) continue;  // no flow to cancel this round
+    wave_lds_sync();
+    for (int i = lane; i < PR; i += 64) {
+      const int xab = m.xab[i], xba = m.xba[i];
+      int ca, cb, da, db, lo, hi;
+      if ((xab == 0 && xba == 0) || !entry(i, round, ca, cb, da, db, lo, hi)) continue;
+      int fab = 0, fba = 0, pab = 0, pba = 0;  // pair totals; sums before this slot
+      for (int s2 = 0; s2 < 2 * R; ++s2) {
+        const int j = s2 < R ? lo * R + s2 : hi * R + (s2 - R);
+        const int x1 = m.xab[j], x2 = m.xba[j];
+        fab += x1;
+        fba += x2;
+        pab += j < i ? x1 : 0;
+        pba += j < i ? x2 : 0;
+      }
+      const int mm = min(fab, fba);
+      const int t = min(xab, max(mm - pab, 0)) - min(xba, max(mm - pba, 0));
+      qadd(ca, t);
+      qadd(cb, -t);
+    }
+    wave_lds_sync();
   }
 }
 
@@ -507,6 +753,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       greedy_regs<32>(a, m);
     else
       greedy_lds(a, m);
+    if (a.repair && R > 0) quota_repair(a, m);
   }
   __syncthreads();
   if (drift) {
@@ -574,7 +821,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
 
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
-                       void* drift_state, const int32_t* blockflags,
+                       void* drift_state, int repair, const int32_t* blockflags,
                        const int32_t* expert_total, int2* host_range, hipStream_t st) {
   PlanArgs a;
   a.N = d.n_tokens;
@@ -592,6 +839,8 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.delta_den = drift ? drift->delta_den : 1;
   a.window = drift ? drift->window : 1;
   a.check_every = drift ? drift->check_every : 1;
+  a.repair = repair;
+  a.counts = o.counts;
   a.expert_total = expert_total;
   a.blockflags = blockflags;
   a.load_pre = o.load_pre;
