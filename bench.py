@@ -45,17 +45,19 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl) -> dict:
+def algorithmic_bytes(wl, combine_fp8: bool = False) -> dict:
     """Bytes the method itself must move per layer call (no padding, no
     staging): dispatch reads each row once and writes it K times, reading
-    pos; combine reads K expert rows, pos and w per token and writes one row."""
+    pos; combine reads K expert rows, pos and w per token and writes one row
+    (with combine_fp8 the expert rows are fp8 plus a 4-byte scale per 128)."""
     N, K, H = wl.n_tokens, wl.top_k, wl.hidden
     b_in = {"f32": 4, "bf16": 2, "fp8": 1}[wl.dtype_in]
     b_out = {"f32": 4, "bf16": 2}[wl.dtype_out]
     row_in = H * b_in + (H // 128 * 4 if wl.dtype_in == "fp8" else 0)
     row_out = H * b_out
+    row_exp = H + H // 128 * 4 if combine_fp8 else row_out
     dispatch = N * row_in + N * K * row_in + N * K * 4
-    combine = N * K * row_out + N * K * 8 + N * row_out
+    combine = N * K * row_exp + N * K * 8 + N * row_out
     return {"dispatch": dispatch, "combine": combine, "row_in": row_in, "row_out": row_out}
 
 
@@ -200,6 +202,9 @@ def main() -> int:
                     help="timed steps (default 20; a drift-gated workload: its call count)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--combine-fp8", action="store_true",
+                    help="fp8-row workloads: expert outputs stay fp8 with their scales and "
+                         "mb_combine_fp8 dequantises while combining")
     ap.add_argument("--repair", action="store_true",
                     help="plan with the quota repair after placement (mb_plan_ex)")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
@@ -284,9 +289,17 @@ def main() -> int:
         wir_equal = float(_speed_ratio(bufs.load_post.cpu().numpy(), speeds, wl))
 
     # Expert outputs: the dispatched rows (identity experts), or for fp8
-    # rows a generated bf16 buffer.
+    # rows a generated bf16 buffer (or, with --combine-fp8, the dispatched
+    # fp8 rows and scales themselves).
     mb.plan(dims, ids_d, ws, bufs, speeds=speeds, repair=args.repair)
-    if wl.dtype_in == wl.dtype_out:
+    if args.combine_fp8:
+        if wl.dtype_in != "fp8":
+            print("--combine-fp8 needs a workload with fp8 rows", file=sys.stderr)
+            return 2
+        y_exp8 = torch.empty((dims.rows, wl.hidden), dtype=torch.uint8, device=dev)
+        ys8 = torch.empty((dims.rows, wl.hidden // 128), dtype=torch.float32, device=dev)
+        mb.dispatch(dims, bufs, x_d, y_exp8, xs_d, ys8)
+    elif wl.dtype_in == wl.dtype_out:
         mb.dispatch(dims, bufs, x_d, y_exp, xs_d, bs)
     else:
         y_exp.copy_(torch.from_numpy(
@@ -303,7 +316,10 @@ def main() -> int:
         mb.dispatch(dims, bufs, x_d, buf, xs_d, bs)
         if ev is not None:
             ev[2].record()
-        mb.combine(dims, bufs, y_exp, w_d, y)
+        if args.combine_fp8:
+            mb.combine_fp8(dims, bufs, y_exp8, ys8, w_d, y)
+        else:
+            mb.combine(dims, bufs, y_exp, w_d, y)
         if ev is not None:
             ev[3].record()
 
@@ -327,14 +343,15 @@ def main() -> int:
     comb_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     total_ms = evs[0][0].elapsed_time(evs[-1][3])
     ms_per_step = total_ms / args.steps
-    ab = algorithmic_bytes(wl)
+    ab = algorithmic_bytes(wl, combine_fp8=args.combine_fp8)
     bytes_step = ab["dispatch"] + ab["combine"]
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
     d_gbps = ab["dispatch"] / (disp_ms.mean() * 1e-3) / 1e9
     c_gbps = ab["combine"] / (comb_ms.mean() * 1e-3) / 1e9
-    dominant = "k_combine" if comb_ms.mean() >= disp_ms.mean() else "k_dispatch"
-    dom_bytes = ab["combine"] if dominant == "k_combine" else ab["dispatch"]
-    dom_ms = comb_ms.mean() if dominant == "k_combine" else disp_ms.mean()
+    comb_name = "k_combine_fp8" if args.combine_fp8 else "k_combine"
+    dominant = comb_name if comb_ms.mean() >= disp_ms.mean() else "k_dispatch"
+    dom_bytes = ab["combine"] if dominant == comb_name else ab["dispatch"]
+    dom_ms = comb_ms.mean() if dominant == comb_name else disp_ms.mean()
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     # Correctness spot check of the timed buffers (identity experts: the
@@ -372,6 +389,7 @@ def main() -> int:
             "top_k": wl.top_k, "logical_ranks": wl.n_ranks, "replica_slots_per_rank":
                 wl.slots_per_rank, "hidden": wl.hidden, "rows_in": wl.dtype_in,
             "rows_out": wl.dtype_out, "cap": wl.cap,
+            "expert_outputs": "fp8+scales" if args.combine_fp8 else wl.dtype_out,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "dispatch_combine_gbps": round(bytes_step / ((disp_ms.mean() + comb_ms.mean()) * 1e-3) / 1e9, 2),

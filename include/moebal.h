@@ -307,6 +307,24 @@ int mb_combine(const mb_dims* dims, const mb_plan_bufs* plan, const void* y_exp_
                const float* w_dev, void* y_dev, hipStream_t stream);
 
 /*
+ * Dequantising combine for fp8 expert outputs [MoonEP fixed buffers; the
+ * fp8 payload format of the dispatch]:
+ *   y[t][i] = sum_k w[t][k] * e4m3(y_exp[p][i]) * y_scale[p][i / 128],
+ *   p = pos[t][k],
+ * accumulated in fp32 in k order as fma(w * scale, value, acc), stored as
+ * dtype_out (F32, or BF16 by round to nearest even). dtype_in is not used.
+ *  y_exp_dev    [P*cap, H] OCP fp8 e4m3fn expert outputs (the dispatch layout).
+ *  y_scale_dev  [P*cap, H/128] fp32 scales, one per 128 elements.
+ *  w_dev        [N*K] fp32 gate weights.
+ *  y_dev        [N, H] of dtype_out.
+ * Needs H % 128 == 0; y_exp and y 16-byte aligned, y_scale 4-byte aligned.
+ * Reads plan->pos and plan->status; does nothing under a fatal status.
+ */
+int mb_combine_fp8(const mb_dims* dims, const mb_plan_bufs* plan, const uint8_t* y_exp_dev,
+                   const float* y_scale_dev, const float* w_dev, void* y_dev,
+                   hipStream_t stream);
+
+/*
  * Copy status[4] to host_status (host memory) after the work enqueued on
  * `stream` so far has finished. The only call that synchronises.
  */

@@ -117,6 +117,11 @@ def lib() -> ctypes.CDLL:
         L.mbref_plan_ex.restype = ctypes.c_int
         L.mbref_circle_schedule.argtypes = [ctypes.c_int32, vp]
         L.mbref_circle_schedule.restype = None
+        L.mbref_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.mbref_e4m3_value.restype = ctypes.c_double
+        L.mbref_combine_fp8.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, ctypes.c_int32,
+                                        ctypes.c_int32, vp, vp]
+        L.mbref_combine_fp8.restype = ctypes.c_int
         L.mbref_dispatch.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, vp]
         L.mbref_dispatch.restype = ctypes.c_int
         L.mbref_dispatch_window.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp,
@@ -313,4 +318,27 @@ def combine(dims: Dims, pos: np.ndarray, status: np.ndarray, w: np.ndarray, y_ex
                              _ptr(w), _ptr(y_exp), t0, t1, _ptr(y), _ptr(mag))
     if rc < 0:
         raise ValueError(f"mbref_combine returned {rc}")
+    return y, mag, rc
+
+
+def e4m3_value(b: int) -> float:
+    return lib().mbref_e4m3_value(b)
+
+
+def combine_fp8(dims: Dims, pos: np.ndarray, status: np.ndarray, w: np.ndarray,
+                y_exp: np.ndarray, y_scale: np.ndarray, t0: int = 0, t1: int | None = None):
+    """(y, mag) in float64 for tokens [t0, t1) from fp8 e4m3 expert outputs
+    (uint8 [rows, H]) and their fp32 scales [rows, H/128]."""
+    t1 = dims.n_tokens if t1 is None else t1
+    H = dims.hidden
+    y = np.zeros((t1 - t0, H), np.float64)
+    mag = np.zeros((t1 - t0, H), np.float64)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    y_exp = np.ascontiguousarray(y_exp, dtype=np.uint8)
+    y_scale = np.ascontiguousarray(y_scale, dtype=np.float32)
+    rc = lib().mbref_combine_fp8(ctypes.byref(dims), _ptr(pos), _ptr(np.ascontiguousarray(status)),
+                                 _ptr(w), _ptr(y_exp), _ptr(y_scale), t0, t1, _ptr(y), _ptr(mag))
+    if rc < 0:
+        raise ValueError(f"mbref_combine_fp8 returned {rc}")
     return y, mag, rc

@@ -661,3 +661,43 @@ int mbref_combine(const mbref_dims* dm, const int32_t* pos,
     }
   return 0;
 }
+
+/* OCP fp8 e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinities. */
+double mbref_e4m3_value(uint8_t b) {
+  const int sign = b >> 7, ex = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (ex == 15 && m == 7)
+    v = NAN;
+  else if (ex == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, ex - 7);
+  return sign ? -v : v;
+}
+
+/* Step O6 with fp8 expert outputs (the dequantising combine):
+ * y[t][i] = sum_k w[t][k] * e4m3(y_exp[pos][i]) * y_scale[pos][i / 128] in
+ * double for tokens [t0, t1); mag receives sum_k |term|. */
+int mbref_combine_fp8(const mbref_dims* dm, const int32_t* pos, const int32_t* status,
+                      const float* w, const uint8_t* y_exp, const float* y_scale, int32_t t0,
+                      int32_t t1, double* y, double* mag) {
+  if (!dm || !valid_dims(dm) || dm->hidden % 128 || t0 < 0 || t1 < t0 || t1 > dm->n_tokens)
+    return MBREF_ERR_INVALID_ARG;
+  if (status[0] & MBREF_ST_FATAL) return 1;
+  const int64_t K = dm->top_k, H = dm->hidden;
+  for (int64_t t = t0; t < t1; ++t)
+    for (int64_t i = 0; i < H; ++i) {
+      double acc = 0.0, a = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t p = pos[t * K + k];
+        const double v = mbref_e4m3_value(y_exp[p * H + i]) * (double)y_scale[p * (H / 128) + i / 128];
+        const double term = (double)w[t * K + k] * v;
+        acc += term;
+        a += fabs(term);
+      }
+      y[(t - t0) * H + i] = acc;
+      if (mag) mag[(t - t0) * H + i] = a;
+    }
+  return 0;
+}

@@ -187,6 +187,16 @@ int mbref_combine(const mbref_dims* dims, const int32_t* pos,
                   const int32_t* status, const float* w, const void* y_exp,
                   int32_t t0, int32_t t1, double* y, double* mag);
 
+/* The value of one OCP fp8 e4m3fn byte (NaN for S.1111.111). */
+double mbref_e4m3_value(uint8_t b);
+
+/* Step O6 for fp8 expert outputs with fp32 scales per 128 elements:
+ * y[t][i] = sum_k w[t][k] * e4m3(y_exp[pos][i]) * y_scale[pos][i/128] in
+ * double; hidden % 128 == 0. Returns 1 if status is fatal, 0 otherwise. */
+int mbref_combine_fp8(const mbref_dims* dims, const int32_t* pos, const int32_t* status,
+                      const float* w, const uint8_t* y_exp, const float* y_scale, int32_t t0,
+                      int32_t t1, double* y, double* mag);
+
 #ifdef __cplusplus
 }
 #endif

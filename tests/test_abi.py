@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     text = open(os.path.join(ROOT, "include", "moebal.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mb_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mb_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -119,3 +119,20 @@ def test_weighted_plan_speed_checks():
     rc = mb.raw_call("mb_plan_weighted", ctypes.byref(d), fake, I4(3, 1, mb.MAX_SPEED, 2), fake,
                      need - 1, ctypes.byref(bufs), None)
     assert rc == mb.ERR_WORKSPACE
+
+
+def test_combine_fp8_host_checks():
+    """mb_combine_fp8 needs H % 128 == 0, scales, and aligned rows."""
+    fake = ctypes.c_void_p(1 << 20)
+    bufs = mb._PlanBufsC(*([1 << 20] * 9))
+    d = mb.Dims.make(64, 2, 16, 4, 1, 64, dtype_in="fp8", dtype_out="bf16")
+    rc = mb.raw_call("mb_combine_fp8", ctypes.byref(d), ctypes.byref(bufs), fake, fake, fake, fake,
+                     None)
+    assert rc == mb.ERR_INVALID_ARG  # H = 64
+    d = mb.Dims.make(64, 2, 16, 4, 1, 128, dtype_in="fp8", dtype_out="bf16")
+    rc = mb.raw_call("mb_combine_fp8", ctypes.byref(d), ctypes.byref(bufs), fake, None, fake, fake,
+                     None)
+    assert rc == mb.ERR_INVALID_ARG  # no scales
+    rc = mb.raw_call("mb_combine_fp8", ctypes.byref(d), ctypes.byref(bufs), fake,
+                     ctypes.c_void_p((1 << 20) + 2), fake, fake, None)
+    assert rc == mb.ERR_INVALID_ARG  # misaligned scales

@@ -637,3 +637,86 @@ def test_repair_with_speeds_and_drift():
         ref = O.plan(od, ids, speeds=speeds, drift=(oprm, st), repair=True)
         G.assert_plan_equal(got, ref)
         _assert_state_equal(state, st, E, f"call {call}")
+
+
+# ---- dequantising fp8 combine ------------------------------------------------------
+
+def _combine_fp8_case(N, K, E, P, R, H, dout, seed, label):
+    ids, w = W.routing(N, E, K, W.NOISE_GUMBEL, 1.1, 1.0, seed)
+    cap = 2 * (N // P) * K
+    dg = mb.Dims.make(N, K, E, P, R, H, cap=cap, dtype_in="fp8", dtype_out=dout)
+    od = O.make_dims(N, K, E, P, R, H, cap=cap, dtype_in="fp8", dtype_out=dout)
+    G.log(f"combine_fp8 {label}: N={N} K={K} H={H} out={dout}")
+    gp = G.GpuPlan(dg).run(ids)
+    ref = O.plan(od, ids)
+    rows = P * cap
+    q, sc, _ = W.rows_fp8(seed, W.TAG_YEXP, H, n=rows)
+    d = G.dev()
+    q_d = torch.from_numpy(q).to(d)
+    sc_d = torch.from_numpy(sc).to(d)
+    w_d = torch.from_numpy(w).to(d)
+    odt = torch.bfloat16 if dout == "bf16" else torch.float32
+    y = torch.full((N, H), float("nan"), dtype=odt, device=d)
+    mb.combine_fp8(dg, gp.bufs, q_d, sc_d, w_d, y)
+    torch.cuda.synchronize()
+    y_ref, mag, rc = O.combine_fp8(od, ref.pos, ref.status, w, q, sc)
+    if ref.status[0] & O.ST_FATAL:
+        assert torch.isnan(y.float()).all()
+        return
+    G.assert_combine_close(G.y_to_f64(y), y_ref, mag, dout)
+
+
+@pytest.mark.parametrize("H", [128, 384, 1024, 1152, 7168, 16384, 17408])
+@pytest.mark.parametrize("K", [1, 3, 8])
+def test_combine_fp8_shapes(H, K):
+    """Whole-KiB rows up to 16 KiB take the straight-line path, others the
+    checked loop; K = 3 takes the runtime-K kernel."""
+    for dout in ("bf16", "f32"):
+        _combine_fp8_case(512, K, 32, 8, 1, H, dout, 4000 + H + K, f"H{H} K{K}")
+
+
+def test_combine_fp8_decode_round_trip():
+    """The decode workload's fp8 dispatch buffer (rows and scales) combined
+    by mb_combine_fp8 against the oracle, and with one-hot weights the
+    exact dequantisation of each token's row (bf16 of the fp32 q * scale)."""
+    wl = W.get_workload("decode_drift")
+    ids, w = W.routing_for(wl, 3)
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    x, xs = W.token_rows(wl, 3)
+    d = G.dev()
+    gp = G.GpuPlan(dg).run(ids)
+    ref = O.plan(od, ids)
+    buf = torch.zeros((dg.rows, wl.hidden), dtype=torch.uint8, device=d)
+    bs = torch.zeros((dg.rows, wl.hidden // 128), dtype=torch.float32, device=d)
+    x_d, xs_d = torch.from_numpy(x).to(d), torch.from_numpy(xs).to(d)
+    mb.dispatch(dg, gp.bufs, x_d, buf, xs_d, bs)
+    y = torch.empty((wl.n_tokens, wl.hidden), dtype=torch.bfloat16, device=d)
+    mb.combine_fp8(dg, gp.bufs, buf, bs, torch.from_numpy(w).to(d), y)
+    torch.cuda.synchronize()
+    t0, t1 = 0, 256
+    ref_buf, ref_bs, _ = O.dispatch(od, ref, x, xs)
+    y_ref, mag, _ = O.combine_fp8(od, ref.pos, ref.status, w, ref_buf, ref_bs, t0, t1)
+    G.assert_combine_close(G.y_to_f64(y[t0:t1]), y_ref, mag, "bf16")
+    onehot = np.zeros_like(w)
+    onehot[:, 0] = 1.0
+    mb.combine_fp8(dg, gp.bufs, buf, bs, torch.from_numpy(onehot).to(d), y)
+    deq = torch.from_numpy(x).view(torch.float8_e4m3fn).float() * \
+        torch.from_numpy(xs).repeat_interleave(128, dim=1)
+    # equal values (a -0 code comes back as +0: the accumulator starts at +0)
+    assert torch.equal(y.cpu().float(), deq.to(torch.bfloat16).float())
+
+
+def test_combine_fp8_fatal_status_writes_nothing():
+    N, K, E, P = 64, 2, 8, 4
+    ids = np.zeros((N, K), np.int32)
+    ids[:, 1] = 1
+    ids[5, 1] = 0  # duplicate id: fatal
+    dg = mb.Dims.make(N, K, E, P, 1, 128, dtype_in="fp8", dtype_out="bf16")
+    gp = G.GpuPlan(dg).run(ids)
+    d = G.dev()
+    q = torch.zeros((dg.rows, 128), dtype=torch.uint8, device=d)
+    sc = torch.ones((dg.rows, 1), dtype=torch.float32, device=d)
+    y = torch.full((N, 128), float("nan"), dtype=torch.bfloat16, device=d)
+    mb.combine_fp8(dg, gp.bufs, q, sc, torch.ones((N, K), device=d), y)
+    torch.cuda.synchronize()
+    assert torch.isnan(y.float()).all()

@@ -85,6 +85,10 @@ MUTANTS = [
      "if (e >= 0 && e / Eh == a) common[nc++] = e;", "if (0) common[nc++] = e;"),
     ("repair skips pairs with the last rank",
      "if (a >= P || b >= P) continue; /* bye */", "if (a >= P - 1 || b >= P - 1) continue;"),
+    ("fp8 combine scale of the wrong block",
+     "(double)y_scale[p * (H / 128) + i / 128];", "(double)y_scale[p * (H / 128) + i / 256];"),
+    ("fp8 decode without the subnormal range",
+     "    v = ldexp((double)m, -9);", "    v = ldexp(1.0 + m / 8.0, -7);"),
     ("duplicate ids not flagged",
      "if (ids[t * K + k2] == e) flags |= MBREF_ST_DUP_ID;", "if (0) flags |= MBREF_ST_DUP_ID;"),
 ]

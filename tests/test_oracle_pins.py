@@ -939,6 +939,58 @@ def test_combine_round_trip_identity_experts():
     assert np.all(np.abs(wsum - 1) < 1e-6)
 
 
+def test_e4m3_decode_matches_torch():
+    """The oracle's OCP e4m3fn decode equals torch's float8_e4m3fn on all 256
+    codes (subnormals, the largest value 448, NaN)."""
+    import torch
+
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mine = np.array([O.e4m3_value(b) for b in range(256)])
+    assert np.array_equal(mine, ref, equal_nan=True)
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_combine_fp8_matches_numpy():
+    """The dequantising combine equals numpy in float64: torch's e4m3 decode
+    times the row's scale of each 128-element block, weighted and summed."""
+    import torch
+
+    wl = W.get_workload("decode_drift")
+    P, K, E, H = 8, 3, 16, 384
+    N, cap = 64, 64
+    ids, w = W.routing(N, E, K, W.NOISE_GUMBEL, 1.1, 1.0, 321)
+    d = O.make_dims(N, K, E, P, 1, H, cap=cap, dtype_in="fp8", dtype_out="bf16")
+    p = O.plan(d, ids)
+    assert p.flags == 0
+    rows = P * cap
+    q, sc, _ = W.rows_fp8(wl.seed, W.TAG_YEXP, H, n=rows)
+    y, mag, rc = O.combine_fp8(d, p.pos, p.status, w, q, sc)
+    deq = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    deq = deq * np.repeat(sc.astype(np.float64), 128, axis=1)
+    terms = w.astype(np.float64)[:, :, None] * deq[p.pos]
+    assert rc == 0
+    assert np.allclose(y, terms.sum(1), rtol=1e-13, atol=1e-12)
+    assert np.allclose(mag, np.abs(terms).sum(1), rtol=1e-13, atol=1e-12)
+
+
+def test_combine_fp8_round_trip():
+    """fp8 rows dispatched with their scales and combined with one-hot
+    weights come back as their exact dequantisation q * scale."""
+    wl = W.get_workload("decode_drift")
+    ids, w = W.routing_for(wl, 5)
+    d = O.dims_for(wl)
+    d.hidden = 256
+    x, xs, _ = W.rows_fp8(wl.seed, W.TAG_X, 256, n=wl.n_tokens)
+    p = O.plan(d, ids)
+    buf, bs, _ = O.dispatch(d, p, x, xs)
+    onehot = np.zeros_like(w)
+    onehot[:, 2] = 1.0
+    y, _, _ = O.combine_fp8(d, p.pos, p.status, onehot, buf, bs, 0, 512)
+    exp = np.array([[O.e4m3_value(b) for b in row] for row in x[:512, :]]) * \
+        np.repeat(xs[:512].astype(np.float64), 128, axis=1)
+    assert np.array_equal(y, exp)
+
+
 def test_fatal_status_skips_dispatch_and_combine():
     wl, ids, w, d, p = _plan_workload("tiny")
     x, _ = W.token_rows(wl)

@@ -118,12 +118,15 @@ _lib.mb_dispatch.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_PlanBufsC), _
 _lib.mb_dispatch.restype = ctypes.c_int
 _lib.mb_combine.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_PlanBufsC), _vp, _vp, _vp, _vp]
 _lib.mb_combine.restype = ctypes.c_int
+_lib.mb_combine_fp8.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_PlanBufsC), _vp, _vp, _vp,
+                                _vp, _vp]
+_lib.mb_combine_fp8.restype = ctypes.c_int
 _lib.mb_plan_status.argtypes = [ctypes.POINTER(_PlanBufsC), _vp, _i32p]
 _lib.mb_plan_status.restype = ctypes.c_int
 
 EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan",
            "mb_plan_weighted", "mb_drift_state_bytes", "mb_plan_drift", "mb_plan_ex",
-           "mb_dispatch", "mb_combine", "mb_plan_status")
+           "mb_dispatch", "mb_combine", "mb_combine_fp8", "mb_plan_status")
 ST_REPLANNED = 16
 MAX_WINDOW = 4096
 MAX_SPEED = 1 << 20
@@ -270,6 +273,19 @@ def drift_header(state: torch.Tensor) -> dict:
     return {"have_plan": int(i32[0]), "countdown": int(i32[1]), "nwin": int(i32[2]),
             "n_moves": int(i32[3]), "calls": int(i64[0]), "replans": int(i64[1]),
             "last_d": float(np.frombuffer(b[32:40], np.float64)[0])}
+
+
+def combine_fp8(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, y_scale: torch.Tensor,
+                w: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """mb_combine_fp8: y[t] = sum_k w[t][k] * dequant(y_exp[pos[t][k]]) from
+    fp8 e4m3 rows (uint8 [rows, H]) and fp32 scales [rows, H/128]."""
+    assert y_exp.dtype == torch.uint8 and y_scale.dtype == torch.float32
+    assert y_exp.is_contiguous() and y_scale.is_contiguous() and w.is_contiguous()
+    assert y.is_contiguous() and w.dtype == torch.float32
+    rc = _lib.mb_combine_fp8(ctypes.byref(dims), ctypes.byref(bufs.c_struct()), _ptr(y_exp),
+                             _ptr(y_scale), _ptr(w), _ptr(y), _stream(stream))
+    if rc != OK:
+        raise MoebalError("mb_combine_fp8", rc)
 
 
 def plan_status(bufs: PlanBuffers, stream=None):

@@ -223,6 +223,23 @@ int mb_combine(const mb_dims* dims, const mb_plan_bufs* plan, const void* y_exp_
                                                                                      : MB_ERR_HIP;
 }
 
+int mb_combine_fp8(const mb_dims* dims, const mb_plan_bufs* plan, const uint8_t* y_exp_dev,
+                   const float* y_scale_dev, const float* w_dev, void* y_dev,
+                   hipStream_t stream) {
+  int rc = validate(dims);
+  if (rc != MB_OK) return rc;
+  if (dims->hidden % 128) return MB_ERR_INVALID_ARG;
+  if (!plan || !plan->status || !y_exp_dev || !y_scale_dev ||
+      (dims->n_tokens > 0 && (!plan->pos || !w_dev || !y_dev)))
+    return MB_ERR_INVALID_ARG;
+  if (!aligned16(y_exp_dev) || !aligned16(y_dev) || ((uintptr_t)y_scale_dev & 3u))
+    return MB_ERR_INVALID_ARG;
+  return launch_combine_fp8(*dims, *plan, y_exp_dev, y_scale_dev, w_dev, y_dev, stream) ==
+                 hipSuccess
+             ? MB_OK
+             : MB_ERR_HIP;
+}
+
 int mb_plan_status(const mb_plan_bufs* plan, hipStream_t stream, int32_t host_status[4]) {
   if (!plan || !plan->status || !host_status) return MB_ERR_INVALID_ARG;
   if (hipMemcpyAsync(host_status, plan->status, 4 * sizeof(int32_t), hipMemcpyDeviceToHost,

@@ -92,6 +92,8 @@ hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* 
                            const float* x_scale, void* buf, float* buf_scale, hipStream_t st);
 hipError_t launch_combine(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
                           const float* w, void* y, hipStream_t st);
+hipError_t launch_combine_fp8(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
+                              const float* y_scale, const float* w, void* y, hipStream_t st);
 
 // Launch KERNEL<K> for the top-K values with a specialised kernel, KERNEL<0>
 // (runtime K) otherwise.

@@ -225,6 +225,89 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
   }
 }
 
+// ---- dequantising combine: fp8 e4m3 expert outputs, fp32 scale per 128 -----
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// acc[0..15] += ws * (16 e4m3 values of v), ws = w * the chunk's scale; the
+// hardware conversion decodes OCP e4m3fn exactly (two bytes per call).
+__device__ __forceinline__ void fma_fp8(float* acc, float ws, u32x4 v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
+    acc[4 * i] = fmaf(ws, lo.x, acc[4 * i]);
+    acc[4 * i + 1] = fmaf(ws, lo.y, acc[4 * i + 1]);
+    acc[4 * i + 2] = fmaf(ws, hi.x, acc[4 * i + 2]);
+    acc[4 * i + 3] = fmaf(ws, hi.y, acc[4 * i + 3]);
+  }
+}
+
+// 16 accumulators to the output row: 2 chunks of bf16 or 4 of fp32.
+template <bool kBF16>
+__device__ __forceinline__ void store_fp8_piece(const float* acc, u32x4* __restrict__ dst) {
+  if constexpr (kBF16) {
+    __builtin_nontemporal_store(pack_row<true>(acc), dst);
+    __builtin_nontemporal_store(pack_row<true>(acc + 8), dst + 1);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(pack_row<false>(acc + 4 * j), dst + j);
+  }
+}
+
+// Dequantising combine: y[t][i] = sum_k w[t][k] * e4m3(y_exp[p][i]) *
+// scale[p][i/128], accumulated in fp32 in k order as fma(w * scale, value,
+// acc). One wave per 1 KiB part of a token's fp8 row (64 lanes x 16
+// elements, each lane's 16 under one scale: chunk c uses scale c / 8), the
+// parts of a token on consecutive waves, as in k_dispatch: with rows half
+// the bytes of bf16, small waves (16 accumulators per lane) keep more loads
+// in flight per CU than a wave holding a whole row. With a compile-time K
+// the K loads of a part are issued before the first FMA.
+template <int KT, bool kBF16>
+__global__ __launch_bounds__(kRowThreads) void k_combine_fp8(
+    const u32x4* __restrict__ ye, const float* __restrict__ ys, const int32_t* __restrict__ pos,
+    const float* __restrict__ w, const int32_t* __restrict__ status, u32x4* __restrict__ y,
+    int N, int K_, int rb16, int wpt, int rows) {
+  constexpr int OPC = kBF16 ? 2 : 4;  // output chunks per input chunk
+  const int K = KT ? KT : K_;
+  const int nsc = rb16 / 8;  // scales per row
+  const int lane = threadIdx.x & 63;
+  const int gw = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  const int t = gw / wpt, part = gw - t * wpt;
+  if (t >= N) return;
+  if (status[0] & MB_ST_FATAL) return;
+  const int ci = part * 64 + lane;  // this lane's chunk of the row
+  if (ci >= rb16) return;
+  const int32_t* pt = pos + (size_t)t * K;
+  const float* wt = w + (size_t)t * K;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  if constexpr (KT > 0) {
+    int p[KT];
+    u32x4 v[KT];
+    float s[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      p[k] = pt[k];
+      const bool ok = (unsigned)p[k] < (unsigned)rows;  // only a broken plan fails this
+      const size_t row = ok ? (size_t)p[k] : 0;
+      v[k] = __builtin_nontemporal_load(ye + row * rb16 + ci);
+      s[k] = ok ? ys[row * nsc + (ci >> 3)] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) fma_fp8(acc, wt[k] * s[k], v[k]);
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if ((unsigned)p >= (unsigned)rows) continue;
+      fma_fp8(acc, wt[k] * ys[(size_t)p * nsc + (ci >> 3)],
+              __builtin_nontemporal_load(ye + (size_t)p * rb16 + ci));
+    }
+  }
+  store_fp8_piece<kBF16>(acc, y + ((size_t)t * rb16 + ci) * OPC);
+}
+
 // Chunks per lane of one piece: the whole row when it is a multiple of
 // 1 KiB up to 16 KiB, else 16-chunk pieces with bounds checks.
 inline int pick_cpl(int rb16, bool& exact) {
@@ -277,6 +360,40 @@ static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x
   }
 #undef MB_CK
 #undef MB_C
+}
+
+template <bool kBF16>
+static void launch_combine_fp8_t(const mb_dims& d, const mb_plan_bufs& o, const u32x4* ye,
+                                 const float* ys, const float* w, u32x4* yy, int rb16, int rows,
+                                 hipStream_t st) {
+  const int wpt = (rb16 + 63) / 64;  // waves per token
+  const int64_t waves = (int64_t)d.n_tokens * wpt;
+  const dim3 grid((unsigned)((waves + kTokensPerRowBlock - 1) / kTokensPerRowBlock));
+#define MB_C(KT)                                                                             \
+  hipLaunchKernelGGL((k_combine_fp8<KT, kBF16>), grid, dim3(kRowThreads), 0, st, ye, ys, o.pos, \
+                     w, o.status, yy, d.n_tokens, d.top_k, rb16, wpt, rows)
+  switch (d.top_k) {
+    case 1: MB_C(1); break;
+    case 2: MB_C(2); break;
+    case 4: MB_C(4); break;
+    case 8: MB_C(8); break;
+    default: MB_C(0); break;
+  }
+#undef MB_C
+}
+
+hipError_t launch_combine_fp8(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
+                              const float* y_scale, const float* w, void* y, hipStream_t st) {
+  if (d.n_tokens == 0) return hipSuccess;
+  const int rb16 = d.hidden / 16;  // 16 fp8 elements per chunk
+  const int rows = d.n_ranks * d.cap;
+  const u32x4* ye = static_cast<const u32x4*>(y_exp);
+  u32x4* yy = static_cast<u32x4*>(y);
+  if (d.dtype_out == MB_BF16)
+    launch_combine_fp8_t<true>(d, o, ye, y_scale, w, yy, rb16, rows, st);
+  else
+    launch_combine_fp8_t<false>(d, o, ye, y_scale, w, yy, rb16, rows, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
