@@ -1,8 +1,8 @@
 // rows.hip — row dispatch (scatter) and combine (weighted gather-reduce).
 //
-// Both kernels are HBM-bound byte movers: one wave64 per token, every lane
-// moving 16-byte chunks (global_load/store_dwordx4) with a whole row piece
-// (up to 16 KiB per wave) in flight at once. The cache hint of each access
+// The kernels are HBM-bound byte movers: one wave64 per 1 KiB part of a
+// token's row, every lane moving 16-byte chunks (global_load/store_dwordx4),
+// a token's parts on consecutive waves. The cache hint of each access
 // (temporal or nontemporal) is the one measured fastest on MI355X for that
 // kernel's traffic mix; see the comment at each kernel.
 //
@@ -24,22 +24,9 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowThreads = 256;
-constexpr int kTokensPerRowBlock = kRowThreads / 64;
+constexpr int kWavesPerRowBlock = kRowThreads / 64;
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// A row is moved in pieces of CPL 16-byte chunks per lane (CPL * 1 KiB per
-// wave). When the row is exactly CPL * 1 KiB long the whole row sits in
-// registers and no access needs a bounds check.
-template <bool kChecked, int CPL>
-__device__ __forceinline__ void load_piece(u32x4 (&v)[CPL], const u32x4* __restrict__ src,
-                                           int c0, int rb16, bool nt) {
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int i = c0 + c * 64;
-    if (!kChecked || i < rb16) v[c] = nt ? __builtin_nontemporal_load(src + i) : src[i];
-  }
-}
 
 // Dispatch: one wave per 1 KiB chunk of a token row (64 lanes x 16 bytes),
 // the chunks of a token on consecutive waves; each wave loads its chunk once
@@ -54,7 +41,7 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch(
     int wpt, int rows, const float* __restrict__ xs, float* __restrict__ bs, int nsc) {
   const int K = KT ? KT : K_;
   const int lane = threadIdx.x & 63;
-  const int gw = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  const int gw = uniform(blockIdx.x * kWavesPerRowBlock + (threadIdx.x >> 6));
   const int t = gw / wpt, part = gw - t * wpt;
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
@@ -119,110 +106,53 @@ __device__ __forceinline__ u32x4 pack_row(const float* acc) {
   return o;
 }
 
-// The whole row (CPL * 1 KiB) of one token, every row valid: straight-line
-// code, so the compiler issues all K * CPL loads before the first FMA.
-template <int KT, int CPL, bool kBF16>
-__device__ __forceinline__ void combine_whole_row(const u32x4* __restrict__ ye, const int (&p)[KT],
-                                                  const float* __restrict__ wt,
-                                                  u32x4* __restrict__ dst, int lane, int rb16) {
-  constexpr int EPC = kBF16 ? 8 : 4;
-  float acc[CPL][EPC];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c)
-#pragma unroll
-    for (int i = 0; i < EPC; ++i) acc[c][i] = 0.0f;
-#pragma unroll
-  for (int k = 0; k < KT; ++k) {
-    const u32x4* src = ye + (size_t)p[k] * rb16 + lane;
-    const float wk = wt[k];
-    u32x4 v[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = __builtin_nontemporal_load(src + c * 64);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) fma_row<kBF16>(acc[c], wk, v[c]);
-  }
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(pack_row<kBF16>(acc[c]), dst + lane + c * 64);
-}
-
-// Combine: one wave per token; a piece of the row keeps fp32 accumulators
-// in registers while the K expert rows stream through in k order. With a
-// compile-time K and every row inside the buffer, the loads of all K rows
-// are issued before the first FMA. Nontemporal loads and stores measured
-// fastest for this K-read / 1-write pattern on MI355X.
-template <int KT, int CPL, bool kExact, bool kBF16>
+// Combine: one wave per 1 KiB part of a token's output row (64 lanes x 16
+// bytes), the parts of a token on consecutive waves; each lane reads its
+// 16-byte chunk of the token's K expert rows, accumulates w[t][k] * value in
+// fp32 in k order and stores the chunk once. With a compile-time K the K
+// loads are issued before the first FMA. On MI355X this shape (many small
+// waves) moved the K-read / 1-write traffic 2 % faster than a wave holding a
+// token's whole row with all K x 14 loads in flight, and nontemporal loads
+// and stores beat temporal ones for it.
+template <int KT, bool kBF16>
 __global__ __launch_bounds__(kRowThreads) void k_combine(
     const u32x4* __restrict__ ye, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    const int32_t* __restrict__ status, u32x4* __restrict__ y, int N, int K_, int rb16,
+    const int32_t* __restrict__ status, u32x4* __restrict__ y, int N, int K_, int rb16, int wpt,
     int rows) {
   constexpr int EPC = kBF16 ? 8 : 4;  // elements per 16-byte chunk
   const int K = KT ? KT : K_;
   const int lane = threadIdx.x & 63;
-  const int t = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  const int gw = uniform(blockIdx.x * kWavesPerRowBlock + (threadIdx.x >> 6));
+  const int t = gw / wpt, part = gw - t * wpt;
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
-  u32x4* dst = y + (size_t)t * rb16;
+  const int ci = part * 64 + lane;  // this lane's chunk of the row
+  if (ci >= rb16) return;
   const int32_t* pt = pos + (size_t)t * K;
   const float* wt = w + (size_t)t * K;
-
+  float acc[EPC];
+#pragma unroll
+  for (int i = 0; i < EPC; ++i) acc[i] = 0.0f;
   if constexpr (KT > 0) {
-    int p[KT];
-    bool all_ok = true;
+    u32x4 v[KT];
+    bool ok[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      p[k] = pt[k];
-      all_ok &= (unsigned)p[k] < (unsigned)rows;
+      const int p = pt[k];
+      ok[k] = (unsigned)p < (unsigned)rows;  // only a broken plan fails this
+      v[k] = __builtin_nontemporal_load(ye + (ok[k] ? (size_t)p : 0) * rb16 + ci);
     }
-    if (all_ok) {
-      if constexpr (kExact) {
-        combine_whole_row<KT, CPL, kBF16>(ye, p, wt, dst, lane, rb16);
-      } else {
-        for (int c0 = lane; c0 < rb16; c0 += CPL * 64) {
-          float acc[CPL][EPC];
 #pragma unroll
-          for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int i = 0; i < EPC; ++i) acc[c][i] = 0.0f;
-#pragma unroll
-          for (int k = 0; k < KT; ++k) {
-            u32x4 v[CPL];
-            load_piece<true, CPL>(v, ye + (size_t)p[k] * rb16, c0, rb16, true);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-              if (c0 + c * 64 < rb16) fma_row<kBF16>(acc[c], wt[k], v[c]);
-          }
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            if (c0 + c * 64 < rb16) __builtin_nontemporal_store(pack_row<kBF16>(acc[c]), dst + c0 + c * 64);
-        }
-      }
-      return;
-    }
-  }
-  // Runtime K, or a row outside the buffer (only a broken plan makes one):
-  // such a row contributes nothing.
-  for (int c0 = lane; c0 < rb16; c0 += CPL * 64) {
-    float acc[CPL][EPC];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-#pragma unroll
-      for (int i = 0; i < EPC; ++i) acc[c][i] = 0.0f;
+    for (int k = 0; k < KT; ++k)
+      if (ok[k]) fma_row<kBF16>(acc, wt[k], v[k]);
+  } else {
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
-      if ((unsigned)p >= (unsigned)rows) continue;
-      const float wk = wt[k];
-      u32x4 v[CPL];
-      load_piece<!kExact, CPL>(v, ye + (size_t)p * rb16, c0, rb16, true);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        if (kExact || c0 + c * 64 < rb16) fma_row<kBF16>(acc[c], wk, v[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int i = c0 + c * 64;
-      if (kExact || i < rb16) __builtin_nontemporal_store(pack_row<kBF16>(acc[c]), dst + i);
+      if ((unsigned)p >= (unsigned)rows) continue;  // a row outside the buffer adds nothing
+      fma_row<kBF16>(acc, wt[k], __builtin_nontemporal_load(ye + (size_t)p * rb16 + ci));
     }
   }
+  __builtin_nontemporal_store(pack_row<kBF16>(acc), y + (size_t)t * rb16 + ci);
 }
 
 // ---- dequantising combine: fp8 e4m3 expert outputs, fp32 scale per 128 -----
@@ -272,7 +202,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_fp8(
   const int K = KT ? KT : K_;
   const int nsc = rb16 / 8;  // scales per row
   const int lane = threadIdx.x & 63;
-  const int gw = uniform(blockIdx.x * kTokensPerRowBlock + (threadIdx.x >> 6));
+  const int gw = uniform(blockIdx.x * kWavesPerRowBlock + (threadIdx.x >> 6));
   const int t = gw / wpt, part = gw - t * wpt;
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
@@ -308,16 +238,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_fp8(
   store_fp8_piece<kBF16>(acc, y + ((size_t)t * rb16 + ci) * OPC);
 }
 
-// Chunks per lane of one piece: the whole row when it is a multiple of
-// 1 KiB up to 16 KiB, else 16-chunk pieces with bounds checks.
-inline int pick_cpl(int rb16, bool& exact) {
-  exact = rb16 % 64 == 0 && rb16 / 64 <= 16;
-  return exact ? rb16 / 64 : 16;
-}
-
 }  // namespace
-
-#define MB_CPL_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 
 hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* x,
                            const float* x_scale, void* buf, float* buf_scale, hipStream_t st) {
@@ -327,7 +248,7 @@ hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* 
   const int rows = d.n_ranks * d.cap;
   const int wpt = (rb16 + 63) / 64;  // waves per token
   const int64_t waves = (int64_t)d.n_tokens * wpt;
-  const dim3 grid((unsigned)((waves + kTokensPerRowBlock - 1) / kTokensPerRowBlock));
+  const dim3 grid((unsigned)((waves + kWavesPerRowBlock - 1) / kWavesPerRowBlock));
   MB_DISPATCH_TOPK(d.top_k, k_dispatch, grid, dim3(kRowThreads), 0, st,
                    static_cast<const u32x4*>(x), o.pos, o.status, static_cast<u32x4*>(buf),
                    d.n_tokens, d.top_k, rb16, wpt, rows, x_scale, buf_scale, nsc);
@@ -337,28 +258,19 @@ hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* 
 template <bool kBF16>
 static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x4* ye,
                              const float* w, u32x4* yy, int rb16, int rows, hipStream_t st) {
-  const dim3 grid((d.n_tokens + kTokensPerRowBlock - 1) / kTokensPerRowBlock);
-  bool exact;
-  const int cpl = pick_cpl(rb16, exact);
-  const int K = d.top_k;
-#define MB_C(KT, C)                                                                        \
-  hipLaunchKernelGGL((k_combine<KT, C, true, kBF16>), grid, dim3(kRowThreads), 0, st, ye,  \
-                     o.pos, w, o.status, yy, d.n_tokens, K, rb16, rows)
-#define MB_CK(C)                       \
-  case C:                              \
-    if (K == 8) MB_C(8, C);            \
-    else if (K == 2) MB_C(2, C);       \
-    else if (K == 1) MB_C(1, C);       \
-    else if (K == 4) MB_C(4, C);       \
-    else MB_C(0, C);                   \
-    break;
-  if (exact) {
-    switch (cpl) { MB_CPL_CASES(MB_CK) default: break; }
-  } else {
-    hipLaunchKernelGGL((k_combine<0, 16, false, kBF16>), grid, dim3(kRowThreads), 0, st, ye,
-                       o.pos, w, o.status, yy, d.n_tokens, K, rb16, rows);
+  const int wpt = (rb16 + 63) / 64;  // waves per token
+  const int64_t waves = (int64_t)d.n_tokens * wpt;
+  const dim3 grid((unsigned)((waves + kWavesPerRowBlock - 1) / kWavesPerRowBlock));
+#define MB_C(KT)                                                                          \
+  hipLaunchKernelGGL((k_combine<KT, kBF16>), grid, dim3(kRowThreads), 0, st, ye, o.pos, w, \
+                     o.status, yy, d.n_tokens, d.top_k, rb16, wpt, rows)
+  switch (d.top_k) {
+    case 1: MB_C(1); break;
+    case 2: MB_C(2); break;
+    case 4: MB_C(4); break;
+    case 8: MB_C(8); break;
+    default: MB_C(0); break;
   }
-#undef MB_CK
 #undef MB_C
 }
 
@@ -368,7 +280,7 @@ static void launch_combine_fp8_t(const mb_dims& d, const mb_plan_bufs& o, const 
                                  hipStream_t st) {
   const int wpt = (rb16 + 63) / 64;  // waves per token
   const int64_t waves = (int64_t)d.n_tokens * wpt;
-  const dim3 grid((unsigned)((waves + kTokensPerRowBlock - 1) / kTokensPerRowBlock));
+  const dim3 grid((unsigned)((waves + kWavesPerRowBlock - 1) / kWavesPerRowBlock));
 #define MB_C(KT)                                                                             \
   hipLaunchKernelGGL((k_combine_fp8<KT, kBF16>), grid, dim3(kRowThreads), 0, st, ye, ys, o.pos, \
                      w, o.status, yy, d.n_tokens, d.top_k, rb16, wpt, rows)
