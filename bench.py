@@ -10,6 +10,12 @@ seeded synthetic routing and rows, resident in HBM before timing starts.
 Expert outputs are the dispatched rows (identity experts), written once
 before timing into a buffer of their own.
 
+A workload of several calls (the 61 layer calls of decode_drift) steps
+through its calls, one per step (the default step count is the number of
+calls), so plan times cover every call. A workload whose row buffers are
+smaller than the last-level cache runs on several buffer sets in turn (at
+least 1 GiB in all), so no step reads what a recent step left in cache.
+
 A workload planned with drift-gated replanning (drift_decode) steps through
 its sequence of calls, one call per step, from a fresh drift state when the
 timed steps begin; the line then also reports which calls replanned, their
@@ -242,7 +248,7 @@ def main() -> int:
     dims = mb.Dims.for_workload(wl)
     log(f"workload {wl.name}: {wl.note}")
     if args.steps is None:
-        args.steps = wl.calls if wl.drift else 20
+        args.steps = wl.calls if wl.calls > 1 else 20
 
     ids, w = W.routing_for(wl)
     x, xs = W.token_rows(wl)
@@ -250,33 +256,54 @@ def main() -> int:
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
     ids_d = torch.from_numpy(ids).to(dev)
     w_d = torch.from_numpy(w).to(dev)
-    x_d = torch.from_numpy(x).view(tdt[wl.dtype_in]).to(dev)
-    xs_d = torch.from_numpy(xs).to(dev) if xs is not None else None
+    # A workload smaller than the 256 MB last-level cache would be timed
+    # warm: its row buffers come in enough sets (at least 1 GiB in all,
+    # at most 32) that each step touches buffers no recent step touched.
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}
+    row_in = wl.hidden * eb[wl.dtype_in] + (wl.hidden // 128 * 4 if wl.dtype_in == "fp8" else 0)
+    footprint = (wl.n_tokens + dims.rows) * row_in + (dims.rows + wl.n_tokens) * wl.hidden * \
+        eb[wl.dtype_out]
+    nsets = min(32, max(1, -(-(1 << 30) // footprint)))
+    x_sets = [torch.from_numpy(x).view(tdt[wl.dtype_in]).to(dev) for _ in range(nsets)]
+    xs_sets = [torch.from_numpy(xs).to(dev) if xs is not None else None for _ in range(nsets)]
+    x_d, xs_d = x_sets[0], xs_sets[0]
     del x
     bufs = mb.PlanBuffers.allocate(dims, dev)
     ws = mb.alloc_workspace(dims, dev)
-    buf = torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_in], device=dev)
-    bs = torch.empty((dims.rows, wl.hidden // 128), dtype=torch.float32, device=dev) \
-        if wl.dtype_in == "fp8" else None
-    y_exp = torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
-    y = torch.empty((wl.n_tokens, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
+    buf_sets = [torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_in], device=dev)
+                for _ in range(nsets)]
+    bs_sets = [torch.empty((dims.rows, wl.hidden // 128), dtype=torch.float32, device=dev)
+               if wl.dtype_in == "fp8" else None for _ in range(nsets)]
+    y_sets = [torch.empty((wl.n_tokens, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
+              for _ in range(nsets)]
+    buf, bs, y = buf_sets[0], bs_sets[0], y_sets[0]
+    y_exp_sets = [torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_out], device=dev)
+                  for _ in range(nsets if not args.combine_fp8 else 1)]
+    y_exp = y_exp_sets[0]
+    # A workload of several calls (layers, or passes of one layer) steps
+    # through its calls' routing decisions, one call per step.
+    if wl.calls > 1:
+        rw = [W.routing_for(wl, c) for c in range(wl.calls)]
+        ids_all = torch.stack([torch.from_numpy(r[0]) for r in rw]).to(dev)
+        w_all = torch.stack([torch.from_numpy(r[1]) for r in rw]).to(dev)
+        del rw
+        log(f"{wl.calls} calls of routing resident; {nsets} buffer set(s)")
+    else:
+        ids_all, w_all = ids_d.unsqueeze(0), w_d.unsqueeze(0)
 
     # Rank speeds of a workload planned against per-rank targets (None: the
     # single water level). For comparison, the equal-target plan's largest
     # ratio of load to the speed-proportional share, outside the timing.
     speeds = W.rank_speeds(wl)
-    # A drift-gated workload: the routing of every call of its sequence, and
-    # a drift state (zero-filled = fresh) for the layer.
+    # A drift-gated workload: a drift state (zero-filled = fresh) for the layer.
     drift = None
     if wl.drift:
-        ids_all = torch.stack([torch.from_numpy(W.routing_for(wl, c)[0])
-                               for c in range(wl.calls)]).to(dev)
         drift = (mb.DriftParams(*wl.drift), mb.alloc_drift_state(dims, dev))
-        log(f"drift gate {wl.drift}: {wl.calls} calls of routing resident")
+        log(f"drift gate {wl.drift}")
 
     def plan_call(i, gated=True):
         if drift is None:
-            mb.plan(dims, ids_d, ws, bufs, speeds=speeds, repair=args.repair)
+            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, repair=args.repair)
         elif gated:
             mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, drift=drift,
                     repair=args.repair)
@@ -300,10 +327,13 @@ def main() -> int:
         ys8 = torch.empty((dims.rows, wl.hidden // 128), dtype=torch.float32, device=dev)
         mb.dispatch(dims, bufs, x_d, y_exp8, xs_d, ys8)
     elif wl.dtype_in == wl.dtype_out:
-        mb.dispatch(dims, bufs, x_d, y_exp, xs_d, bs)
+        for ye in y_exp_sets:
+            mb.dispatch(dims, bufs, x_d, ye, xs_d, bs)
     else:
-        y_exp.copy_(torch.from_numpy(
-            W.rows_bf16(wl.seed, W.TAG_YEXP, wl.hidden, n=dims.rows)).view(torch.bfloat16))
+        gen = torch.from_numpy(W.rows_bf16(wl.seed, W.TAG_YEXP, wl.hidden, n=dims.rows))
+        for ye in y_exp_sets:
+            ye.copy_(gen.view(torch.bfloat16))
+        del gen
     status = mb.plan_status(bufs)
     log(f"status {status.tolist()} (flags, T, max load, moves)")
 
@@ -313,13 +343,15 @@ def main() -> int:
         plan_call(i)
         if ev is not None:
             ev[1].record()
-        mb.dispatch(dims, bufs, x_d, buf, xs_d, bs)
+        k = i % nsets
+        mb.dispatch(dims, bufs, x_sets[k], buf_sets[k], xs_sets[k], bs_sets[k])
         if ev is not None:
             ev[2].record()
+        wi = w_all[i % wl.calls]
         if args.combine_fp8:
-            mb.combine_fp8(dims, bufs, y_exp8, ys8, w_d, y)
+            mb.combine_fp8(dims, bufs, y_exp8, ys8, wi, y_sets[k])
         else:
-            mb.combine(dims, bufs, y_exp, w_d, y)
+            mb.combine(dims, bufs, y_exp_sets[k % len(y_exp_sets)], wi, y_sets[k])
         if ev is not None:
             ev[3].record()
 
@@ -361,9 +393,10 @@ def main() -> int:
     # pairs served on a rank other than the one their token originates on
     src = torch.arange(wl.n_tokens, device=dev).unsqueeze(1) // wl.tokens_per_rank
     nonlocal_pairs = int((bufs.pos.view(wl.n_tokens, wl.top_k) // wl.cap != src).sum())
-    if wl.dtype_in == wl.dtype_out:
+    if wl.dtype_in == wl.dtype_out and wl.calls == 1 and not args.combine_fp8:
         samp = torch.arange(0, wl.n_tokens, max(1, wl.n_tokens // 256), device=dev)
-        err = (y[samp].float() - x_d[samp].float() * w_d[samp].sum(1, keepdim=True)).abs().max()
+        y_last = y_sets[(args.steps - 1) % nsets]
+        err = (y_last[samp].float() - x_d[samp].float() * w_d[samp].sum(1, keepdim=True)).abs().max()
         log(f"identity-expert check: max |y - x * sum(w)| = {float(err):.3e}")
 
     drift_report = None
@@ -390,6 +423,7 @@ def main() -> int:
                 wl.slots_per_rank, "hidden": wl.hidden, "rows_in": wl.dtype_in,
             "rows_out": wl.dtype_out, "cap": wl.cap,
             "expert_outputs": "fp8+scales" if args.combine_fp8 else wl.dtype_out,
+            "calls": wl.calls, "buffer_sets": nsets,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "dispatch_combine_gbps": round(bytes_step / ((disp_ms.mean() + comb_ms.mean()) * 1e-3) / 1e9, 2),
@@ -419,7 +453,7 @@ def main() -> int:
             "traffic": measured_traffic(dominant, wl.name),
         },
     }
-    del buf, y_exp, y, x_d
+    del buf, y_exp, y, x_d, xs_d, bs, buf_sets, y_exp_sets, y_sets, x_sets, xs_sets, bs_sets
     torch.cuda.empty_cache()
     if not args.skip_cpu_baseline:
         log("cpu baseline (oracle)")
