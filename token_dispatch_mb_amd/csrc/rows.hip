@@ -25,6 +25,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowThreads = 256;
 constexpr int kWavesPerRowBlock = kRowThreads / 64;
+// The combine kernels launch 16-wave workgroups: for their small waves this
+// measured 1.5-2 % faster on MI355X than 4- or 8-wave groups (dispatch is
+// fastest with 4).
+constexpr int kCombThreads = 1024;
+constexpr int kWavesPerCombBlock = kCombThreads / 64;
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -115,14 +120,14 @@ __device__ __forceinline__ u32x4 pack_row(const float* acc) {
 // token's whole row with all K x 14 loads in flight, and nontemporal loads
 // and stores beat temporal ones for it.
 template <int KT, bool kBF16>
-__global__ __launch_bounds__(kRowThreads) void k_combine(
+__global__ __launch_bounds__(kCombThreads) void k_combine(
     const u32x4* __restrict__ ye, const int32_t* __restrict__ pos, const float* __restrict__ w,
     const int32_t* __restrict__ status, u32x4* __restrict__ y, int N, int K_, int rb16, int wpt,
     int rows) {
   constexpr int EPC = kBF16 ? 8 : 4;  // elements per 16-byte chunk
   const int K = KT ? KT : K_;
   const int lane = threadIdx.x & 63;
-  const int gw = uniform(blockIdx.x * kWavesPerRowBlock + (threadIdx.x >> 6));
+  const int gw = uniform(blockIdx.x * kWavesPerCombBlock + (threadIdx.x >> 6));
   const int t = gw / wpt, part = gw - t * wpt;
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
@@ -194,7 +199,7 @@ __device__ __forceinline__ void store_fp8_piece(const float* acc, u32x4* __restr
 // in flight per CU than a wave holding a whole row. With a compile-time K
 // the K loads of a part are issued before the first FMA.
 template <int KT, bool kBF16>
-__global__ __launch_bounds__(kRowThreads) void k_combine_fp8(
+__global__ __launch_bounds__(kCombThreads) void k_combine_fp8(
     const u32x4* __restrict__ ye, const float* __restrict__ ys, const int32_t* __restrict__ pos,
     const float* __restrict__ w, const int32_t* __restrict__ status, u32x4* __restrict__ y,
     int N, int K_, int rb16, int wpt, int rows) {
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_fp8(
   const int K = KT ? KT : K_;
   const int nsc = rb16 / 8;  // scales per row
   const int lane = threadIdx.x & 63;
-  const int gw = uniform(blockIdx.x * kWavesPerRowBlock + (threadIdx.x >> 6));
+  const int gw = uniform(blockIdx.x * kWavesPerCombBlock + (threadIdx.x >> 6));
   const int t = gw / wpt, part = gw - t * wpt;
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
@@ -260,9 +265,9 @@ static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x
                              const float* w, u32x4* yy, int rb16, int rows, hipStream_t st) {
   const int wpt = (rb16 + 63) / 64;  // waves per token
   const int64_t waves = (int64_t)d.n_tokens * wpt;
-  const dim3 grid((unsigned)((waves + kWavesPerRowBlock - 1) / kWavesPerRowBlock));
+  const dim3 grid((unsigned)((waves + kWavesPerCombBlock - 1) / kWavesPerCombBlock));
 #define MB_C(KT)                                                                          \
-  hipLaunchKernelGGL((k_combine<KT, kBF16>), grid, dim3(kRowThreads), 0, st, ye, o.pos, w, \
+  hipLaunchKernelGGL((k_combine<KT, kBF16>), grid, dim3(kCombThreads), 0, st, ye, o.pos, w, \
                      o.status, yy, d.n_tokens, d.top_k, rb16, wpt, rows)
   switch (d.top_k) {
     case 1: MB_C(1); break;
@@ -280,9 +285,9 @@ static void launch_combine_fp8_t(const mb_dims& d, const mb_plan_bufs& o, const 
                                  hipStream_t st) {
   const int wpt = (rb16 + 63) / 64;  // waves per token
   const int64_t waves = (int64_t)d.n_tokens * wpt;
-  const dim3 grid((unsigned)((waves + kWavesPerRowBlock - 1) / kWavesPerRowBlock));
+  const dim3 grid((unsigned)((waves + kWavesPerCombBlock - 1) / kWavesPerCombBlock));
 #define MB_C(KT)                                                                             \
-  hipLaunchKernelGGL((k_combine_fp8<KT, kBF16>), grid, dim3(kRowThreads), 0, st, ye, ys, o.pos, \
+  hipLaunchKernelGGL((k_combine_fp8<KT, kBF16>), grid, dim3(kCombThreads), 0, st, ye, ys, o.pos, \
                      w, o.status, yy, d.n_tokens, d.top_k, rb16, wpt, rows)
   switch (d.top_k) {
     case 1: MB_C(1); break;
