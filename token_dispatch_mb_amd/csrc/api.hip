@@ -136,18 +136,23 @@ static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t*
 
   // count -> per-source offsets and totals -> greedy placement -> lookup
   // tables -> per-pair rows, all on `stream`, no host synchronisation.
-  if (launch_count(*dims, g, ids_dev, blockcnt, blockflags, brank, stream) != hipSuccess)
+  // With one routing block per source rank, the block counts are d[s][e]
+  // and every block offset is 0: k_count writes d itself, the scan is
+  // skipped and k_plan sums c_e.
+  const bool one_block = g.nbps == 1;
+  if (launch_count(*dims, g, ids_dev, one_block ? out->counts : blockcnt, blockflags, brank,
+                   stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
+  if (!one_block &&
+      launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_plan(*dims, g, *out, rank_speed, drift, drift_state, repair, blockflags,
-                  expert_total, host_range, stream) != hipSuccess)
+                  one_block ? nullptr : expert_total, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_assign(*dims, g, ids_dev, brank, blockoff, pair_tab, host_list, host_range, *out,
-                    stream) !=
-      hipSuccess)
+  if (launch_assign(*dims, g, ids_dev, brank, one_block ? nullptr : blockoff, pair_tab, host_list,
+                    host_range, *out, stream) != hipSuccess)
     return MB_ERR_HIP;
   return MB_OK;
 }

@@ -726,9 +726,21 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     return;
   }
 
-  // c_e (summed over sources by k_scan); initial quotas and holders.
+  // c_e (summed over sources by k_scan, or here from d[s][e] when k_scan
+  // did not run); initial quotas and holders.
   for (int e = tid; e < E; e += kPlanThreads) {
-    const int c = a.expert_total[e];
+    int c = 0;
+    if (a.expert_total) {
+      c = a.expert_total[e];
+    } else {
+      for (int s0 = 0; s0 < P; s0 += 32) {  // 32 independent loads in flight
+        int v[32];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) v[q] = s0 + q < P ? a.counts[(size_t)(s0 + q) * E + e] : 0;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) c += v[q];
+      }
+    }
     m.c[e] = c;
     m.qh[e] = c;
   }

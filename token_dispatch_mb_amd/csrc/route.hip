@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   }
   if (has_tokens) {
     for (int i = tl; i < E; i += kTokensPerBlock) {
-      boff[i] = blockoff[(size_t)b * E + i];
+      boff[i] = blockoff ? blockoff[(size_t)b * E + i] : 0;  // null: one block per source
       ptab[i] = pair_tab[(size_t)s * E + i];
       hrange[i] = host_range[i];
     }
@@ -207,13 +207,21 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   const int rows = P * cap;
   // Pass 1 keeps the first local_quota pairs of (s, e) on s; a later pair is
   // surplus number u of e and goes to the host whose share covers u.
+  // The hosts' share ends ascend (each host listed has spare quota), so the
+  // host of surplus number u is found by bisection.
   auto search = [&](int e, int u, int q0) {
     const int2 rg = hrange[e];
-    for (int q = q0; q < rg.y; ++q) {
-      const HostEntry h = hosts[rg.x + q];
-      if (u < h.end) return h.base + u + (h.rank < s ? h.lt : 0);
+    int lo = q0, hi = rg.y;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (u < hosts[rg.x + mid].end)
+        hi = mid;
+      else
+        lo = mid + 1;
     }
-    return -1;
+    if (lo >= rg.y) return -1;
+    const HostEntry h = hosts[rg.x + lo];
+    return h.base + u + (h.rank < s ? h.lt : 0);
   };
   if constexpr (KT > 0) {
     // All table reads of the K pairs are independent; the first two hosts of
