@@ -720,3 +720,91 @@ def test_combine_fp8_fatal_status_writes_nothing():
     mb.combine_fp8(dg, gp.bufs, q, sc, torch.ones((N, K), device=d), y)
     torch.cuda.synchronize()
     assert torch.isnan(y.float()).all()
+
+
+# ---- HIP graph capture ---------------------------------------------------------------
+
+def test_graph_capture_replays():
+    """plan + dispatch + combine captured once in a HIP graph (no host
+    synchronisation, no allocation, no memset inside the calls) and replayed
+    on three different routings copied into the captured inputs, with eager
+    library work between the replays: every replay equals the oracle."""
+    wl = W.get_workload("mixtral")
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    d = G.dev()
+    ids0, w0 = W.routing_for(wl, 0)
+    x0, _ = W.token_rows(wl, 0)
+    ids_s = torch.from_numpy(ids0).to(d)
+    w_s = torch.from_numpy(w0).to(d)
+    x_s = G.torch_rows(x0, O.BF16)
+    bufs = mb.PlanBuffers.allocate(dg, d)
+    ws = mb.alloc_workspace(dg, d)
+    buf = torch.zeros((dg.rows, dg.hidden), dtype=torch.bfloat16, device=d)
+    y = torch.zeros((dg.n_tokens, dg.hidden), dtype=torch.bfloat16, device=d)
+
+    def layer():
+        mb.plan(dg, ids_s, ws, bufs)
+        mb.dispatch(dg, bufs, x_s, buf)
+        mb.combine(dg, bufs, buf, w_s, y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    other = G.GpuPlan(dg)
+    for call in (3, 7, 11):
+        ids, w = W.routing_for(wl, call)
+        x, _ = W.token_rows(wl, call)
+        ids_s.copy_(torch.from_numpy(ids))
+        w_s.copy_(torch.from_numpy(w))
+        x_s.copy_(G.torch_rows(x, O.BF16))
+        graph.replay()
+        other.run(W.routing_for(wl, call + 1)[0])  # eager work between replays
+        torch.cuda.synchronize()
+        ref = O.plan(od, ids)
+        got = {k: getattr(bufs, k).cpu().numpy() for k in G.PLAN_FIELDS}
+        got["rep_expert"] = got["rep_expert"][:, : dg.slots_per_rank]
+        G.assert_plan_equal(got, ref)
+        ref_buf, _, _ = O.dispatch(od, ref, x, None)
+        used = ref.row_src >= 0
+        assert np.array_equal(G.rows_to_bytes(buf)[used], ref_buf[used]), call
+        y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, ref_buf.view(np.uint16).reshape(
+            -1, od.hidden))
+        G.assert_combine_close(G.y_to_f64(y), y_ref, mag, "bf16")
+
+
+def test_graph_capture_drift_state_advances():
+    """A drift-gated plan captured in a graph: each replay advances the
+    caller's state exactly as the oracle's sequence does."""
+    wl = W.get_workload("drift_decode")
+    dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
+    dg.hidden = od.hidden = 128
+    d = G.dev()
+    num, den, win, _ = wl.drift
+    gprm, oprm = mb.DriftParams(num, den, win, 2), O.DriftParams(num, den, win, 2)
+    ids_s = torch.from_numpy(W.routing_for(wl, 0)[0]).to(d)
+    state = mb.alloc_drift_state(dg, d)
+    st = O.DriftState(wl.n_experts, wl.n_ranks, wl.slots_per_rank)
+    gp = G.GpuPlan(dg)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mb.plan(dg, ids_s, gp.ws, gp.bufs, drift=(gprm, state))
+    torch.cuda.current_stream().wait_stream(side)
+    state.zero_()  # the warm-up call above advanced it
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mb.plan(dg, ids_s, gp.ws, gp.bufs, drift=(gprm, state))
+    state.zero_()  # capture does not run the kernels; start fresh anyway
+    for call in range(0, 30, 3):
+        ids, _ = W.routing_for(wl, call)
+        ids_s.copy_(torch.from_numpy(ids))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = O.plan(od, ids, drift=(oprm, st))
+        G.assert_plan_equal(gp.fetch(), ref)
+        _assert_state_equal(state, st, wl.n_experts, f"replay at call {call}")
