@@ -211,6 +211,9 @@ def main() -> int:
     ap.add_argument("--combine-fp8", action="store_true",
                     help="fp8-row workloads: expert outputs stay fp8 with their scales and "
                          "mb_combine_fp8 dequantises while combining")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps replayed from HIP graphs captured once per "
+                         "(call, buffer set): the launch cost leaves the step")
     ap.add_argument("--repair", action="store_true",
                     help="plan with the quota repair after placement (mb_plan_ex)")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
@@ -404,6 +407,36 @@ def main() -> int:
         drift_report = _drift_report(args.steps, plan_ms, plan_call, bufs, drift, mean_load, mb,
                                      torch, np)
 
+    graph_report = None
+    if args.graph:
+        # One graph per distinct (call, buffer set) of the step sequence,
+        # captured after the eager run and its checks; the replays take the same steps.
+        graphs = {}
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            key = (i % wl.calls, i % nsets)
+            if key not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(i)
+                graphs[key] = g
+        if drift is not None:
+            drift[1].zero_()
+        for i in range(min(args.warmup, args.steps)):
+            graphs[(i % wl.calls, i % nsets)].replay()
+        if drift is not None:
+            drift[1].zero_()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record()
+        for i in range(args.steps):
+            graphs[(i % wl.calls, i % nsets)].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        g_ms = g0.elapsed_time(g1) / args.steps
+        graph_report = {"graphs": len(graphs), "ms_per_step": round(g_ms, 4)}
+        log(f"graph replay: {g_ms:.4f} ms per step over {len(graphs)} graph(s)")
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -442,6 +475,9 @@ def main() -> int:
             "max_load_over_share": round(float(_speed_ratio(bufs.load_post.cpu().numpy(), speeds, wl)), 5),
             "same_with_equal_targets": round(wir_equal, 5)},
         "drift_gate": drift_report,
+        "graph_replay": None if graph_report is None else dict(
+            graph_report, value=round((ab["dispatch"] + ab["combine"]) /
+                                      (graph_report["ms_per_step"] * 1e-3) / 1e9, 2)),
         "wall_s_timed": round(t_wall, 4),
         "roofline": {
             "kernel": dominant,

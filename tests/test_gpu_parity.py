@@ -227,6 +227,35 @@ def test_maximum_sizes():
     _edge(P * S, 8, P * eh, P, R, 4, ids, din="f32", dout="f32", label="16-byte f32 rows")
 
 
+def _skewed_ids(N, K, E, seed):
+    """Distinct ids per token, (b + k) mod E for k < K, from a skewed first
+    choice b = floor(E u^3): cheap to draw at tens of millions of pairs."""
+    rng = np.random.default_rng(seed)
+    b = np.floor(E * rng.random(N) ** 3).astype(np.int64)
+    return ((b[:, None] + np.arange(K)[None]) % E).astype(np.int32)
+
+
+@pytest.mark.parametrize("N,K,E,P,R,kind", [
+    (2 ** 25 - 64, 1, 128, 64, 1, "one"),   # register greedy, loads up to the key limit
+    (2 ** 25, 1, 128, 64, 1, "one"),        # N*K = 2^25: the LDS greedy
+    (2 ** 22 - 32, 8, 256, 32, 2, "skew"),  # register greedy, 32 lanes
+    (2 ** 22, 8, 256, 32, 2, "skew"),       # the LDS greedy
+])
+def test_plan_around_the_packed_key_limit(N, K, E, P, R, kind):
+    """The register greedy packs (value, index) into one int32 key, exact
+    while N*K < 2^25; larger plans run the LDS greedy. Both sides of the
+    limit, with the busiest rank's excess close to it, are bit-exact."""
+    ids = np.zeros((N, 1), np.int32) if kind == "one" else _skewed_ids(N, K, E, 5)
+    cap = 2 * (N // P) * K
+    G.log(f"case packed-key limit N={N} K={K} E={E} P={P} R={R} {kind}")
+    dg = mb.Dims.make(N, K, E, P, R, 8, cap=cap, dtype_in="f32", dtype_out="f32")
+    od = O.make_dims(N, K, E, P, R, 8, cap=cap, dtype_in="f32", dtype_out="f32")
+    got = G.GpuPlan(dg).run(ids).fetch()
+    ref = O.plan(od, ids)
+    G.assert_plan_equal(got, ref)
+    assert ref.status[0] == 0 and ref.status[3] > 0
+
+
 def test_fp8_rows_and_scales_small():
     ids, _ = W.routing(512, 32, 4, W.NOISE_GUMBEL, 1.1, 1.0, 21)
     _edge(512, 4, 32, 8, 1, 256, ids, din="fp8", dout="bf16", label="fp8")

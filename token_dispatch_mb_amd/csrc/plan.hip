@@ -1,7 +1,7 @@
 // plan.hip — the single-workgroup replica planner of libmoebal.
 //
-// One workgroup of 256 threads:
-//  1. routed pairs per expert c_e (summed over sources by k_scan);
+// One workgroup of 256 threads (the per-rank targets come from the host):
+//  1. routed pairs per expert c_e (summed over sources by k_scan, or here);
 //  2. wave 0 runs the greedy with lane r = logical rank r (P <= 64): the
 //     rank farthest above its target tau_r gives a replica of its heaviest
 //     home expert to the rank farthest below its own target that has a free
@@ -12,9 +12,10 @@
 // The lookup tables that turn a pair's stable rank into its dispatch row are
 // built afterwards by k_tables (route.hip), one wave per expert.
 //
-// Every choice is made by full-wave DPP reductions followed by a ballot that
-// picks the lowest lane (or a per-lane scan in index order), so ties resolve
-// to the lowest rank / expert index and the result does not depend on timing.
+// Every choice is a full-wave DPP reduction over keys that carry the lane or
+// expert index in their low bits (or a ballot that picks the lowest lane, or
+// a per-lane scan in index order), so ties resolve to the lowest rank /
+// expert index and the result does not depend on timing.
 //
 // Sources: ISER-MoE, Methodology, HALO-Q Scheduler — Objective 1 (water
 // level T = ceil(sum L_r / P)), stage 2 (busiest rank's heaviest home expert
@@ -33,7 +34,8 @@ namespace {
 
 struct PlanArgs {
   int N, K, E, P, R, cap, Eh, NS, nblk;
-  int32_t speed[kMaxRanks];  // rank speeds (all 1: the single water level)
+  int32_t tau[kMaxRanks];  // target of each rank (all T with equal speeds)
+  int tau_max;
   // drift-gated replanning: state buffer (nullptr: run the greedy every call)
   uint8_t* drift_state;
   int delta_num, delta_den, window, check_every;
@@ -136,72 +138,84 @@ __device__ __forceinline__ void wave_lds_sync() {
 // plus reads of the busiest rank's heaviest expert, which each rank lane
 // keeps up to date in registers.
 //
-// EHM >= Eh: registers per lane for the home quotas of its rank.
+// EHM >= Eh: registers per lane for the home quotas of its rank; kLanes =
+// 32 when P <= 32 (shorter reductions), else 64.
 //
-// One basic block per move: the tournament for every lane's heaviest expert
-// (which only the previous donor's quota changed) sits next to the two load
-// reductions it does not depend on, so their dependency chains interleave;
-// the state updates are selects, and each move is recorded in the registers
+// Packed keys make every choice one max or min: a rank lane enters the
+// busiest-rank reduction with x*64 + (63 - lane) and, when open, the
+// open-rank reduction with x*64 + lane, and keeps its home quotas as
+// q*32 + (31 - j), so the extreme key also names the lowest rank or expert
+// index among equal values. The keys are exact while |x| and q stay below
+// 2^25, which N*K < 2^25 guarantees (loads, targets and quotas are at most
+// N*K); larger plans take greedy_lds. A move changes two lanes (the donor's
+// load and one quota key, the destination's load and slot count); those
+// updates run under a one-lane mask. Each move is recorded in the registers
 // of lane (move mod 64) and written to LDS 64 moves at a time.
-template <int EHM>
+constexpr long long kPackedPairsLimit = 1LL << 25;
+
+template <int EHM, int kLanes>
 __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
+  static_assert(EHM <= 32, "five index bits per quota key");
   const int lane = threadIdx.x;
   const int P = a.P, R = a.R, Eh = a.Eh;
   const bool rank_lane = lane < P;
   const int tau = rank_lane ? m.tau[lane] : 0;
-  int q[EHM];
+  int kq[EHM];  // quota keys; -1 pads ranks with fewer home experts
   int load = 0;
 #pragma unroll
   for (int j = 0; j < EHM; ++j) {
-    q[j] = (rank_lane && j < Eh) ? m.c[lane * Eh + j] : 0;
-    load += q[j];
+    const bool real = rank_lane && j < Eh;
+    const int q = real ? m.c[lane * Eh + j] : 0;
+    load += q;
+    kq[j] = real ? q * 32 + (31 - j) : -1;
   }
   const int lpre = load;
   int used = 0, moves = 0, unbalanced = 0;
   int rec_e = 0, rec_m = 0, rec_i = 0;  // the move recorded in this lane
 
   for (;;) {
-    // Heaviest remaining home expert of this lane's rank, lowest index on
-    // ties: a pairwise tournament, log2(EHM) levels.
-    int v[EHM], ix[EHM];
+    // Heaviest remaining home expert of each rank (max3 chain).
+    int bk = kq[0];
 #pragma unroll
-    for (int j = 0; j < EHM; ++j) {
-      v[j] = q[j];
-      ix[j] = j;
-    }
-#pragma unroll
-    for (int width = EHM / 2; width >= 1; width /= 2)
-#pragma unroll
-      for (int j = 0; j < width; ++j) {
-        const bool right = v[2 * j + 1] > v[2 * j];  // ties keep the lower index
-        v[j] = right ? v[2 * j + 1] : v[2 * j];
-        ix[j] = right ? ix[2 * j + 1] : ix[2 * j];
-      }
-    const int bq = v[0], bj = ix[0];
+    for (int j = 1; j + 1 < EHM; j += 2) bk = max(bk, max(kq[j], kq[j + 1]));
+    bk = max(bk, kq[EHM - 1]);
 
     const int x = load - tau;
     const bool open_lane = rank_lane && used < R && x < 0;
-    int xmax, xmin;
-    wave_max_min_i32(rank_lane ? x : INT32_MIN, open_lane ? x : INT32_MAX, xmax, xmin);
-    if (xmax <= 0) break;
-    if (xmin == INT32_MAX) {  // no open rank
+    int kmax, kmin;
+    wave_max_min_i32<kLanes>(rank_lane ? x * 64 + (63 - lane) : INT32_MIN,
+                             open_lane ? x * 64 + lane : INT32_MAX, kmax, kmin);
+    __asm__ volatile("" : "+v"(bk));  // keep the tournament beside the reductions
+    if (kmax < 64) break;             // largest x <= 0: every rank at or below target
+    if (kmin == INT32_MAX) {          // no open rank
       unbalanced = 1;
       break;
     }
-    const int rs = lowest_lane(ballot64(rank_lane && x == xmax));
-    const int d = lowest_lane(ballot64(open_lane && x == xmin));
-    const int qmax = __builtin_amdgcn_readlane(bq, rs);
-    const int jb = __builtin_amdgcn_readlane(bj, rs);
+    const int rs = 63 - (kmax & 63);
+    const int d = kmin & 63;
+    const int kd = __builtin_amdgcn_readlane(bk, rs);
     const int slot = __builtin_amdgcn_readlane(used, d);  // slots fill in index order
-    const int mv = min(-xmin, qmax);
+    const int mv = min(-(kmin >> 6), kd >> 5);
+    const int jb = 31 - (kd & 31);
     const int mi = moves & 63;
-    rec_e = lane == mi ? rs * Eh + jb : rec_e;
-    rec_m = lane == mi ? mv : rec_m;
-    rec_i = lane == mi ? d * R + slot : rec_i;
-    load += (lane == d ? mv : 0) - (lane == rs ? mv : 0);
-    used += lane == d ? 1 : 0;
+    if (lane == mi) {
+      rec_e = rs * Eh + jb;
+      rec_m = mv;
+      rec_i = d * R + slot;
+    }
+    if (lane == d) {
+      load += mv;
+      used += 1;
+    }
+    if (lane == rs) {
+      load -= mv;
+      if constexpr (EHM <= 8) {
 #pragma unroll
-    for (int j = 0; j < EHM; ++j) q[j] -= (lane == rs && j == jb) ? mv : 0;
+        for (int j = 0; j < EHM; ++j) kq[j] -= j == jb ? mv * 32 : 0;
+      } else {
+        kq[jb] -= mv * 32;  // uniform index: relative register addressing
+      }
+    }
     ++moves;
     if ((moves & 63) == 0) {
       m.repE[rec_i] = rec_e;
@@ -217,7 +231,7 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
   if (rank_lane) {
 #pragma unroll
     for (int j = 0; j < EHM; ++j)
-      if (j < Eh) m.qh[lane * Eh + j] = q[j];
+      if (j < Eh) m.qh[lane * Eh + j] = kq[j] >> 5;
     m.loadv[lane] = load;
     m.lpre[lane] = lpre;
   }
@@ -225,6 +239,18 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     m.misc[0] = moves;
     m.misc[1] = unbalanced;
   }
+}
+
+template <int kLanes>
+__device__ void greedy_regs_for(const PlanArgs& a, PlanSmem& m) {
+  if (a.Eh <= 4)
+    greedy_regs<4, kLanes>(a, m);
+  else if (a.Eh <= 8)
+    greedy_regs<8, kLanes>(a, m);
+  else if (a.Eh <= 16)
+    greedy_regs<16, kLanes>(a, m);
+  else
+    greedy_regs<32, kLanes>(a, m);
 }
 
 // The same greedy for ranks with more home experts than fit in registers:
@@ -698,25 +724,54 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   const int E = a.E, P = a.P, R = a.R, Eh = a.Eh, NS = a.NS;
   PlanSmem m = carve(smem, E, P, R, NS);
 
-  // Targets (ViBE, token target in proportion to speed), exact in integers:
-  // tau_r = ceil(N*K * s_r / sum s); equal speeds give T = ceil(N*K / P).
-  if (tid < 64) {
-    const bool rank_lane = tid < P;
-    const int s = rank_lane ? a.speed[tid] : 0;
-    const int sum = __builtin_amdgcn_readlane(wave_inclusive_sum(s), 63);
-    const long long nk = (long long)a.N * a.K;
-    const int tau = rank_lane ? (int)((nk * s + sum - 1) / sum) : 0;
-    m.tau[tid] = tau;
-    const int tmax = wave_max_i32(tau);
-    if (tid == 0) m.misc[3] = tmax;
+  // The targets, the status bits of the routing decisions and c_e (summed
+  // over sources by k_scan, or here from d[s][e] when k_scan did not run)
+  // are loaded before any of them is used, so their latencies overlap.
+  static_assert(kMaxExperts <= 4 * kPlanThreads, "c_e takes one batch of loads");
+  const int tau_v = a.tau[tid & (kMaxRanks - 1)];
+  int f[4], cv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = u * kPlanThreads + tid;
+    f[u] = i < a.nblk ? a.blockflags[i] : 0;
   }
-
-  // Status bits of the routing decisions.
-  int fl = 0;
-  for (int i = tid; i < a.nblk; i += kPlanThreads) fl |= a.blockflags[i];
-  const int bad = __syncthreads_or(fl & MB_ST_BAD_ID);
-  const int dup = __syncthreads_or(fl & MB_ST_DUP_ID);
-  if (bad || dup) {
+  if (a.expert_total) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = u * kPlanThreads + tid;
+      cv[u] = e < E ? a.expert_total[e] : 0;
+    }
+  }
+  int fl = f[0] | f[1] | f[2] | f[3];
+  for (int i = 4 * kPlanThreads + tid; i < a.nblk; i += kPlanThreads) fl |= a.blockflags[i];
+  if (a.expert_total) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = u * kPlanThreads + tid;
+      if (e < E) m.c[e] = m.qh[e] = cv[u];
+    }
+  } else {
+    for (int e = tid; e < E; e += kPlanThreads) {
+      int c = 0;
+      for (int s0 = 0; s0 < P; s0 += 32) {  // 32 independent loads in flight
+        int v[32];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) v[q] = s0 + q < P ? a.counts[(size_t)(s0 + q) * E + e] : 0;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) c += v[q];
+      }
+      m.c[e] = m.qh[e] = c;
+    }
+  }
+  if (tid < 64) m.tau[tid] = tid < P ? tau_v : 0;
+  if (tid == 0) m.misc[3] = a.tau_max;
+  for (int i = tid; i < P * R; i += kPlanThreads) {
+    m.repE[i] = -1;
+    m.repM[i] = 0;
+  }
+  if (__syncthreads_or(fl)) {
+    const int bad = __syncthreads_or(fl & MB_ST_BAD_ID);
+    const int dup = __syncthreads_or(fl & MB_ST_DUP_ID);
     if (tid == 0) {
       a.status[0] = (bad ? MB_ST_BAD_ID : 0) | (dup ? MB_ST_DUP_ID : 0);
       a.status[1] = m.misc[3];
@@ -726,45 +781,17 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     return;
   }
 
-  // c_e (summed over sources by k_scan, or here from d[s][e] when k_scan
-  // did not run); initial quotas and holders.
-  for (int e = tid; e < E; e += kPlanThreads) {
-    int c = 0;
-    if (a.expert_total) {
-      c = a.expert_total[e];
-    } else {
-      for (int s0 = 0; s0 < P; s0 += 32) {  // 32 independent loads in flight
-        int v[32];
-#pragma unroll
-        for (int q = 0; q < 32; ++q) v[q] = s0 + q < P ? a.counts[(size_t)(s0 + q) * E + e] : 0;
-#pragma unroll
-        for (int q = 0; q < 32; ++q) c += v[q];
-      }
-    }
-    m.c[e] = c;
-    m.qh[e] = c;
-  }
-  for (int i = tid; i < P * R; i += kPlanThreads) {
-    m.repE[i] = -1;
-    m.repM[i] = 0;
-  }
-  __syncthreads();
-
   const bool drift = a.drift_state != nullptr;
   if (tid < 64) {
     if (drift) drift_decide(a, m);
     if (drift && !m.misc[4])
       replay_kept(a, m);
-    else if (Eh <= 4)
-      greedy_regs<4>(a, m);
-    else if (Eh <= 8)
-      greedy_regs<8>(a, m);
-    else if (Eh <= 16)
-      greedy_regs<16>(a, m);
-    else if (Eh <= 32)
-      greedy_regs<32>(a, m);
-    else
+    else if ((long long)a.N * a.K >= kPackedPairsLimit || Eh > 32)
       greedy_lds(a, m);
+    else if (P <= 32)
+      greedy_regs_for<32>(a, m);
+    else
+      greedy_regs_for<64>(a, m);
     if (a.repair && R > 0) quota_repair(a, m);
   }
   __syncthreads();
@@ -773,16 +800,38 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     __syncthreads();
   }
 
-  // Slot quotas, cu_seqlens and loads, one thread per rank.
-  for (int r = tid; r < P; r += kPlanThreads) {
-    int acc = 0;
-    a.cu_seqlens[r * (NS + 1)] = 0;
-    for (int i = 0; i < NS; ++i) {
-      const int q = i < Eh ? m.qh[r * Eh + i] : m.repM[r * R + (i - Eh)];
-      a.slot_quota[r * NS + i] = q;
-      acc += q;
-      a.cu_seqlens[r * (NS + 1) + i + 1] = acc;
+  // Slot quotas, cu_seqlens and loads: one thread per rank, or with many
+  // slots per rank one wave per rank (lane = slot, a wave scan per 64).
+  auto slot_q = [&](int r, int i) { return i < Eh ? m.qh[r * Eh + i] : m.repM[r * R + (i - Eh)]; };
+  if (NS <= 16) {
+    for (int r = tid; r < P; r += kPlanThreads) {
+      int acc = 0;
+      a.cu_seqlens[r * (NS + 1)] = 0;
+      for (int i = 0; i < NS; ++i) {
+        const int q = slot_q(r, i);
+        a.slot_quota[r * NS + i] = q;
+        acc += q;
+        a.cu_seqlens[r * (NS + 1) + i + 1] = acc;
+      }
     }
+  } else {
+    const int w = tid >> 6, ln = tid & 63;
+    for (int r = w; r < P; r += kPlanThreads / 64) {
+      int base = 0;
+      if (ln == 0) a.cu_seqlens[r * (NS + 1)] = 0;
+      for (int i0 = 0; i0 < NS; i0 += 64) {
+        const int i = i0 + ln;
+        const int q = i < NS ? slot_q(r, i) : 0;
+        const int inc = wave_inclusive_sum(q);
+        if (i < NS) {
+          a.slot_quota[r * NS + i] = q;
+          a.cu_seqlens[r * (NS + 1) + i + 1] = base + inc;
+        }
+        base += __builtin_amdgcn_readlane(inc, 63);
+      }
+    }
+  }
+  for (int r = tid; r < P; r += kPlanThreads) {
     a.load_pre[r] = m.lpre[r];
     a.load_post[r] = m.loadv[r];
   }
@@ -845,7 +894,16 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.Eh = g.Eh;
   a.NS = g.NS;
   a.nblk = g.nblk;
-  for (int r = 0; r < kMaxRanks; ++r) a.speed[r] = r < d.n_ranks ? rank_speed[r] : 0;
+  // Targets (ViBE, token target in proportion to speed), exact in integers:
+  // tau_r = ceil(N*K * s_r / sum s); equal speeds give T = ceil(N*K / P).
+  long long sum = 0;
+  for (int r = 0; r < d.n_ranks; ++r) sum += rank_speed[r];
+  const long long nk = (long long)d.n_tokens * d.top_k;
+  a.tau_max = 0;
+  for (int r = 0; r < kMaxRanks; ++r) {
+    a.tau[r] = r < d.n_ranks ? (int32_t)((nk * rank_speed[r] + sum - 1) / sum) : 0;
+    a.tau_max = a.tau[r] > a.tau_max ? a.tau[r] : a.tau_max;
+  }
   a.drift_state = static_cast<uint8_t*>(drift_state);
   a.delta_num = drift ? drift->delta_num : 0;
   a.delta_den = drift ? drift->delta_den : 1;

@@ -45,9 +45,13 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// max of `a` and min of `b` over the wave, the two DPP chains interleaved so
-// that each hides the other's latency.
+// max of `a` and min of `b` over lanes 0..kLanes-1 (kLanes = 32 or 64; the
+// other lanes must hold the identities), the two DPP chains interleaved so
+// that each hides the other's latency. With 32 lanes the row_bcast 31 step
+// is left out and the result is read from lane 31.
+template <int kLanes = 64>
 __device__ __forceinline__ void wave_max_min_i32(int a, int b, int& amax, int& bmin) {
+  static_assert(kLanes == 32 || kLanes == 64, "lane count");
   constexpr int IA = INT32_MIN, IB = INT32_MAX;
   a = max(a, dpp_or_identity<0x111, 0xf>(IA, a));
   b = min(b, dpp_or_identity<0x111, 0xf>(IB, b));
@@ -59,10 +63,12 @@ __device__ __forceinline__ void wave_max_min_i32(int a, int b, int& amax, int& b
   b = min(b, dpp_or_identity<0x118, 0xf>(IB, b));
   a = max(a, dpp_or_identity<0x142, 0xa>(IA, a));
   b = min(b, dpp_or_identity<0x142, 0xa>(IB, b));
-  a = max(a, dpp_or_identity<0x143, 0xc>(IA, a));
-  b = min(b, dpp_or_identity<0x143, 0xc>(IB, b));
-  amax = __builtin_amdgcn_readlane(a, 63);
-  bmin = __builtin_amdgcn_readlane(b, 63);
+  if constexpr (kLanes == 64) {
+    a = max(a, dpp_or_identity<0x143, 0xc>(IA, a));
+    b = min(b, dpp_or_identity<0x143, 0xc>(IB, b));
+  }
+  amax = __builtin_amdgcn_readlane(a, kLanes - 1);
+  bmin = __builtin_amdgcn_readlane(b, kLanes - 1);
 }
 
 // Inclusive prefix sum over the 64 lanes (every lane active).
