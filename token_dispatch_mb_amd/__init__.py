@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import torch
 
@@ -154,6 +154,38 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check(t, name: str, dtype=None, numel: int | None = None, nbytes: int | None = None) -> None:
+    """Refuse, before any C call, what the kernels cannot take: a tensor off
+    the GPU (a host pointer would fault the device), a strided view, a wrong
+    dtype or too few elements / bytes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (it is {t.dtype})")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _speeds(dims: "Dims", speeds):
+    if len(speeds) < dims.n_ranks:
+        raise ValueError(f"speeds lists {len(speeds)} ranks, {dims.n_ranks} needed")
+    return (ctypes.c_int32 * dims.n_ranks)(*[int(v) for v in speeds[: dims.n_ranks]])
+
+
+def _dims_key(dims: "Dims") -> tuple:
+    return tuple(getattr(dims, n) for n, _ in Dims._fields_)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -173,6 +205,8 @@ class PlanBuffers:
     pos: torch.Tensor
     row_src: torch.Tensor
     status: torch.Tensor
+    _key: tuple | None = field(default=None, init=False, repr=False, compare=False)
+    _c: _PlanBufsC | None = field(default=None, init=False, repr=False, compare=False)
 
     @classmethod
     def allocate(cls, dims: Dims, device) -> "PlanBuffers":
@@ -183,8 +217,27 @@ class PlanBuffers:
                    slot_quota=z(P, ns), cu_seqlens=z(P, ns + 1), pos=z(N, K),
                    row_src=z(dims.rows), status=z(4))
 
-    def c_struct(self) -> _PlanBufsC:
-        return _PlanBufsC(*[self.__dict__[n].data_ptr() for n, _ in _PlanBufsC._fields_])
+    def check(self, dims: Dims) -> None:
+        """Every buffer an int32 GPU tensor with room for its output."""
+        P, E, R, N, K, ns = (dims.n_ranks, dims.n_experts, dims.slots_per_rank, dims.n_tokens,
+                             dims.top_k, dims.n_slots)
+        need = {"counts": P * E, "load_pre": P, "load_post": P, "rep_expert": P * R,
+                "slot_quota": P * ns, "cu_seqlens": P * (ns + 1), "pos": N * K,
+                "row_src": dims.rows, "status": 4}
+        for name, n in need.items():
+            _check(getattr(self, name), name, torch.int32, numel=n)
+
+    def c_struct(self, dims: Dims | None = None) -> _PlanBufsC:
+        """The mb_plan_bufs of these tensors; with `dims`, checked against
+        them first (once per set of pointers and sizes)."""
+        ptrs = tuple(getattr(self, n).data_ptr() for n, _ in _PlanBufsC._fields_)
+        if dims is None:
+            return self._c if self._key is not None and self._key[0] == ptrs else _PlanBufsC(*ptrs)
+        key = (ptrs, _dims_key(dims))
+        if key != self._key:
+            self.check(dims)
+            self._c, self._key = _PlanBufsC(*ptrs), key
+        return self._c
 
 
 def alloc_workspace(dims: Dims, device) -> torch.Tensor:
@@ -200,35 +253,36 @@ def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, str
     ``speeds`` (P host ints), mb_plan_weighted; with ``drift`` =
     (DriftParams, state tensor), mb_plan_drift; with ``repair``, mb_plan_ex
     (any of the three options)."""
-    assert ids.dtype == torch.int32 and ids.is_contiguous()
+    _check(ids, "ids", torch.int32, numel=dims.n_tokens * dims.top_k)
+    _check(ws, "ws")
+    cb = bufs.c_struct(dims)
+    sp = None if speeds is None else _speeds(dims, speeds)
+    if drift is not None:
+        prm, state = drift
+        _check(state, "drift state", nbytes=int(_lib.mb_drift_state_bytes(ctypes.byref(dims))))
     if repair:
-        sp = None if speeds is None else (ctypes.c_int32 * len(speeds))(*[int(v) for v in speeds])
         opt = _PlanOptionsC(ctypes.cast(sp, _i32p) if sp is not None else None,
                             ctypes.pointer(drift[0]) if drift else None,
                             _ptr(drift[1]) if drift else None, 1)
         rc = _lib.mb_plan_ex(ctypes.byref(dims), _ptr(ids), ctypes.byref(opt), _ptr(ws),
-                             ws.numel(), ctypes.byref(bufs.c_struct()), _stream(stream))
+                             _nbytes(ws), ctypes.byref(cb), _stream(stream))
         if rc != OK:
             raise MoebalError("mb_plan_ex", rc)
         return
     if drift is not None:
-        prm, state = drift
-        sp = None if speeds is None else (ctypes.c_int32 * len(speeds))(*[int(v) for v in speeds])
         rc = _lib.mb_plan_drift(ctypes.byref(dims), _ptr(ids), sp, ctypes.byref(prm), _ptr(state),
-                                _ptr(ws), ws.numel(), ctypes.byref(bufs.c_struct()),
-                                _stream(stream))
+                                _ptr(ws), _nbytes(ws), ctypes.byref(cb), _stream(stream))
         if rc != OK:
             raise MoebalError("mb_plan_drift", rc)
         return
-    if speeds is None:
-        rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), ws.numel(),
-                          ctypes.byref(bufs.c_struct()), _stream(stream))
+    if sp is None:
+        rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), _nbytes(ws), ctypes.byref(cb),
+                          _stream(stream))
         if rc != OK:
             raise MoebalError("mb_plan", rc)
         return
-    sp = (ctypes.c_int32 * len(speeds))(*[int(v) for v in speeds])
-    rc = _lib.mb_plan_weighted(ctypes.byref(dims), _ptr(ids), sp, _ptr(ws), ws.numel(),
-                               ctypes.byref(bufs.c_struct()), _stream(stream))
+    rc = _lib.mb_plan_weighted(ctypes.byref(dims), _ptr(ids), sp, _ptr(ws), _nbytes(ws),
+                               ctypes.byref(cb), _stream(stream))
     if rc != OK:
         raise MoebalError("mb_plan_weighted", rc)
 
@@ -237,8 +291,13 @@ def dispatch(dims: Dims, bufs: PlanBuffers, x: torch.Tensor, buf: torch.Tensor,
              x_scale: torch.Tensor | None = None, buf_scale: torch.Tensor | None = None,
              stream=None) -> None:
     """mb_dispatch: buf[pos[t][k]] = x[t] (and the fp8 scale rows)."""
-    assert x.is_contiguous() and buf.is_contiguous()
-    rc = _lib.mb_dispatch(ctypes.byref(dims), ctypes.byref(bufs.c_struct()), _ptr(x),
+    row = dims.hidden * ELT_BYTES.get(dims.dtype_in, 0)
+    _check(x, "x", nbytes=dims.n_tokens * row)
+    _check(buf, "buf", nbytes=dims.rows * row)
+    if dims.dtype_in == FP8_E4M3:
+        _check(x_scale, "x_scale", torch.float32, numel=dims.n_tokens * (dims.hidden // 128))
+        _check(buf_scale, "buf_scale", torch.float32, numel=dims.rows * (dims.hidden // 128))
+    rc = _lib.mb_dispatch(ctypes.byref(dims), ctypes.byref(bufs.c_struct(dims)), _ptr(x),
                           _ptr(x_scale), _ptr(buf), _ptr(buf_scale), _stream(stream))
     if rc != OK:
         raise MoebalError("mb_dispatch", rc)
@@ -247,9 +306,11 @@ def dispatch(dims: Dims, bufs: PlanBuffers, x: torch.Tensor, buf: torch.Tensor,
 def combine(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, w: torch.Tensor, y: torch.Tensor,
             stream=None) -> None:
     """mb_combine: y[t] = sum_k w[t][k] * y_exp[pos[t][k]] (fp32 accumulation)."""
-    assert y_exp.is_contiguous() and w.is_contiguous() and y.is_contiguous()
-    assert w.dtype == torch.float32
-    rc = _lib.mb_combine(ctypes.byref(dims), ctypes.byref(bufs.c_struct()), _ptr(y_exp), _ptr(w),
+    row = dims.hidden * ELT_BYTES.get(dims.dtype_out, 0)
+    _check(y_exp, "y_exp", nbytes=dims.rows * row)
+    _check(w, "w", torch.float32, numel=dims.n_tokens * dims.top_k)
+    _check(y, "y", nbytes=dims.n_tokens * row)
+    rc = _lib.mb_combine(ctypes.byref(dims), ctypes.byref(bufs.c_struct(dims)), _ptr(y_exp), _ptr(w),
                          _ptr(y), _stream(stream))
     if rc != OK:
         raise MoebalError("mb_combine", rc)
@@ -279,10 +340,11 @@ def combine_fp8(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, y_scale: tor
                 w: torch.Tensor, y: torch.Tensor, stream=None) -> None:
     """mb_combine_fp8: y[t] = sum_k w[t][k] * dequant(y_exp[pos[t][k]]) from
     fp8 e4m3 rows (uint8 [rows, H]) and fp32 scales [rows, H/128]."""
-    assert y_exp.dtype == torch.uint8 and y_scale.dtype == torch.float32
-    assert y_exp.is_contiguous() and y_scale.is_contiguous() and w.is_contiguous()
-    assert y.is_contiguous() and w.dtype == torch.float32
-    rc = _lib.mb_combine_fp8(ctypes.byref(dims), ctypes.byref(bufs.c_struct()), _ptr(y_exp),
+    _check(y_exp, "y_exp", torch.uint8, numel=dims.rows * dims.hidden)
+    _check(y_scale, "y_scale", torch.float32, numel=dims.rows * (dims.hidden // 128))
+    _check(w, "w", torch.float32, numel=dims.n_tokens * dims.top_k)
+    _check(y, "y", nbytes=dims.n_tokens * dims.hidden * ELT_BYTES.get(dims.dtype_out, 0))
+    rc = _lib.mb_combine_fp8(ctypes.byref(dims), ctypes.byref(bufs.c_struct(dims)), _ptr(y_exp),
                              _ptr(y_scale), _ptr(w), _ptr(y), _stream(stream))
     if rc != OK:
         raise MoebalError("mb_combine_fp8", rc)
@@ -292,6 +354,7 @@ def plan_status(bufs: PlanBuffers, stream=None):
     """mb_plan_status: [flags, T, max load, moves] on the host (synchronises)."""
     import numpy as np
 
+    _check(bufs.status, "status", torch.int32, numel=4)
     out = (ctypes.c_int32 * 4)()
     rc = _lib.mb_plan_status(ctypes.byref(bufs.c_struct()), _stream(stream), out)
     if rc != OK:
