@@ -51,6 +51,16 @@
  *    are in ascending token order; local slots are numbered home experts
  *    first (by id), then replica slots;
  *  - a rank needing more than cap rows sets CAPACITY and nothing is laid out.
+ *
+ * Pins (tests/test_oracle_pins.py, run without a GPU): numpy bincount for the
+ * counts, closed forms (one expert; uniform loads as a stable argsort),
+ * brute force and an LP for the locality of the assignment, exhaustive
+ * placements of the tiny workload, hand-derived worked examples, the E1
+ * table of [ISER], numpy for dispatch and combine, and planted mistakes that
+ * must fail them. Parity unpinned: the exact choices of the greedy, the
+ * drift gate and the quota repair follow the readings above, which no page
+ * illustrates with a worked example of its own; they are pinned only by the
+ * hand-derived examples, the invariants and the exhaustive bound.
  */
 #include "mbref.h"
 
