@@ -1,0 +1,84 @@
+"""Seeded random shapes, plan bit-exact against the oracle on the GPU.
+
+240 cases over rank counts 1..64 (both reduction widths of the register
+greedy), 1..40 home experts per rank (every register width and the LDS
+greedy), top-K up to 32, 0..4 replica slots, 1..700 tokens per rank, skewed
+and flat popularity, rank speeds on a third of the cases, and capacities from
+generous to too small (CAPACITY). Every fourth case also dispatches and
+combines small rows. Inputs come from ``workload``; expected values from the
+oracle only.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import token_dispatch_mb_amd as mb
+import workload as W
+from tests import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_required():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def fuzz_cases(n: int = 240, seed: int = 4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        P = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 24, 31, 32, 33, 48, 63, 64]))
+        eh = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 40]))
+        eh = max(1, min(eh, 1024 // P))
+        E = P * eh
+        K = int(min(E, 32, rng.choice([1, 2, 3, 4, 6, 8, 8, 8, 16, 32])))
+        R = int(rng.integers(0, 5))
+        S = int(rng.integers(1, 701))
+        S = max(1, min(S, (1 << 22) // (P * E)))  # keeps the routing draw small
+        noise = int(rng.choice([W.NOISE_NORMAL, W.NOISE_GUMBEL]))
+        zipf = float(rng.uniform(0.5, 1.5))
+        beta = float(rng.choice([0.0, 0.3, 1.0, 2.0]))
+        cap_kind = str(rng.choice(["tight", "double", "quad", "short"]))
+        speeds = None
+        if rng.random() < 1 / 3:
+            speeds = rng.integers(1, 9, P).astype(np.int32)
+        out.append((i, P, eh, K, R, S, noise, zipf, beta, cap_kind, speeds))
+    return out
+
+
+def test_random_shapes_plan_bit_exact():
+    n_rows = 0
+    for (i, P, eh, K, R, S, noise, zipf, beta, cap_kind, speeds) in fuzz_cases():
+        E, N = P * eh, P * S
+        cap = {"tight": S * K, "double": 2 * S * K, "quad": 4 * S * K,
+               "short": max(1, S * K - 1 - i % 5)}[cap_kind]
+        label = (f"fuzz {i}: P={P} Eh={eh} K={K} R={R} S={S} noise={noise} zipf={zipf:.2f} "
+                 f"beta={beta} cap={cap} speeds={None if speeds is None else speeds.tolist()}")
+        G.log(label)
+        ids, w = W.routing(N, E, K, noise, zipf, beta, 50000 + i)
+        H = 16
+        dg = mb.Dims.make(N, K, E, P, R, H, cap=cap, dtype_in="f32", dtype_out="f32")
+        od = O.make_dims(N, K, E, P, R, H, cap=cap, dtype_in="f32", dtype_out="f32")
+        sp = None if speeds is None else speeds.tolist()
+        gp = G.GpuPlan(dg).run(ids, speeds=sp)
+        got = gp.fetch()
+        ref = O.plan(od, ids, speeds=sp)
+        G.assert_plan_equal(got, ref)
+        if i % 4 == 0 and not ref.status[0] & O.ST_FATAL:
+            x = W.rows_f32(60000 + i, W.TAG_X, H, n=N)
+            ye = W.rows_f32(60000 + i, W.TAG_YEXP, H, n=P * cap)
+            buf, _, y = G.run_rows(dg, gp, x, None, ye, w)
+            ref_buf, _, _ = O.dispatch(od, ref, x, None)
+            used = ref.row_src >= 0
+            assert np.array_equal(buf[used], ref_buf[used]), label
+            y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, ye)
+            G.assert_combine_close(y, y_ref, mag, "f32")
+            n_rows += 1
+    assert n_rows > 20
