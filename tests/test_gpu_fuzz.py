@@ -82,3 +82,18 @@ def test_random_shapes_plan_bit_exact():
             G.assert_combine_close(y, y_ref, mag, "f32")
             n_rows += 1
     assert n_rows > 20
+
+
+def test_random_shapes_with_quota_repair_bit_exact():
+    """The same shapes planned with the pairwise quota repair (mb_plan_ex)."""
+    for (i, P, eh, K, R, S, noise, zipf, beta, cap_kind, speeds) in fuzz_cases()[::2]:
+        E, N = P * eh, P * S
+        cap = {"tight": S * K, "double": 2 * S * K, "quad": 4 * S * K,
+               "short": max(1, S * K - 1 - i % 5)}[cap_kind]
+        G.log(f"fuzz repair {i}: P={P} Eh={eh} K={K} R={R} S={S} cap={cap}")
+        ids, _ = W.routing(N, E, K, noise, zipf, beta, 50000 + i)
+        dg = mb.Dims.make(N, K, E, P, R, 16, cap=cap, dtype_in="f32", dtype_out="f32")
+        od = O.make_dims(N, K, E, P, R, 16, cap=cap, dtype_in="f32", dtype_out="f32")
+        sp = None if speeds is None else speeds.tolist()
+        got = G.GpuPlan(dg).run(ids, speeds=sp, repair=True).fetch()
+        G.assert_plan_equal(got, O.plan(od, ids, speeds=sp, repair=True))
