@@ -415,44 +415,49 @@ __device__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
   if (rank_lane)
     for (int i = 0; i < Eh; ++i) load += m.c[lane * Eh + i];
   const int lpre = load;
+  // x = load - tau per rank lane: a move needs its home above target
+  // (x_h > 0) and its host below (x_d < 0), and gives min(-x_d, quota).
+  int x = load - tau;
   wave_lds_sync();
   for (int base = 0; base < n_moves; base += 64) {
     const int i = base + lane;
-    int slot = 0, e = 0, dst = 0, h = 0;
-    bool ok = false;
+    int slot = 0, e = 0, dst = -1, h = 0;  // dst < 0: no move in this lane
     if (i < n_moves) {
       slot = m.order[i];
-      ok = (unsigned)slot < (unsigned)(P * R);
-      e = ok ? m.repE[slot] : 0;
-      ok = ok && (unsigned)e < (unsigned)a.E;
-      dst = ok ? slot / R : 0;
-      h = ok ? e / Eh : 0;
-      e = ok ? e : 0;
+      const bool ok_slot = (unsigned)slot < (unsigned)(P * R);
+      e = ok_slot ? m.repE[slot] : -1;
+      if (ok_slot && (unsigned)e < (unsigned)a.E) {
+        dst = slot / R;
+        h = e / Eh;
+      } else {
+        e = 0;
+      }
     }
+    const bool ok = dst >= 0;
     int q = ok ? m.qh[e] : 0;  // remaining home quota of this lane's expert
     int mine = 0;
     const int cnt = min(64, n_moves - base);
     for (int j = 0; j < cnt; ++j) {
       const int sd = __builtin_amdgcn_readlane(dst, j);
-      const int se = __builtin_amdgcn_readlane(e, j);
       const int sh = __builtin_amdgcn_readlane(h, j);
-      const int ld = __builtin_amdgcn_readlane(load, sd);
-      const int lh = __builtin_amdgcn_readlane(load, sh);
-      const int td = __builtin_amdgcn_readlane(tau, sd);
-      const int th = __builtin_amdgcn_readlane(tau, sh);
+      const int se = __builtin_amdgcn_readlane(e, j);
       const int qe = __builtin_amdgcn_readlane(q, j);
-      const bool okj = __builtin_amdgcn_readlane((int)ok, j) != 0;
-      const int mv = (okj && lh > th && ld < td) ? min(td - ld, qe) : 0;
+      const int xd = __builtin_amdgcn_readlane(x, sd & 63);
+      const int xh = __builtin_amdgcn_readlane(x, sh);
+      // no move unless the home is above target and the host below (q is
+      // 0 in lanes without a move)
+      const int mv = min(min(max(-xd, 0), qe), xh > 0 ? INT32_MAX : 0);
       mine = lane == j ? mv : mine;
       q -= (ok && e == se) ? mv : 0;
-      load += (lane == sd ? mv : 0) - (lane == sh ? mv : 0);
+      x += (lane == sd ? mv : 0) - (lane == sh ? mv : 0);
     }
-    if (i < n_moves && ok) {
+    if (ok) {
       m.repM[slot] = mine;
       m.qh[e] = q;  // lanes of one expert hold the same final quota
     }
     wave_lds_sync();
   }
+  load = x + tau;
   const int unbalanced = ballot64(rank_lane && load > tau) != 0;
   if (rank_lane) {
     m.loadv[lane] = load;
