@@ -5,8 +5,9 @@ greedy), 1..40 home experts per rank (every register width and the LDS
 greedy), top-K up to 32, 0..4 replica slots, 1..700 tokens per rank, skewed
 and flat popularity, rank speeds on a third of the cases, and capacities from
 generous to too small (CAPACITY). Every fourth case also dispatches and
-combines small rows. Inputs come from ``workload``; expected values from the
-oracle only.
+combines small rows; the same shapes again with the quota repair; and 40
+drift-gated sequences with random thresholds, windows and check intervals.
+Inputs come from ``workload``; expected values from the oracle only.
 """
 from __future__ import annotations
 
@@ -97,3 +98,48 @@ def test_random_shapes_with_quota_repair_bit_exact():
         sp = None if speeds is None else speeds.tolist()
         got = G.GpuPlan(dg).run(ids, speeds=sp, repair=True).fetch()
         G.assert_plan_equal(got, O.plan(od, ids, speeds=sp, repair=True))
+
+
+def test_random_drift_sequences_bit_exact():
+    """40 seeded drift-gated sequences of 6-14 calls: random shapes,
+    thresholds (including 0 and 1), windows, check intervals, popularity
+    changes, rank speeds and the quota repair on some; every call's plan and
+    the whole drift state after it equal the oracle's."""
+    rng = np.random.default_rng(777)
+    for n in range(40):
+        P = int(rng.choice([1, 2, 5, 16, 31, 32, 33, 64]))
+        eh = max(1, min(int(rng.choice([1, 2, 4, 8, 17, 40])), 1024 // P))
+        E = P * eh
+        K = int(min(E, rng.choice([1, 2, 4, 8])))
+        R = int(rng.integers(0, 4))
+        S = int(rng.integers(2, 120))
+        N = P * S
+        cap = 4 * S * K if R > 0 else N * K
+        num, den = [(0, 1), (1, 1), (1, 20), (3, 100), (1, 2)][int(rng.integers(0, 5))]
+        window, every = int(rng.integers(1, 6)), int(rng.integers(1, 5))
+        change = int(rng.integers(2, 6))
+        speeds = rng.integers(1, 5, P).tolist() if rng.random() < 0.3 else None
+        repair = bool(rng.random() < 0.25)
+        calls = int(rng.integers(6, 15))
+        label = (f"drift fuzz {n}: P={P} Eh={eh} K={K} R={R} S={S} delta={num}/{den} "
+                 f"window={window} every={every} change={change} speeds={speeds} repair={repair}")
+        G.log(label)
+        dg = mb.Dims.make(N, K, E, P, R, 16, cap=cap, dtype_in="f32", dtype_out="f32")
+        od = O.make_dims(N, K, E, P, R, 16, cap=cap, dtype_in="f32", dtype_out="f32")
+        state = mb.alloc_drift_state(dg, G.dev())
+        st = O.DriftState(E, P, R)
+        gprm = mb.DriftParams(num, den, window, every)
+        oprm = O.DriftParams(num, den, window, every)
+        gp = G.GpuPlan(dg)
+        for call in range(calls):
+            ids, _ = W.routing(N, E, K, W.NOISE_GUMBEL, 1.1, 1.0, 70000 + 100 * n + call,
+                               pop_seed=80000 + 100 * n + call // change)
+            got = gp.run(ids, speeds=speeds, drift=(gprm, state), repair=repair).fetch()
+            ref = O.plan(od, ids, speeds=speeds, drift=(oprm, st), repair=repair)
+            G.assert_plan_equal(got, ref)
+            h = mb.drift_header(state)
+            for key in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans"):
+                assert h[key] == getattr(st, key), (label, call, key, h[key], getattr(st, key))
+            assert h["last_d"] == st.last_d, (label, call, "last_d")
+            wsum = state[64:64 + 8 * E].cpu().numpy().view(np.int64)
+            assert np.array_equal(wsum, st.wsum), (label, call, "reference")
