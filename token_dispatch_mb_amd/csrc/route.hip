@@ -194,12 +194,21 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   }
   const HostEntry* hosts = kStageHosts ? hl : host_list;
   // Padding rows: region r has rows [r*cap + load_post[r], (r+1)*cap); with
-  // every region full (a balanced plan at cap = T) there are none.
+  // every region full (a balanced plan at cap = T) there are none. Global
+  // wave gw fills region gw mod P, the waves of one region interleaving in
+  // 64-row strides (or, with fewer waves than regions, wave gw fills
+  // regions gw, gw + GW, ...).
   if (__syncthreads_or(pad > 0)) {
-    for (int r = 0; r < P; ++r) {
+    const int GW = gridDim.x * kWaves, gw = b * kWaves + (tl >> 6), ln = tl & 63;
+    if (GW >= P) {
+      const int r = gw % P, k = gw / P, nk = (GW - 1 - r) / P + 1;  // waves r, r + P, ... < GW
       const int lp = lp_s[r];
-      for (int i = b * kTokensPerBlock + tl; i < cap - lp; i += gridDim.x * kTokensPerBlock)
-        row_src[r * cap + lp + i] = -1;
+      for (int i = k * 64 + ln; i < cap - lp; i += nk * 64) row_src[(size_t)r * cap + lp + i] = -1;
+    } else {
+      for (int r = gw; r < P; r += GW) {
+        const int lp = lp_s[r];
+        for (int i = ln; i < cap - lp; i += 64) row_src[(size_t)r * cap + lp + i] = -1;
+      }
     }
   }
   if (tl >= nt) return;
