@@ -38,7 +38,9 @@
  *    stated otherwise. The library never allocates or frees memory and keeps
  *    no state between calls; all calls except mb_plan_status only enqueue
  *    work on `stream` and return without waiting. Calls on different streams
- *    with disjoint buffers may run concurrently.
+ *    with disjoint buffers may run concurrently. Since they neither allocate
+ *    nor synchronise, mb_plan*, mb_dispatch and mb_combine* can be captured
+ *    in a HIP graph and replayed (a drift state then advances per replay).
  *  - All integers are int32, all arrays row-major and densely packed.
  *  - Host-detectable errors (bad sizes, null pointers, misaligned rows, a
  *    workspace that is too small) return a negative MB_ERR_* code and enqueue
