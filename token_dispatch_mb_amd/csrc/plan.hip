@@ -756,15 +756,21 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       if (e < E) m.c[e] = m.qh[e] = cv[u];
     }
   } else {
+    // Every source's count of the thread's expert in flight at once; the
+    // address advances in a vector register (kept there by the empty asm),
+    // so the row offsets are not all held in scalar registers.
     for (int e = tid; e < E; e += kPlanThreads) {
-      int c = 0;
-      for (int s0 = 0; s0 < P; s0 += 32) {  // 32 independent loads in flight
-        int v[32];
+      const int32_t* col = a.counts + e;
+      int v[kMaxRanks];
 #pragma unroll
-        for (int q = 0; q < 32; ++q) v[q] = s0 + q < P ? a.counts[(size_t)(s0 + q) * E + e] : 0;
-#pragma unroll
-        for (int q = 0; q < 32; ++q) c += v[q];
+      for (int q = 0; q < kMaxRanks; ++q) {
+        v[q] = q < P ? *col : 0;
+        col += E;
+        __asm__ volatile("" : "+v"(col));
       }
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < kMaxRanks; ++q) c += v[q];
       m.c[e] = m.qh[e] = c;
     }
   }
