@@ -69,10 +69,12 @@ static int validate(const mb_dims* d) {
   if ((int64_t)d->hidden * bin % 16 || (int64_t)d->hidden * elt_bytes(d->dtype_out) % 16)
     return MB_ERR_INVALID_ARG;
   if ((int64_t)d->hidden * bin / 16 > INT32_MAX) return MB_ERR_INVALID_ARG;
-  // dispatch and combine run one wave per 1 KiB part of every token row
+  // dispatch runs one wave per 1 KiB part of every token row, the combines
+  // one per 512 bytes of output row (at least as many as per 512 fp8
+  // elements of an expert row, which the fp8 combine uses)
   if ((int64_t)d->n_tokens * (((int64_t)d->hidden * bin / 16 + 63) / 64) > INT32_MAX)
     return MB_ERR_INVALID_ARG;
-  if ((int64_t)d->n_tokens * (((int64_t)d->hidden * elt_bytes(d->dtype_out) / 16 + 63) / 64) >
+  if ((int64_t)d->n_tokens * (((int64_t)d->hidden * elt_bytes(d->dtype_out) / 8 + 63) / 64) >
       INT32_MAX)
     return MB_ERR_INVALID_ARG;
   if (d->dtype_in == MB_FP8_E4M3 && d->hidden % 128) return MB_ERR_INVALID_ARG;

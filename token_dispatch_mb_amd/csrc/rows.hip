@@ -1,10 +1,11 @@
 // rows.hip — row dispatch (scatter) and combine (weighted gather-reduce).
 //
-// The kernels are HBM-bound byte movers: one wave64 per 1 KiB part of a
-// token's row, every lane moving 16-byte chunks (global_load/store_dwordx4),
-// a token's parts on consecutive waves. The cache hint of each access
-// (temporal or nontemporal) is the one measured fastest on MI355X for that
-// kernel's traffic mix; see the comment at each kernel.
+// The kernels are HBM-bound byte movers: one wave64 per part of a token's
+// row, a token's parts on consecutive waves; dispatch moves 1 KiB parts in
+// 16-byte lane chunks (global_load/store_dwordx4), the combines 512-byte
+// parts in 8-byte lane chunks. The part size and the cache hint of each
+// access (temporal or nontemporal) are the ones measured fastest on MI355X
+// for that kernel's traffic mix; see the comment at each kernel.
 //
 // Dispatch reads each token row once and stores it to its K rows (the
 // one-GPU form of "a token's experts on one node share a transfer" in the
@@ -37,8 +38,9 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // the chunks of a token on consecutive waves; each wave loads its chunk once
 // and stores it to the token's K rows. On MI355X this shape moved the
 // 1-read / K-write traffic faster than a wave holding a whole row (many small
-// waves keep more independent store streams in flight), and plain (temporal)
-// loads and stores beat nontemporal ones here.
+// waves keep more independent store streams in flight) and 3 % faster than
+// 512-byte chunks, and plain (temporal) loads and stores beat nontemporal
+// ones here.
 template <int KT>
 __global__ __launch_bounds__(kRowThreads) void k_dispatch(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos,
@@ -82,49 +84,53 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
-// acc[0..7] += w * (8 bf16 of v), or acc[0..3] += w * (4 f32 of v).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// acc[0..3] += w * (4 bf16 of v), or acc[0..1] += w * (2 f32 of v).
 template <bool kBF16>
-__device__ __forceinline__ void fma_row(float* acc, float w, u32x4 v) {
+__device__ __forceinline__ void fma_chunk(float* acc, float w, u32x2 v) {
   if constexpr (kBF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
       acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xffff0000u), acc[2 * i + 1]);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, __uint_as_float(v[i]), acc[i]);
+    for (int i = 0; i < 2; ++i) acc[i] = fmaf(w, __uint_as_float(v[i]), acc[i]);
   }
 }
 
+// 4 accumulators to bf16 pairs, or 2 to f32.
 template <bool kBF16>
-__device__ __forceinline__ u32x4 pack_row(const float* acc) {
-  u32x4 o;
+__device__ __forceinline__ u32x2 pack_chunk(const float* acc) {
+  u32x2 o;
   if constexpr (kBF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
       o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+    for (int i = 0; i < 2; ++i) o[i] = __float_as_uint(acc[i]);
   }
   return o;
 }
 
-// Combine: one wave per 1 KiB part of a token's output row (64 lanes x 16
+// Combine: one wave per 512-byte part of a token's output row (64 lanes x 8
 // bytes), the parts of a token on consecutive waves; each lane reads its
-// 16-byte chunk of the token's K expert rows, accumulates w[t][k] * value in
+// 8-byte chunk of the token's K expert rows, accumulates w[t][k] * value in
 // fp32 in k order and stores the chunk once. With a compile-time K the K
-// loads are issued before the first FMA. On MI355X this shape (many small
-// waves) moved the K-read / 1-write traffic 2 % faster than a wave holding a
-// token's whole row with all K x 14 loads in flight, and nontemporal loads
-// and stores beat temporal ones for it.
+// loads are issued before the first FMA. On MI355X, 8-byte lane chunks moved
+// the K-read / 1-write traffic 3 % faster than 16-byte chunks (2.89 against
+// 2.99 ms at 131072 tokens x top-8 x 7168 bf16) and 2 % faster than 4-byte
+// chunks; waves of 16-byte chunks had in turn beaten one wave per whole row
+// by 2 %, and nontemporal loads and stores beat temporal ones.
 template <int KT, bool kBF16>
 __global__ __launch_bounds__(kCombThreads) void k_combine(
-    const u32x4* __restrict__ ye, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    const int32_t* __restrict__ status, u32x4* __restrict__ y, int N, int K_, int rb16, int wpt,
+    const u32x2* __restrict__ ye, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    const int32_t* __restrict__ status, u32x2* __restrict__ y, int N, int K_, int rc8, int wpt,
     int rows) {
-  constexpr int EPC = kBF16 ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int EPC = kBF16 ? 4 : 2;  // elements per 8-byte chunk
   const int K = KT ? KT : K_;
   const int lane = threadIdx.x & 63;
   const int gw = uniform(blockIdx.x * kWavesPerCombBlock + (threadIdx.x >> 6));
@@ -132,43 +138,43 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
   const int ci = part * 64 + lane;  // this lane's chunk of the row
-  if (ci >= rb16) return;
+  if (ci >= rc8) return;
   const int32_t* pt = pos + (size_t)t * K;
   const float* wt = w + (size_t)t * K;
   float acc[EPC];
 #pragma unroll
   for (int i = 0; i < EPC; ++i) acc[i] = 0.0f;
   if constexpr (KT > 0) {
-    u32x4 v[KT];
+    u32x2 v[KT];
     bool ok[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       const int p = pt[k];
       ok[k] = (unsigned)p < (unsigned)rows;  // only a broken plan fails this
-      v[k] = __builtin_nontemporal_load(ye + (ok[k] ? (size_t)p : 0) * rb16 + ci);
+      v[k] = __builtin_nontemporal_load(ye + (ok[k] ? (size_t)p : 0) * rc8 + ci);
     }
 #pragma unroll
     for (int k = 0; k < KT; ++k)
-      if (ok[k]) fma_row<kBF16>(acc, wt[k], v[k]);
+      if (ok[k]) fma_chunk<kBF16>(acc, wt[k], v[k]);
   } else {
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
       if ((unsigned)p >= (unsigned)rows) continue;  // a row outside the buffer adds nothing
-      fma_row<kBF16>(acc, wt[k], __builtin_nontemporal_load(ye + (size_t)p * rb16 + ci));
+      fma_chunk<kBF16>(acc, wt[k], __builtin_nontemporal_load(ye + (size_t)p * rc8 + ci));
     }
   }
-  __builtin_nontemporal_store(pack_row<kBF16>(acc), y + (size_t)t * rb16 + ci);
+  __builtin_nontemporal_store(pack_chunk<kBF16>(acc), y + (size_t)t * rc8 + ci);
 }
 
 // ---- dequantising combine: fp8 e4m3 expert outputs, fp32 scale per 128 -----
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// acc[0..15] += ws * (16 e4m3 values of v), ws = w * the chunk's scale; the
+// acc[0..7] += ws * (8 e4m3 values of v), ws = w * the chunk's scale; the
 // hardware conversion decodes OCP e4m3fn exactly (two bytes per call).
-__device__ __forceinline__ void fma_fp8(float* acc, float ws, u32x4 v) {
+__device__ __forceinline__ void fma_fp8(float* acc, float ws, u32x2 v) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
     const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
     acc[4 * i] = fmaf(ws, lo.x, acc[4 * i]);
@@ -178,57 +184,65 @@ __device__ __forceinline__ void fma_fp8(float* acc, float ws, u32x4 v) {
   }
 }
 
-// 16 accumulators to the output row: 2 chunks of bf16 or 4 of fp32.
+// 8 accumulators to the output row: one 16-byte chunk of bf16 (chunk ci of
+// the row) or two of fp32 (chunks 2 ci, 2 ci + 1).
 template <bool kBF16>
-__device__ __forceinline__ void store_fp8_piece(const float* acc, u32x4* __restrict__ dst) {
+__device__ __forceinline__ void store_fp8_piece(const float* acc, u32x4* __restrict__ y, size_t ci) {
   if constexpr (kBF16) {
-    __builtin_nontemporal_store(pack_row<true>(acc), dst);
-    __builtin_nontemporal_store(pack_row<true>(acc + 8), dst + 1);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+    __builtin_nontemporal_store(o, y + ci);
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(pack_row<false>(acc + 4 * j), dst + j);
+    for (int j = 0; j < 2; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[4 * j + i]);
+      __builtin_nontemporal_store(o, y + 2 * ci + j);
+    }
   }
 }
 
 // Dequantising combine: y[t][i] = sum_k w[t][k] * e4m3(y_exp[p][i]) *
 // scale[p][i/128], accumulated in fp32 in k order as fma(w * scale, value,
-// acc). One wave per 1 KiB part of a token's fp8 row (64 lanes x 16
-// elements, each lane's 16 under one scale: chunk c uses scale c / 8), the
-// parts of a token on consecutive waves, as in k_dispatch: with rows half
-// the bytes of bf16, small waves (16 accumulators per lane) keep more loads
-// in flight per CU than a wave holding a whole row. With a compile-time K
-// the K loads of a part are issued before the first FMA.
+// acc). One wave per 512-element part of a token's fp8 row (64 lanes x 8
+// elements, each lane's 8 under one scale: chunk c uses scale c / 16), the
+// parts of a token on consecutive waves. On MI355X 8 elements per lane ran
+// 23 % faster than 16 (96 against 125 us for 8192 tokens x top-8 x 7168) and
+// 10 % faster than 4: small waves with few accumulators keep the most loads
+// in flight. With a compile-time K the K loads of a part are issued before
+// the first FMA.
 template <int KT, bool kBF16>
 __global__ __launch_bounds__(kCombThreads) void k_combine_fp8(
-    const u32x4* __restrict__ ye, const float* __restrict__ ys, const int32_t* __restrict__ pos,
+    const u32x2* __restrict__ ye, const float* __restrict__ ys, const int32_t* __restrict__ pos,
     const float* __restrict__ w, const int32_t* __restrict__ status, u32x4* __restrict__ y,
-    int N, int K_, int rb16, int wpt, int rows) {
-  constexpr int OPC = kBF16 ? 2 : 4;  // output chunks per input chunk
+    int N, int K_, int rc8, int wpt, int rows) {
   const int K = KT ? KT : K_;
-  const int nsc = rb16 / 8;  // scales per row
+  const int nsc = rc8 / 16;  // scales per row
   const int lane = threadIdx.x & 63;
   const int gw = uniform(blockIdx.x * kWavesPerCombBlock + (threadIdx.x >> 6));
   const int t = gw / wpt, part = gw - t * wpt;
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
   const int ci = part * 64 + lane;  // this lane's chunk of the row
-  if (ci >= rb16) return;
+  if (ci >= rc8) return;
   const int32_t* pt = pos + (size_t)t * K;
   const float* wt = w + (size_t)t * K;
-  float acc[16];
+  float acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   if constexpr (KT > 0) {
-    int p[KT];
-    u32x4 v[KT];
+    u32x2 v[KT];
     float s[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      p[k] = pt[k];
-      const bool ok = (unsigned)p[k] < (unsigned)rows;  // only a broken plan fails this
-      const size_t row = ok ? (size_t)p[k] : 0;
-      v[k] = __builtin_nontemporal_load(ye + row * rb16 + ci);
-      s[k] = ok ? ys[row * nsc + (ci >> 3)] : 0.0f;
+      const int p = pt[k];
+      const bool ok = (unsigned)p < (unsigned)rows;  // only a broken plan fails this
+      const size_t row = ok ? (size_t)p : 0;
+      v[k] = __builtin_nontemporal_load(ye + row * rc8 + ci);
+      s[k] = ok ? ys[row * nsc + (ci >> 4)] : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < KT; ++k) fma_fp8(acc, wt[k] * s[k], v[k]);
@@ -236,11 +250,11 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_fp8(
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
       if ((unsigned)p >= (unsigned)rows) continue;
-      fma_fp8(acc, wt[k] * ys[(size_t)p * nsc + (ci >> 3)],
-              __builtin_nontemporal_load(ye + (size_t)p * rb16 + ci));
+      fma_fp8(acc, wt[k] * ys[(size_t)p * nsc + (ci >> 4)],
+              __builtin_nontemporal_load(ye + (size_t)p * rc8 + ci));
     }
   }
-  store_fp8_piece<kBF16>(acc, y + ((size_t)t * rb16 + ci) * OPC);
+  store_fp8_piece<kBF16>(acc, y, (size_t)t * rc8 + ci);
 }
 
 }  // namespace
@@ -261,14 +275,14 @@ hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* 
 }
 
 template <bool kBF16>
-static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x4* ye,
-                             const float* w, u32x4* yy, int rb16, int rows, hipStream_t st) {
-  const int wpt = (rb16 + 63) / 64;  // waves per token
+static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x2* ye,
+                             const float* w, u32x2* yy, int rc8, int rows, hipStream_t st) {
+  const int wpt = (rc8 + 63) / 64;  // waves per token
   const int64_t waves = (int64_t)d.n_tokens * wpt;
   const dim3 grid((unsigned)((waves + kWavesPerCombBlock - 1) / kWavesPerCombBlock));
 #define MB_C(KT)                                                                          \
   hipLaunchKernelGGL((k_combine<KT, kBF16>), grid, dim3(kCombThreads), 0, st, ye, o.pos, w, \
-                     o.status, yy, d.n_tokens, d.top_k, rb16, wpt, rows)
+                     o.status, yy, d.n_tokens, d.top_k, rc8, wpt, rows)
   switch (d.top_k) {
     case 1: MB_C(1); break;
     case 2: MB_C(2); break;
@@ -280,15 +294,15 @@ static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x
 }
 
 template <bool kBF16>
-static void launch_combine_fp8_t(const mb_dims& d, const mb_plan_bufs& o, const u32x4* ye,
-                                 const float* ys, const float* w, u32x4* yy, int rb16, int rows,
+static void launch_combine_fp8_t(const mb_dims& d, const mb_plan_bufs& o, const u32x2* ye,
+                                 const float* ys, const float* w, u32x4* yy, int rc8, int rows,
                                  hipStream_t st) {
-  const int wpt = (rb16 + 63) / 64;  // waves per token
+  const int wpt = (rc8 + 63) / 64;  // waves per token
   const int64_t waves = (int64_t)d.n_tokens * wpt;
   const dim3 grid((unsigned)((waves + kWavesPerCombBlock - 1) / kWavesPerCombBlock));
 #define MB_C(KT)                                                                             \
   hipLaunchKernelGGL((k_combine_fp8<KT, kBF16>), grid, dim3(kCombThreads), 0, st, ye, ys, o.pos, \
-                     w, o.status, yy, d.n_tokens, d.top_k, rb16, wpt, rows)
+                     w, o.status, yy, d.n_tokens, d.top_k, rc8, wpt, rows)
   switch (d.top_k) {
     case 1: MB_C(1); break;
     case 2: MB_C(2); break;
@@ -302,28 +316,28 @@ static void launch_combine_fp8_t(const mb_dims& d, const mb_plan_bufs& o, const 
 hipError_t launch_combine_fp8(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
                               const float* y_scale, const float* w, void* y, hipStream_t st) {
   if (d.n_tokens == 0) return hipSuccess;
-  const int rb16 = d.hidden / 16;  // 16 fp8 elements per chunk
+  const int rc8 = d.hidden / 8;  // 8 fp8 elements per chunk
   const int rows = d.n_ranks * d.cap;
-  const u32x4* ye = static_cast<const u32x4*>(y_exp);
+  const u32x2* ye = static_cast<const u32x2*>(y_exp);
   u32x4* yy = static_cast<u32x4*>(y);
   if (d.dtype_out == MB_BF16)
-    launch_combine_fp8_t<true>(d, o, ye, y_scale, w, yy, rb16, rows, st);
+    launch_combine_fp8_t<true>(d, o, ye, y_scale, w, yy, rc8, rows, st);
   else
-    launch_combine_fp8_t<false>(d, o, ye, y_scale, w, yy, rb16, rows, st);
+    launch_combine_fp8_t<false>(d, o, ye, y_scale, w, yy, rc8, rows, st);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
                           const float* w, void* y, hipStream_t st) {
   if (d.n_tokens == 0) return hipSuccess;
-  const int rb16 = (int)(d.hidden * elt_bytes(d.dtype_out) / 16);
+  const int rc8 = (int)(d.hidden * elt_bytes(d.dtype_out) / 8);
   const int rows = d.n_ranks * d.cap;
-  const u32x4* ye = static_cast<const u32x4*>(y_exp);
-  u32x4* yy = static_cast<u32x4*>(y);
+  const u32x2* ye = static_cast<const u32x2*>(y_exp);
+  u32x2* yy = static_cast<u32x2*>(y);
   if (d.dtype_out == MB_BF16)
-    launch_combine_t<true>(d, o, ye, w, yy, rb16, rows, st);
+    launch_combine_t<true>(d, o, ye, w, yy, rc8, rows, st);
   else
-    launch_combine_t<false>(d, o, ye, w, yy, rb16, rows, st);
+    launch_combine_t<false>(d, o, ye, w, yy, rc8, rows, st);
   return hipGetLastError();
 }
 
