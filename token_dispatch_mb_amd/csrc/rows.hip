@@ -17,6 +17,8 @@
 // into fixed-shape expert-grouped buffers, kernels indexing rows through the
 // planner's layout); Zepp summary §4.2 (Merge: dispatch shares a token's
 // transfer, combine aggregates a token's expert outputs).
+#include <type_traits>
+
 #include "mb_internal.h"
 
 namespace mb {
@@ -86,51 +88,58 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// acc[0..3] += w * (4 bf16 of v), or acc[0..1] += w * (2 f32 of v).
-template <bool kBF16>
-__device__ __forceinline__ void fma_chunk(float* acc, float w, u32x2 v) {
+// A lane chunk of CW dwords (8 or 16 bytes).
+template <int CW>
+using chunk_t = typename std::conditional<CW == 4, u32x4, u32x2>::type;
+
+// acc[0..2CW) += w * (2 CW bf16 of v), or acc[0..CW) += w * (CW f32 of v).
+template <bool kBF16, int CW>
+__device__ __forceinline__ void fma_chunk(float* acc, float w, chunk_t<CW> v) {
   if constexpr (kBF16) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < CW; ++i) {
       acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
       acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xffff0000u), acc[2 * i + 1]);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i] = fmaf(w, __uint_as_float(v[i]), acc[i]);
+    for (int i = 0; i < CW; ++i) acc[i] = fmaf(w, __uint_as_float(v[i]), acc[i]);
   }
 }
 
-// 4 accumulators to bf16 pairs, or 2 to f32.
-template <bool kBF16>
-__device__ __forceinline__ u32x2 pack_chunk(const float* acc) {
-  u32x2 o;
+// The accumulators of one chunk to bf16 pairs or f32.
+template <bool kBF16, int CW>
+__device__ __forceinline__ chunk_t<CW> pack_chunk(const float* acc) {
+  chunk_t<CW> o;
   if constexpr (kBF16) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < CW; ++i)
       o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) o[i] = __float_as_uint(acc[i]);
+    for (int i = 0; i < CW; ++i) o[i] = __float_as_uint(acc[i]);
   }
   return o;
 }
 
-// Combine: one wave per 512-byte part of a token's output row (64 lanes x 8
-// bytes), the parts of a token on consecutive waves; each lane reads its
-// 8-byte chunk of the token's K expert rows, accumulates w[t][k] * value in
+// Combine: one wave per part of a token's output row (64 lanes x one chunk
+// of CW dwords), the parts of a token on consecutive waves; each lane reads
+// its chunk of the token's K expert rows, accumulates w[t][k] * value in
 // fp32 in k order and stores the chunk once. With a compile-time K the K
-// loads are issued before the first FMA. On MI355X, 8-byte lane chunks moved
-// the K-read / 1-write traffic 3 % faster than 16-byte chunks (2.89 against
-// 2.99 ms at 131072 tokens x top-8 x 7168 bf16) and 2 % faster than 4-byte
-// chunks; waves of 16-byte chunks had in turn beaten one wave per whole row
-// by 2 %, and nontemporal loads and stores beat temporal ones.
-template <int KT, bool kBF16>
+// loads are issued before the first FMA. Measured on MI355X: with K = 8,
+// 8-byte chunks (512-byte parts) moved the K-read / 1-write traffic faster
+// than 16-byte chunks (2.71-2.89 against 2.99 ms at 131072 tokens x top-8 x
+// 7168 bf16; 170 against 183 us at 8192 tokens x 8) and 4-byte chunks; with
+// K = 2, 16-byte chunks are faster (20.8 against 22.5 us at 4096 tokens x 2
+// x 4096), a wave with only two loads needing the wider chunk. Waves of
+// 16-byte chunks had in turn beaten one wave per whole row, and nontemporal
+// loads and stores beat temporal ones.
+template <int KT, bool kBF16, int CW>
 __global__ __launch_bounds__(kCombThreads) void k_combine(
-    const u32x2* __restrict__ ye, const int32_t* __restrict__ pos, const float* __restrict__ w,
-    const int32_t* __restrict__ status, u32x2* __restrict__ y, int N, int K_, int rc8, int wpt,
-    int rows) {
-  constexpr int EPC = kBF16 ? 4 : 2;  // elements per 8-byte chunk
+    const chunk_t<CW>* __restrict__ ye, const int32_t* __restrict__ pos,
+    const float* __restrict__ w, const int32_t* __restrict__ status, chunk_t<CW>* __restrict__ y,
+    int N, int K_, int rc, int wpt, int rows) {
+  constexpr int EPC = kBF16 ? 2 * CW : CW;  // elements per chunk
   const int K = KT ? KT : K_;
   const int lane = threadIdx.x & 63;
   const int gw = uniform(blockIdx.x * kWavesPerCombBlock + (threadIdx.x >> 6));
@@ -138,32 +147,32 @@ __global__ __launch_bounds__(kCombThreads) void k_combine(
   if (t >= N) return;
   if (status[0] & MB_ST_FATAL) return;
   const int ci = part * 64 + lane;  // this lane's chunk of the row
-  if (ci >= rc8) return;
+  if (ci >= rc) return;
   const int32_t* pt = pos + (size_t)t * K;
   const float* wt = w + (size_t)t * K;
   float acc[EPC];
 #pragma unroll
   for (int i = 0; i < EPC; ++i) acc[i] = 0.0f;
   if constexpr (KT > 0) {
-    u32x2 v[KT];
+    chunk_t<CW> v[KT];
     bool ok[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       const int p = pt[k];
       ok[k] = (unsigned)p < (unsigned)rows;  // only a broken plan fails this
-      v[k] = __builtin_nontemporal_load(ye + (ok[k] ? (size_t)p : 0) * rc8 + ci);
+      v[k] = __builtin_nontemporal_load(ye + (ok[k] ? (size_t)p : 0) * rc + ci);
     }
 #pragma unroll
     for (int k = 0; k < KT; ++k)
-      if (ok[k]) fma_chunk<kBF16>(acc, wt[k], v[k]);
+      if (ok[k]) fma_chunk<kBF16, CW>(acc, wt[k], v[k]);
   } else {
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
       if ((unsigned)p >= (unsigned)rows) continue;  // a row outside the buffer adds nothing
-      fma_chunk<kBF16>(acc, wt[k], __builtin_nontemporal_load(ye + (size_t)p * rc8 + ci));
+      fma_chunk<kBF16, CW>(acc, wt[k], __builtin_nontemporal_load(ye + (size_t)p * rc + ci));
     }
   }
-  __builtin_nontemporal_store(pack_chunk<kBF16>(acc), y + (size_t)t * rc8 + ci);
+  __builtin_nontemporal_store(pack_chunk<kBF16, CW>(acc), y + (size_t)t * rc + ci);
 }
 
 // ---- dequantising combine: fp8 e4m3 expert outputs, fp32 scale per 128 -----
@@ -274,15 +283,18 @@ hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* 
   return hipGetLastError();
 }
 
-template <bool kBF16>
-static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const u32x2* ye,
-                             const float* w, u32x2* yy, int rc8, int rows, hipStream_t st) {
-  const int wpt = (rc8 + 63) / 64;  // waves per token
+template <bool kBF16, int CW>
+static void launch_combine_t(const mb_dims& d, const mb_plan_bufs& o, const void* ye,
+                             const float* w, void* yy, int rows, hipStream_t st) {
+  const int rc = (int)(d.hidden * elt_bytes(d.dtype_out) / (4 * CW));  // chunks per row
+  const int wpt = (rc + 63) / 64;                                      // waves per token
   const int64_t waves = (int64_t)d.n_tokens * wpt;
   const dim3 grid((unsigned)((waves + kWavesPerCombBlock - 1) / kWavesPerCombBlock));
-#define MB_C(KT)                                                                          \
-  hipLaunchKernelGGL((k_combine<KT, kBF16>), grid, dim3(kCombThreads), 0, st, ye, o.pos, w, \
-                     o.status, yy, d.n_tokens, d.top_k, rc8, wpt, rows)
+  const auto* src = static_cast<const chunk_t<CW>*>(ye);
+  auto* dst = static_cast<chunk_t<CW>*>(yy);
+#define MB_C(KT)                                                                                 \
+  hipLaunchKernelGGL((k_combine<KT, kBF16, CW>), grid, dim3(kCombThreads), 0, st, src, o.pos, w, \
+                     o.status, dst, d.n_tokens, d.top_k, rc, wpt, rows)
   switch (d.top_k) {
     case 1: MB_C(1); break;
     case 2: MB_C(2); break;
@@ -330,14 +342,20 @@ hipError_t launch_combine_fp8(const mb_dims& d, const mb_plan_bufs& o, const voi
 hipError_t launch_combine(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,
                           const float* w, void* y, hipStream_t st) {
   if (d.n_tokens == 0) return hipSuccess;
-  const int rc8 = (int)(d.hidden * elt_bytes(d.dtype_out) / 8);
   const int rows = d.n_ranks * d.cap;
-  const u32x2* ye = static_cast<const u32x2*>(y_exp);
-  u32x2* yy = static_cast<u32x2*>(y);
-  if (d.dtype_out == MB_BF16)
-    launch_combine_t<true>(d, o, ye, w, yy, rc8, rows, st);
-  else
-    launch_combine_t<false>(d, o, ye, w, yy, rc8, rows, st);
+  // 16-byte lane chunks for K <= 2, 8-byte chunks for more rows per token
+  const bool wide = d.top_k <= 2;
+  if (d.dtype_out == MB_BF16) {
+    if (wide)
+      launch_combine_t<true, 4>(d, o, y_exp, w, y, rows, st);
+    else
+      launch_combine_t<true, 2>(d, o, y_exp, w, y, rows, st);
+  } else {
+    if (wide)
+      launch_combine_t<false, 4>(d, o, y_exp, w, y, rows, st);
+    else
+      launch_combine_t<false, 2>(d, o, y_exp, w, y, rows, st);
+  }
   return hipGetLastError();
 }
 
