@@ -54,6 +54,9 @@ def test_workspace_bytes_host_only():
     ((64, 2, 16, 4, -1, 128), 32),     # R < 0
     ((64, 2, 16, 4, 1, 128), 0),       # cap = 0
     ((64, 2, 16, 4, 1, 4), 32),        # bf16 row of 8 bytes
+    ((1 << 28, 8, 16, 4, 1, 128), 32),  # N * K > INT32_MAX pairs
+    # 2^23 tokens of 65536 bf16: 2^30 dispatch waves fit an int32, 2^31 combine waves do not
+    ((1 << 23, 1, 4, 1, 1, 65536), 1 << 23),
 ])
 def test_invalid_sizes_rejected_on_host(args, cap):
     d = mb.Dims.make(*args, cap=cap)
