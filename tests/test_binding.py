@@ -59,3 +59,13 @@ def test_host_rows_are_refused():
     with pytest.raises(ValueError, match="GPU tensor"):
         mb.combine(d, _host_bufs(d), torch.zeros(d.rows, 128, dtype=torch.bfloat16),
                    torch.zeros(64, 2), x)
+
+
+def test_tensors_on_another_device_than_the_stream_are_refused():
+    class _Stream:  # stands in for a torch stream on GPU 1
+        device = torch.device("cuda", 1)
+        cuda_stream = 0
+
+    with pytest.raises(ValueError, match="the stream on cuda:1"):
+        mb._stream(_Stream(), torch.zeros(4))
+    assert mb._stream(_Stream(), None).value is None

@@ -186,9 +186,16 @@ def _dims_key(dims: "Dims") -> tuple:
     return tuple(getattr(dims, n) for n, _ in Dims._fields_)
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, *tensors) -> ctypes.c_void_p:
+    """The stream's HIP handle (torch's current stream by default), after
+    checking that the given tensors live on the stream's GPU (a pointer into
+    another GPU's memory would fault in the kernel)."""
     if stream is None:
         stream = torch.cuda.current_stream()
+    dev = stream.device
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError(f"a tensor is on {t.device}, the stream on {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -226,6 +233,8 @@ class PlanBuffers:
                 "row_src": dims.rows, "status": 4}
         for name, n in need.items():
             _check(getattr(self, name), name, torch.int32, numel=n)
+            if getattr(self, name).device != self.status.device:
+                raise ValueError(f"{name} is on another GPU than status")
 
     def c_struct(self, dims: Dims | None = None) -> _PlanBufsC:
         """The mb_plan_bufs of these tensors; with `dims`, checked against
@@ -260,29 +269,29 @@ def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, str
     if drift is not None:
         prm, state = drift
         _check(state, "drift state", nbytes=int(_lib.mb_drift_state_bytes(ctypes.byref(dims))))
+    st = _stream(stream, ids, ws, bufs.status, drift[1] if drift is not None else None)
     if repair:
         opt = _PlanOptionsC(ctypes.cast(sp, _i32p) if sp is not None else None,
                             ctypes.pointer(drift[0]) if drift else None,
                             _ptr(drift[1]) if drift else None, 1)
         rc = _lib.mb_plan_ex(ctypes.byref(dims), _ptr(ids), ctypes.byref(opt), _ptr(ws),
-                             _nbytes(ws), ctypes.byref(cb), _stream(stream))
+                             _nbytes(ws), ctypes.byref(cb), st)
         if rc != OK:
             raise MoebalError("mb_plan_ex", rc)
         return
     if drift is not None:
         rc = _lib.mb_plan_drift(ctypes.byref(dims), _ptr(ids), sp, ctypes.byref(prm), _ptr(state),
-                                _ptr(ws), _nbytes(ws), ctypes.byref(cb), _stream(stream))
+                                _ptr(ws), _nbytes(ws), ctypes.byref(cb), st)
         if rc != OK:
             raise MoebalError("mb_plan_drift", rc)
         return
     if sp is None:
-        rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), _nbytes(ws), ctypes.byref(cb),
-                          _stream(stream))
+        rc = _lib.mb_plan(ctypes.byref(dims), _ptr(ids), _ptr(ws), _nbytes(ws), ctypes.byref(cb), st)
         if rc != OK:
             raise MoebalError("mb_plan", rc)
         return
     rc = _lib.mb_plan_weighted(ctypes.byref(dims), _ptr(ids), sp, _ptr(ws), _nbytes(ws),
-                               ctypes.byref(cb), _stream(stream))
+                               ctypes.byref(cb), st)
     if rc != OK:
         raise MoebalError("mb_plan_weighted", rc)
 
@@ -298,7 +307,8 @@ def dispatch(dims: Dims, bufs: PlanBuffers, x: torch.Tensor, buf: torch.Tensor,
         _check(x_scale, "x_scale", torch.float32, numel=dims.n_tokens * (dims.hidden // 128))
         _check(buf_scale, "buf_scale", torch.float32, numel=dims.rows * (dims.hidden // 128))
     rc = _lib.mb_dispatch(ctypes.byref(dims), ctypes.byref(bufs.c_struct(dims)), _ptr(x),
-                          _ptr(x_scale), _ptr(buf), _ptr(buf_scale), _stream(stream))
+                          _ptr(x_scale), _ptr(buf), _ptr(buf_scale),
+                          _stream(stream, x, buf, x_scale, buf_scale, bufs.status))
     if rc != OK:
         raise MoebalError("mb_dispatch", rc)
 
@@ -311,7 +321,7 @@ def combine(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, w: torch.Tensor,
     _check(w, "w", torch.float32, numel=dims.n_tokens * dims.top_k)
     _check(y, "y", nbytes=dims.n_tokens * row)
     rc = _lib.mb_combine(ctypes.byref(dims), ctypes.byref(bufs.c_struct(dims)), _ptr(y_exp), _ptr(w),
-                         _ptr(y), _stream(stream))
+                         _ptr(y), _stream(stream, y_exp, w, y, bufs.status))
     if rc != OK:
         raise MoebalError("mb_combine", rc)
 
@@ -345,7 +355,8 @@ def combine_fp8(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, y_scale: tor
     _check(w, "w", torch.float32, numel=dims.n_tokens * dims.top_k)
     _check(y, "y", nbytes=dims.n_tokens * dims.hidden * ELT_BYTES.get(dims.dtype_out, 0))
     rc = _lib.mb_combine_fp8(ctypes.byref(dims), ctypes.byref(bufs.c_struct(dims)), _ptr(y_exp),
-                             _ptr(y_scale), _ptr(w), _ptr(y), _stream(stream))
+                             _ptr(y_scale), _ptr(w), _ptr(y),
+                             _stream(stream, y_exp, y_scale, w, y, bufs.status))
     if rc != OK:
         raise MoebalError("mb_combine_fp8", rc)
 
