@@ -837,3 +837,122 @@ def test_graph_capture_drift_state_advances():
         ref = O.plan(od, ids, drift=(oprm, st))
         G.assert_plan_equal(gp.fetch(), ref)
         _assert_state_equal(state, st, wl.n_experts, f"replay at call {call}")
+
+
+def test_graph_capture_weighted_repair_fp8():
+    """The fp8 decode path captured in one graph: mb_plan_weighted with the
+    quota repair, the fp8 dispatch with its scale rows, and mb_combine_fp8,
+    replayed on three routings copied into the captured inputs with eager
+    library work between the replays; every replay equals the oracle (plan
+    bit-exact, rows and scales byte-exact, combine on two token ranges). The
+    repair leaves these plans as placed; the next test captures one that
+    changes them."""
+    wl = W.get_workload("decode_drift")
+    # uneven speeds move rows toward the fast ranks: room for 1.5x the even share
+    dg, od = mb.Dims.for_workload(wl, cap=3 * wl.cap // 2), O.dims_for(wl, cap=3 * wl.cap // 2)
+    d = G.dev()
+    speeds = np.random.default_rng(77).integers(4000, 8001, wl.n_ranks).astype(np.int32)
+    ids0, w0 = W.routing_for(wl, 0)
+    x0, xs0 = W.token_rows(wl, 0)
+    ids_s, w_s = torch.from_numpy(ids0).to(d), torch.from_numpy(w0).to(d)
+    x_s, xs_s = torch.from_numpy(x0).to(d), torch.from_numpy(xs0).to(d)
+    bufs = mb.PlanBuffers.allocate(dg, d)
+    ws = mb.alloc_workspace(dg, d)
+    buf = torch.zeros((dg.rows, dg.hidden), dtype=torch.uint8, device=d)
+    bs = torch.zeros((dg.rows, dg.hidden // 128), dtype=torch.float32, device=d)
+    y = torch.zeros((dg.n_tokens, dg.hidden), dtype=torch.bfloat16, device=d)
+
+    def layer():
+        mb.plan(dg, ids_s, ws, bufs, speeds=speeds.tolist(), repair=True)
+        mb.dispatch(dg, bufs, x_s, buf, xs_s, bs)
+        mb.combine_fp8(dg, bufs, buf, bs, w_s, y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    other = G.GpuPlan(dg)
+    for call in (2, 5, 9):
+        ids, w = W.routing_for(wl, call)
+        x, xs = W.token_rows(wl, call)
+        ids_s.copy_(torch.from_numpy(ids))
+        w_s.copy_(torch.from_numpy(w))
+        x_s.copy_(torch.from_numpy(x))
+        xs_s.copy_(torch.from_numpy(xs))
+        graph.replay()
+        other.run(W.routing_for(wl, call + 1)[0], repair=True)  # eager work between replays
+        torch.cuda.synchronize()
+        ref = O.plan(od, ids, speeds=speeds, repair=True)
+        got = {k: getattr(bufs, k).cpu().numpy() for k in G.PLAN_FIELDS}
+        got["rep_expert"] = got["rep_expert"][:, : dg.slots_per_rank]
+        G.assert_plan_equal(got, ref)
+        ref_buf, ref_bs, _ = O.dispatch(od, ref, x, xs)
+        used = ref.row_src >= 0
+        assert np.array_equal(buf.cpu().numpy()[used], ref_buf[used]), call
+        assert np.array_equal(bs.cpu().numpy().view(np.uint32)[used],
+                              ref_bs.view(np.uint32)[used]), call
+        for t0, t1 in ((0, 192), (dg.n_tokens - 192, dg.n_tokens)):
+            y_ref, mag, _ = O.combine_fp8(od, ref.pos, ref.status, w, ref_buf, ref_bs, t0, t1)
+            G.assert_combine_close(G.y_to_f64(y[t0:t1]), y_ref, mag, "bf16")
+
+
+def test_graph_capture_repair_changes_quotas():
+    """mb_plan_ex with the repair, mb_dispatch and mb_combine captured once
+    and replayed on repair pattern inputs where the repair moves quota (and
+    so positions) away from the placed plan: each replay equals the oracle's
+    repaired plan, rows and combine."""
+    from tests.crafted import repair_pattern_ids
+
+    P, R, H = 8, 2, 64
+    N, E = 8 * P, 3 * P
+    dg = mb.Dims.make(N, 1, E, P, R, H, cap=16, dtype_in="f32", dtype_out="f32")
+    od = O.make_dims(N, 1, E, P, R, H, cap=16, dtype_in="f32", dtype_out="f32")
+    d = G.dev()
+    cases = [([(0, 1)], 1), ([(2, 5), (3, 7)], 2), ([(6, 7)], 4)]
+    ids_s = torch.from_numpy(repair_pattern_ids(P, *cases[0])).to(d)
+    w = np.ones((N, 1), np.float32)
+    w_s = torch.from_numpy(w).to(d)
+    x_s = torch.zeros((N, H), dtype=torch.float32, device=d)
+    ye = W.rows_f32(5, W.TAG_YEXP, H, n=P * 16)
+    ye_s = torch.from_numpy(ye).to(d)
+    bufs = mb.PlanBuffers.allocate(dg, d)
+    ws = mb.alloc_workspace(dg, d)
+    buf = torch.zeros((dg.rows, H), dtype=torch.float32, device=d)
+    y = torch.zeros((N, H), dtype=torch.float32, device=d)
+
+    def layer():
+        mb.plan(dg, ids_s, ws, bufs, repair=True)
+        mb.dispatch(dg, bufs, x_s, buf)
+        mb.combine(dg, bufs, ye_s, w_s, y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    other = G.GpuPlan(dg)
+    for pairs, seed in cases:
+        ids = repair_pattern_ids(P, pairs, seed)
+        x = W.rows_f32(seed, W.TAG_X, H, n=N)
+        ids_s.copy_(torch.from_numpy(ids))
+        x_s.copy_(torch.from_numpy(x))
+        graph.replay()
+        other.run(ids)  # eager, unrepaired, between replays
+        torch.cuda.synchronize()
+        ref = O.plan(od, ids, repair=True)
+        assert not np.array_equal(ref.slot_quota, O.plan(od, ids).slot_quota), seed
+        got = {k: getattr(bufs, k).cpu().numpy() for k in G.PLAN_FIELDS}
+        got["rep_expert"] = got["rep_expert"][:, : dg.slots_per_rank]
+        G.assert_plan_equal(got, ref)
+        ref_buf, _, _ = O.dispatch(od, ref, x, None)
+        used = ref.row_src >= 0
+        assert np.array_equal(G.rows_to_bytes(buf)[used], ref_buf[used]), seed
+        y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, ye)
+        G.assert_combine_close(y.cpu().numpy().astype(np.float64), y_ref, mag, "f32")
