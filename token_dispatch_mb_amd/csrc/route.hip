@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_count(
     const int32_t* __restrict__ ids, int K_, int E, int S, int nbps,
     int32_t* __restrict__ blockcnt, int32_t* __restrict__ blockflags,
     uint8_t* __restrict__ brank) {
-  extern __shared__ unsigned long long masks[];  // [kWaves][E]
+  extern __shared__ unsigned long long masks[];  // [kWaves][E], then int32 [kWaves][E]
   const int K = KT ? KT : K_;
   const int b = blockIdx.x;
   const int s = b / nbps, j = b - s * nbps;
@@ -65,20 +65,24 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_count(
   if (tl < nt) flags = mark_token<KT>(row, K, E, masks + w * E, lane);
   const int bad = __syncthreads_or(flags & MB_ST_BAD_ID);
   const int dup = __syncthreads_or(flags & MB_ST_DUP_ID);
+  // before[w][e]: pairs of e in the waves before w
+  int32_t* before = reinterpret_cast<int32_t*>(masks + kWaves * E);
   for (int e = tl; e < E; e += kTokensPerBlock) {
     int c = 0;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) c += __popcll(masks[ww * E + e]);
+    for (int ww = 0; ww < kWaves; ++ww) {
+      before[ww * E + e] = c;
+      c += __popcll(masks[ww * E + e]);
+    }
     blockcnt[(size_t)b * E + e] = c;
   }
   if (tl == 0) blockflags[b] = (bad ? MB_ST_BAD_ID : 0) | (dup ? MB_ST_DUP_ID : 0);
+  __syncthreads();
   if (tl >= nt) return;
   // In-workgroup rank of each of the token's pairs (0 for a bad id).
   auto rank_in_block = [&](int e) -> uint32_t {
     if ((unsigned)e >= (unsigned)E) return 0u;
-    int r = 0;
-    for (int ww = 0; ww < w; ++ww) r += __popcll(masks[ww * E + e]);
-    return (uint32_t)(r + lanes_below(masks[w * E + e]));
+    return (uint32_t)(before[w * E + e] + lanes_below(masks[w * E + e]));
   };
   if constexpr (KT == 8) {
     uint32_t lo = 0, hi = 0;
@@ -154,7 +158,9 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   // LDS: offsets [E4] | pairs [E] | ranges [E4] | hosts [nhost]
   extern __shared__ int4 lds[];
   __shared__ int32_t lp_s[kMaxRanks];
-  if (status[0] & MB_ST_FATAL) return;
+  // The plan's status is loaded with the tables and checked after staging,
+  // before anything is stored.
+  const int st = status[0];
   const int K = KT ? KT : K_;
   const int b = blockIdx.x;
   const int tl = threadIdx.x;
@@ -198,7 +204,9 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   // wave gw fills region gw mod P, the waves of one region interleaving in
   // 64-row strides (or, with fewer waves than regions, wave gw fills
   // regions gw, gw + GW, ...).
-  if (__syncthreads_or(pad > 0)) {
+  const bool fill = __syncthreads_or(pad > 0);
+  if (st & MB_ST_FATAL) return;
+  if (fill) {
     const int GW = gridDim.x * kWaves, gw = b * kWaves + (tl >> 6), ln = tl & 63;
     if (GW >= P) {
       const int r = gw % P, k = gw / P, nk = (GW - 1 - r) / P + 1;  // waves r, r + P, ... < GW
@@ -218,8 +226,7 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   // surplus number u of e and goes to the host whose share covers u.
   // The hosts' share ends ascend (each host listed has spare quota), so the
   // host of surplus number u is found by bisection.
-  auto search = [&](int e, int u, int q0) {
-    const int2 rg = hrange[e];
+  auto search = [&](const int2 rg, int u, int q0) {
     int lo = q0, hi = rg.y;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -251,17 +258,24 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
       h0[k] = hosts[rg[k].x];
       h1[k] = hosts[rg[k].x + (rg[k].y > 1 ? 1 : 0)];
     }
+    // Every candidate row is computed and the right one selected, so the
+    // table reads above stay independent of each other; only a share past
+    // the second host needs the bisection.
+    unsigned far = 0;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       const int u = rho[k] + pe[k].surplus_shift;
-      if (rho[k] < pe[k].local_quota)
-        p[k] = pe[k].local_base + rho[k];
-      else if (u < h0[k].end)
-        p[k] = h0[k].base + u + (h0[k].rank < s ? h0[k].lt : 0);
-      else if (rg[k].y > 1 && u < h1[k].end)
-        p[k] = h1[k].base + u + (h1[k].rank < s ? h1[k].lt : 0);
-      else
-        p[k] = search(er[k], u, 2);
+      const int p0 = h0[k].base + u + (h0[k].rank < s ? h0[k].lt : 0);
+      const int p1 = h1[k].base + u + (h1[k].rank < s ? h1[k].lt : 0);
+      const bool loc = rho[k] < pe[k].local_quota, in0 = u < h0[k].end;
+      const bool in1 = rg[k].y > 1 && u < h1[k].end;
+      p[k] = loc ? pe[k].local_base + rho[k] : in0 ? p0 : p1;
+      far |= (!loc && !in0 && !in1) ? 1u << k : 0u;
+    }
+    if (far) {
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+        if (far >> k & 1) p[k] = search(rg[k], rho[k] + pe[k].surplus_shift, 2);
     }
 #pragma unroll
     for (int k = 0; k < KT; ++k) pos[t * K + k] = p[k];
@@ -274,7 +288,7 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
       const int rho = boff[e] + brank[t * K + k];
       const PairEntry pe = ptab[e];
       const int p = rho < pe.local_quota ? pe.local_base + rho
-                                         : search(e, rho + pe.surplus_shift, 0);
+                                         : search(hrange[e], rho + pe.surplus_shift, 0);
       pos[t * K + k] = p;
       if ((unsigned)p < (unsigned)rows) row_src[p] = (int32_t)t;
     }
@@ -342,7 +356,7 @@ __global__ __launch_bounds__(256) void k_tables(
 hipError_t launch_count(const mb_dims& d, const Geometry& g, const int32_t* ids,
                         int32_t* blockcnt, int32_t* blockflags, uint8_t* brank, hipStream_t st) {
   if (g.nblk == 0) return hipSuccess;
-  const size_t shmem = sizeof(unsigned long long) * kWaves * d.n_experts;
+  const size_t shmem = (sizeof(unsigned long long) + sizeof(int32_t)) * kWaves * d.n_experts;
   MB_DISPATCH_TOPK(d.top_k, k_count, dim3(g.nblk), dim3(kTokensPerBlock), shmem, st, ids,
                    d.top_k, d.n_experts, g.S, g.nbps, blockcnt, blockflags, brank);
   return hipGetLastError();
