@@ -148,9 +148,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // index among equal values. The keys are exact while |x| and q stay below
 // 2^25, which N*K < 2^25 guarantees (loads, targets and quotas are at most
 // N*K); larger plans take greedy_lds. A move changes two lanes (the donor's
-// load and one quota key, the destination's load and slot count); those
-// updates run under a one-lane mask. Each move is recorded in the registers
-// of lane (move mod 64) and written to LDS 64 moves at a time.
+// load and one quota key, the destination's load and slot count); every
+// lane applies it through selects (the donor's quota key, with more than 8
+// per lane, addressed by the uniform expert index). Each move is recorded
+// in the registers of lane (move mod 64) and written to LDS 64 moves at a
+// time.
 constexpr long long kPackedPairsLimit = 1LL << 25;
 
 template <int EHM, int kLanes>
@@ -170,7 +172,12 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     kq[j] = real ? q * 32 + (31 - j) : -1;
   }
   const int lpre = load;
-  int used = 0, moves = 0, unbalanced = 0;
+  // The lane keeps x*64 itself: both reduction keys are then one add away,
+  // and a move adds or subtracts mv*64. A lane without a rank sits far
+  // below every key (never the busiest) with no free slot (never open).
+  int kx = rank_lane ? (load - tau) * 64 : -(1 << 30);
+  int used = rank_lane ? 0 : R;
+  int moves = 0, unbalanced = 0;
   int rec_e = 0, rec_m = 0, rec_i = 0;  // the move recorded in this lane
 
   for (;;) {
@@ -180,11 +187,9 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     for (int j = 1; j + 1 < EHM; j += 2) bk = max(bk, max(kq[j], kq[j + 1]));
     bk = max(bk, kq[EHM - 1]);
 
-    const int x = load - tau;
-    const bool open_lane = rank_lane && used < R && x < 0;
+    const int kn = kx + lane;  // x*64 + lane: negative exactly when x < 0
     int kmax, kmin;
-    wave_max_min_i32<kLanes>(rank_lane ? x * 64 + (63 - lane) : INT32_MIN,
-                             open_lane ? x * 64 + lane : INT32_MAX, kmax, kmin);
+    wave_max_min_i32<kLanes>(kx + (63 - lane), used < R && kn < 0 ? kn : INT32_MAX, kmax, kmin);
     __asm__ volatile("" : "+v"(bk));  // keep the tournament beside the reductions
     if (kmax < 64) break;             // largest x <= 0: every rank at or below target
     if (kmin == INT32_MAX) {          // no open rank
@@ -203,18 +208,17 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
       rec_m = mv;
       rec_i = d * R + slot;
     }
-    if (lane == d) {
-      load += mv;
-      used += 1;
-    }
-    if (lane == rs) {
-      load -= mv;
-      if constexpr (EHM <= 8) {
+    // Every lane applies the move; it changes only the lanes d and rs.
+    const bool at_d = lane == d, at_rs = lane == rs;
+    kx += (at_d ? mv * 64 : 0) - (at_rs ? mv * 64 : 0);
+    used += at_d ? 1 : 0;
+    if constexpr (EHM <= 8) {
+      if (at_rs) {
 #pragma unroll
         for (int j = 0; j < EHM; ++j) kq[j] -= j == jb ? mv * 32 : 0;
-      } else {
-        kq[jb] -= mv * 32;  // uniform index: relative register addressing
       }
+    } else {
+      kq[jb] -= at_rs ? mv * 32 : 0;  // uniform index: relative register addressing
     }
     ++moves;
     if ((moves & 63) == 0) {
@@ -223,6 +227,7 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
       m.order[moves - 64 + lane] = rec_i;
     }
   }
+  load = rank_lane ? (kx >> 6) + tau : 0;
   if (lane < (moves & 63)) {
     m.repE[rec_i] = rec_e;
     m.repM[rec_i] = rec_m;
