@@ -26,21 +26,36 @@ namespace mb {
 namespace {
 
 // Sets this lane's bit in the wave's mask of each of its token's experts and
-// returns the token's status bits (bad or repeated ids).
+// returns the token's status bits (bad or repeated ids). With a compile-time
+// K the ids are already in registers; otherwise they are read one by one.
 template <int KT>
-__device__ __forceinline__ int mark_token(const int32_t* __restrict__ row, int K_, int E,
-                                          unsigned long long* wmask, int lane) {
-  const int K = KT ? KT : K_;
+__device__ __forceinline__ int mark_token(const int* ev, const int32_t* __restrict__ row, int K_,
+                                          int E, unsigned long long* wmask, int lane) {
   int flags = 0;
-  for (int k = 0; k < K; ++k) {
-    const int e = row[k];
-    for (int k2 = 0; k2 < k; ++k2)
-      if (row[k2] == e) flags |= MB_ST_DUP_ID;
-    if ((unsigned)e >= (unsigned)E) {
-      flags |= MB_ST_BAD_ID;
-      continue;
+  if constexpr (KT > 0) {
+#pragma unroll
+    for (int k = 1; k < KT; ++k)
+#pragma unroll
+      for (int k2 = 0; k2 < k; ++k2)
+        if (ev[k2] == ev[k]) flags |= MB_ST_DUP_ID;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      if ((unsigned)ev[k] >= (unsigned)E)
+        flags |= MB_ST_BAD_ID;
+      else
+        atomicOr(&wmask[ev[k]], 1ull << lane);
     }
-    atomicOr(&wmask[e], 1ull << lane);
+  } else {
+    for (int k = 0; k < K_; ++k) {
+      const int e = row[k];
+      for (int k2 = 0; k2 < k; ++k2)
+        if (row[k2] == e) flags |= MB_ST_DUP_ID;
+      if ((unsigned)e >= (unsigned)E) {
+        flags |= MB_ST_BAD_ID;
+        continue;
+      }
+      atomicOr(&wmask[e], 1ull << lane);
+    }
   }
   return flags;
 }
@@ -56,13 +71,19 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_count(
   const int s = b / nbps, j = b - s * nbps;
   const int tl = threadIdx.x;
   const int nt = min(kTokensPerBlock, S - j * kTokensPerBlock);
-  for (int i = tl; i < kWaves * E; i += kTokensPerBlock) masks[i] = 0ull;
-  __syncthreads();
   const int w = tl >> 6, lane = tl & 63;
   const size_t t = (size_t)s * S + (size_t)j * kTokensPerBlock + tl;
   const int32_t* row = ids + t * K;
+  // The lane's ids are loaded before the masks are cleared, so their
+  // latency overlaps the clearing; they stay in registers for the ranks.
+  constexpr int KR = KT ? KT : 1;
+  int ev[KR];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) ev[k] = KT && tl < nt ? row[k] : 0;
+  for (int i = tl; i < kWaves * E; i += kTokensPerBlock) masks[i] = 0ull;
+  __syncthreads();
   int flags = 0;
-  if (tl < nt) flags = mark_token<KT>(row, K, E, masks + w * E, lane);
+  if (tl < nt) flags = mark_token<KT>(ev, row, K, E, masks + w * E, lane);
   const int bad = __syncthreads_or(flags & MB_ST_BAD_ID);
   const int dup = __syncthreads_or(flags & MB_ST_DUP_ID);
   // before[w][e]: pairs of e in the waves before w
@@ -87,15 +108,18 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_count(
   if constexpr (KT == 8) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) lo |= rank_in_block(row[k]) << (8 * k);
+    for (int k = 0; k < 4; ++k) lo |= rank_in_block(ev[k]) << (8 * k);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) hi |= rank_in_block(row[4 + k]) << (8 * k);
+    for (int k = 0; k < 4; ++k) hi |= rank_in_block(ev[4 + k]) << (8 * k);
     reinterpret_cast<uint2*>(brank)[t] = make_uint2(lo, hi);
   } else if constexpr (KT == 4) {
     uint32_t v = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v |= rank_in_block(row[k]) << (8 * k);
+    for (int k = 0; k < 4; ++k) v |= rank_in_block(ev[k]) << (8 * k);
     reinterpret_cast<uint32_t*>(brank)[t] = v;
+  } else if constexpr (KT > 0) {
+#pragma unroll
+    for (int k = 0; k < KT; ++k) brank[t * K + k] = (uint8_t)rank_in_block(ev[k]);
   } else {
     for (int k = 0; k < K; ++k) brank[t * K + k] = (uint8_t)rank_in_block(row[k]);
   }
