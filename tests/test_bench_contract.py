@@ -1,0 +1,57 @@
+"""bench.py's command line and its one-line JSON report.
+
+The CPU test checks that a request for more than one GPU is refused before
+anything touches a device; the GPU test runs a short benchmark in a child
+process and checks every key of the line it prints."""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+METRIC = "dispatch+combine GB/s (% of HBM peak) and mb_plan µs per MoE layer call"
+
+
+def _bench(*args, timeout=240):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=timeout)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _bench("--gpus", "2", timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.gpu
+def test_report_line_keys():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    r = _bench("--workload", "mixtral", "--steps", "3", "--warmup", "1")
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    assert d["metric"] == METRIC and d["unit"] == "GB/s"
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["higher_is_better"] is True and d["scaling"] == "weak"
+    assert d["vs_baseline"] is None and d["data"] == "synthetic"
+    assert d["dtype"] == "bf16" and d["config"]["workload"] == "mixtral"
+    assert d["value"] > 0 and d["ms_per_step"] > 0
+    # value: the step's algorithmic bytes over the step time
+    nbytes = sum(d["algorithmic_bytes"].values())
+    assert d["value"] == pytest.approx(nbytes / (d["ms_per_step"] * 1e6), rel=2e-3)
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-3)
+    assert "traffic" in rf
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s"
+    assert cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert d["plan_us"]["p50"] > 0
