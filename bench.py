@@ -130,9 +130,10 @@ def _speed_ratio(load, speeds, wl):
 
 
 def cpu_baseline(wl, fraction: int = 2) -> dict:
-    """The CPU oracle as it stands (single thread) on 1/fraction of the
-    tokens of the same workload: plan, dispatch and combine; GB/s over the
-    same algorithmic bytes, plus the oracle's plan time on the full call."""
+    """The CPU oracle as it stands (single thread, pinned to one core) on
+    1/fraction of the tokens of the same workload: plan, dispatch and combine,
+    the median of five runs of each; GB/s over the same algorithmic bytes,
+    plus the oracle's plan time on the full call."""
     import numpy as np
 
     import oracle as O
@@ -153,39 +154,63 @@ def cpu_baseline(wl, fraction: int = 2) -> dict:
     mag = np.empty_like(y64)
     mag.fill(0.0)
     speeds = W.rank_speeds(wl)
-    t0 = time.perf_counter()
-    p = O.plan(od, ids, speeds=speeds)
-    t1 = time.perf_counter()
-    O.dispatch(od, p, x, xs, out=buf)
-    t2 = time.perf_counter()
     if od.dtype_out == O.BF16 and od.dtype_in == O.BF16:
-        y_exp = buf.view(np.uint16).reshape(-1, od.hidden)
+        y_exp = None  # the dispatch buffer itself (identity experts)
     elif od.dtype_out == O.F32 and od.dtype_in == O.F32:
-        y_exp = buf.view(np.float32).reshape(-1, od.hidden)
+        y_exp = None
     else:
         y_exp = W.rows_bf16(sub.seed, W.TAG_YEXP, od.hidden, n=rows)
-    t3 = time.perf_counter()
-    O.combine(od, p.pos, p.status, w, y_exp, out=(y64, mag))
-    t4 = time.perf_counter()
-    if p.flags & O.ST_FATAL:
-        raise RuntimeError(f"oracle sample plan failed: status {p.status.tolist()}")
+    # One thread pinned to one host core; each stage timed five times (about
+    # 10 s of oracle work at the prefill workloads) and the median kept.
+    try:
+        prev = os.sched_getaffinity(0)
+        core = min(prev)
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        prev, core = None, None
+    tp, td, tc = [], [], []
+    try:
+        for _ in range(5):
+            t0 = time.perf_counter()
+            p = O.plan(od, ids, speeds=speeds)
+            t1 = time.perf_counter()
+            O.dispatch(od, p, x, xs, out=buf)
+            t2 = time.perf_counter()
+            ye = y_exp
+            if ye is None:
+                ye = buf.view(np.uint16 if od.dtype_out == O.BF16 else np.float32).reshape(
+                    -1, od.hidden)
+            t3 = time.perf_counter()
+            O.combine(od, p.pos, p.status, w, ye, out=(y64, mag))
+            t4 = time.perf_counter()
+            tp.append(t1 - t0)
+            td.append(t2 - t1)
+            tc.append(t4 - t3)
+        if p.flags & O.ST_FATAL:
+            raise RuntimeError(f"oracle sample plan failed: status {p.status.tolist()}")
+        full_ids, _ = W.routing_for(wl)
+        f0 = time.perf_counter()
+        O.plan(O.dims_for(wl), full_ids, speeds=speeds)
+        f1 = time.perf_counter()
+    finally:
+        if prev is not None:
+            os.sched_setaffinity(0, prev)
+    med = lambda v: sorted(v)[len(v) // 2]  # noqa: E731
+    t_plan, t_disp, t_comb = med(tp), med(td), med(tc)
     ab = algorithmic_bytes(sub)
-    full_ids, _ = W.routing_for(wl)
-    f0 = time.perf_counter()
-    O.plan(O.dims_for(wl), full_ids, speeds=speeds)
-    f1 = time.perf_counter()
     return {
-        "value": round((ab["dispatch"] + ab["combine"]) / ((t2 - t1) + (t4 - t3)) / 1e9, 3),
+        "value": round((ab["dispatch"] + ab["combine"]) / (t_disp + t_comb) / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"{sub.n_tokens} of {wl.n_tokens} tokens of {wl.name} (same routing model, "
                   f"same E/K/P/R/H, regions of 2*S*K rows): plan + dispatch + combine, "
-                  f"single-threaded C oracle",
-        "plan_us_sample": round((t1 - t0) * 1e6, 1),
-        "dispatch_s": round(t2 - t1, 3),
-        "combine_s": round(t4 - t3, 3),
+                  f"single-threaded C oracle pinned to one core, median of 5 runs per stage",
+        "plan_us_sample": round(t_plan * 1e6, 1),
+        "dispatch_s": round(t_disp, 3),
+        "combine_s": round(t_comb, 3),
         "plan_us_full_call": round((f1 - f0) * 1e6, 1),
+        "pinned_core": core,
         "host_cpu": _cpu_model(),
         "host_nproc": os.cpu_count(),
     }
