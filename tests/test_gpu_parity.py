@@ -191,6 +191,18 @@ def test_bad_and_duplicate_ids():
     assert ref.status[0] == O.ST_DUP_ID
 
 
+@pytest.mark.parametrize("din,dout,H", [("bf16", "f32", 200), ("f32", "bf16", 200),
+                                         ("fp8", "f32", 384), ("fp8", "bf16", 384)])
+def test_mixed_row_types(din, dout, H):
+    """Input rows and expert outputs of different types in one plan: the
+    dispatch follows the input type (fp8 with its scale rows), the combine
+    the output type; both against the oracle on a skewed routing."""
+    P, S, K, eh, R = 8, 300, 8, 8, 2
+    ids, _ = W.routing(P * S, P * eh, K, W.NOISE_GUMBEL, 1.1, 1.0, 6100 + H)
+    _edge(P * S, K, P * eh, P, R, H, ids, cap=2 * S * K, din=din, dout=dout, seed=H,
+          label=f"mixed {din}->{dout} H{H}")
+
+
 def test_empty_batch():
     dg = mb.Dims.make(0, 2, 16, 4, 1, 64, cap=8, dtype_in="bf16", dtype_out="bf16")
     od = O.make_dims(0, 2, 16, 4, 1, 64, cap=8, dtype_in="bf16", dtype_out="bf16")
