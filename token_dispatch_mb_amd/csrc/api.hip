@@ -149,7 +149,7 @@ static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t*
       launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_plan(*dims, g, *out, rank_speed, drift, drift_state, repair, blockflags,
-                  one_block ? nullptr : expert_total, host_range, stream) != hipSuccess)
+                  one_block ? nullptr : expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;

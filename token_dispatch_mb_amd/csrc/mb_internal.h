@@ -34,7 +34,7 @@ struct alignas(16) PairEntry {
 
 // Hosts of expert e that take surplus pairs, ascending rank, stored in a
 // compact list: expert e owns entries [host_range[e].x, host_range[e].x +
-// host_range[e].y); its capacity (1 + replicas of e) is fixed by k_plan.
+// host_range[e].y); its capacity is 1 + (replicas of e).
 //   end  = surplus index one past this host's share
 //   base = dispatch row of surplus index 0 on this host (row - start index)
 //   rank = host rank
@@ -76,7 +76,7 @@ hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* block
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
                        void* drift_state, int repair, const int32_t* blockflags,
-                       const int32_t* expert_total, int2* host_range, hipStream_t st);
+                       const int32_t* expert_total, hipStream_t st);
 
 // Bytes of a drift state buffer: header, int64 reference [E], kept replicas
 // and their placement order [P*R] each.

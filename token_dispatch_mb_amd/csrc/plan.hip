@@ -49,7 +49,6 @@ struct PlanArgs {
   int32_t* slot_quota;
   int32_t* cu_seqlens;
   int32_t* status;
-  int2* host_range;
 };
 
 constexpr int kPlanThreads = 256;
@@ -855,42 +854,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   int mymax = 0;
   for (int r = tid; r < P; r += kPlanThreads) mymax = max(mymax, m.loadv[r]);
   if (tid < 64) {
-    const int mx = wave_max_i32(mymax);
-    if (tid == 0) m.misc[2] = mx;
-  }
-  // Compact host-list ranges: expert e gets 1 + (replicas of e) entries,
-  // offsets by a block-wide exclusive scan in expert order.
-  for (int e = tid; e < E; e += kPlanThreads) m.c[e] = 1;
-  __syncthreads();
-  for (int i = tid; i < P * R; i += kPlanThreads)
-    if (m.repE[i] >= 0) atomicAdd(&m.c[m.repE[i]], 1);
-  __syncthreads();
-  const int per = (E + kPlanThreads - 1) / kPlanThreads;
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int e = tid * per + i;
-    if (e < E) local += m.c[e];
-  }
-  const int incl = wave_inclusive_sum(local);
-  if ((tid & 63) == 63) m.lpre[tid >> 6] = incl;  // per-wave totals (lpre is free now)
-  const int max_load = m.misc[2];
-  __syncthreads();
-  int before = incl - local;
-  for (int w = 0; w < (tid >> 6); ++w) before += m.lpre[w];
-  for (int i = 0; i < per; ++i) {
-    const int e = tid * per + i;
-    if (e < E) {
-      a.host_range[e] = make_int2(before, 0);
-      before += m.c[e];
+    const int max_load = wave_max_i32(mymax);
+    if (tid == 0) {
+      a.status[0] = (m.misc[1] ? MB_ST_UNBALANCED : 0) | (max_load > a.cap ? MB_ST_CAPACITY : 0) |
+                    (drift && m.misc[4] ? MB_ST_REPLANNED : 0);
+      a.status[1] = m.misc[3];
+      a.status[2] = max_load;
+      a.status[3] = m.misc[0];
     }
-  }
-  const bool over_cap = max_load > a.cap;
-  if (tid == 0) {
-    a.status[0] = (m.misc[1] ? MB_ST_UNBALANCED : 0) | (over_cap ? MB_ST_CAPACITY : 0) |
-                  (drift && m.misc[4] ? MB_ST_REPLANNED : 0);
-    a.status[1] = m.misc[3];
-    a.status[2] = max_load;
-    a.status[3] = m.misc[0];
   }
 }
 
@@ -899,7 +870,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
                        void* drift_state, int repair, const int32_t* blockflags,
-                       const int32_t* expert_total, int2* host_range, hipStream_t st) {
+                       const int32_t* expert_total, hipStream_t st) {
   PlanArgs a;
   a.N = d.n_tokens;
   a.K = d.top_k;
@@ -935,7 +906,6 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.slot_quota = o.slot_quota;
   a.cu_seqlens = o.cu_seqlens;
   a.status = o.status;
-  a.host_range = host_range;
   const size_t shmem = plan_smem_bytes(a.E, a.P, a.R, a.NS);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), shmem, st, a);
   return hipGetLastError();

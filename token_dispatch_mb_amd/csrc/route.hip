@@ -335,15 +335,15 @@ __global__ __launch_bounds__(256) void k_tables(
   const int s = threadIdx.x & 63;
   const bool valid = s < P;
   const int home = e / Eh;
-  int d = 0, slot = -1, lq = 0, rowbase = 0;
+  int d = 0, slot = -1, lq = 0, rowbase = 0, reps_below = 0;
   if (valid) {
     d = counts[(size_t)s * E + e];
-    if (s == home) {
-      slot = e - s * Eh;
-    } else {
-      for (int q = 0; q < R; ++q)
-        if (rep_expert[s * R + q] == e) slot = Eh + q;
+    for (int q = 0; q < R; ++q) {
+      const int re = rep_expert[s * R + q];
+      reps_below += (unsigned)re < (unsigned)e ? 1 : 0;
+      if (s != home && re == e) slot = Eh + q;
     }
+    if (s == home) slot = e - s * Eh;
     if (slot >= 0) {
       lq = slot_quota[s * NS + slot];
       rowbase = s * cap + cu_seqlens[s * (NS + 1) + slot];
@@ -361,8 +361,10 @@ __global__ __launch_bounds__(256) void k_tables(
     pe.pad = 0;
     pair_tab[(size_t)s * E + e] = pe;
   }
+  // The host list in expert order, 1 + (replicas of e) entries for e: its
+  // entries start after those of the experts below it.
+  const int off = e + __builtin_amdgcn_readlane(wave_inclusive_sum(reps_below), 63);
   const uint64_t hb = ballot64(valid && sp > 0);
-  const int off = host_range[e].x;  // set by k_plan
   if (valid && sp > 0) {
     HostEntry h;
     h.end = sp_before + sp;
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(256) void k_tables(
     h.lt = lt;
     host_list[off + lanes_below(hb)] = h;
   }
-  if (s == 0) host_range[e].y = __popcll(hb);
+  if (s == 0) host_range[e] = make_int2(off, __popcll(hb));
 }
 
 }  // namespace
