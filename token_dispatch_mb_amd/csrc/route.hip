@@ -142,12 +142,12 @@ __global__ __launch_bounds__(256) void k_scan(const int32_t* __restrict__ blockc
   if (s < P && e < E) {
     const size_t b0 = (size_t)s * nbps;
     int j = 0;
-    for (; j + 8 <= nbps; j += 8) {
-      int c[8];
+    for (; j + 16 <= nbps; j += 16) {  // 16 loads in flight per round trip
+      int c[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = blockcnt[(b0 + j + i) * E + e];
+      for (int i = 0; i < 16; ++i) c[i] = blockcnt[(b0 + j + i) * E + e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 16; ++i) {
         blockoff[(b0 + j + i) * E + e] = off;
         off += c[i];
       }
