@@ -84,8 +84,9 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_count(
   __syncthreads();
   int flags = 0;
   if (tl < nt) flags = mark_token<KT>(ev, row, K, E, masks + w * E, lane);
-  const int bad = __syncthreads_or(flags & MB_ST_BAD_ID);
-  const int dup = __syncthreads_or(flags & MB_ST_DUP_ID);
+  __shared__ int wfl[kWaves];
+  const int fl_all = block_or_bits(flags, wfl, kWaves);
+  const int bad = fl_all & MB_ST_BAD_ID, dup = fl_all & MB_ST_DUP_ID;
   // before[w][e]: pairs of e in the waves before w
   int32_t* before = reinterpret_cast<int32_t*>(masks + kWaves * E);
   for (int e = tl; e < E; e += kTokensPerBlock) {
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   // wave gw fills region gw mod P, the waves of one region interleaving in
   // 64-row strides (or, with fewer waves than regions, wave gw fills
   // regions gw, gw + GW, ...).
-  const bool fill = __syncthreads_or(pad > 0);
+  __shared__ int wfl[kWaves];
+  const bool fill = block_or_bits(pad > 0 ? 1 : 0, wfl, kWaves) != 0;
   if (st & MB_ST_FATAL) return;
   if (fill) {
     const int GW = gridDim.x * kWaves, gw = b * kWaves + (tl >> 6), ln = tl & 63;

@@ -14,6 +14,21 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
+// OR over the workgroup of per-thread status bits (the low 8 bits): one
+// ballot per bit in each wave, a word per wave in `wfl`, and one barrier,
+// which also orders the workgroup's earlier LDS writes as __syncthreads()
+// does. Called once per kernel (wfl is not reset).
+__device__ __forceinline__ int block_or_bits(int bits, int* wfl, int nwaves) {
+  int w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= __ballot((bits >> i) & 1) ? 1 << i : 0;
+  if ((threadIdx.x & 63) == 0) wfl[threadIdx.x >> 6] = w;
+  __syncthreads();
+  int all = 0;
+  for (int i = 0; i < nwaves; ++i) all |= wfl[i];
+  return all;
+}
+
 // DPP row shift / broadcast with `identity` for lanes that receive nothing.
 template <int kCtrl, int kRowMask>
 __device__ __forceinline__ int dpp_or_identity(int identity, int v) {
