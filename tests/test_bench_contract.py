@@ -55,3 +55,18 @@ def test_report_line_keys():
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s"
     assert cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     assert d["plan_us"]["p50"] > 0
+    assert d["graph_replay"] is None
+
+
+@pytest.mark.gpu
+def test_graph_replay_report():
+    """--graph adds the steps replayed from HIP graphs beside the eager ones."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    r = _bench("--workload", "mixtral", "--steps", "3", "--warmup", "1", "--graph",
+               "--skip-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    g = d["graph_replay"]
+    assert g["graphs"] >= 1 and g["ms_per_step"] > 0 and g["value"] > 0
+    assert d["cpu_baseline"] is None
