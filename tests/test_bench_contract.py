@@ -70,3 +70,25 @@ def test_graph_replay_report():
     g = d["graph_replay"]
     assert g["graphs"] >= 1 and g["ms_per_step"] > 0 and g["value"] > 0
     assert d["cpu_baseline"] is None
+
+
+@pytest.mark.gpu
+def test_fp8_and_drift_reports():
+    """The fp8 decode workload with the dequantising combine, and the
+    drift-gated sequence with its replan report."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    r = _bench("--workload", "decode_drift", "--combine-fp8", "--steps", "4", "--warmup", "1",
+               "--skip-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["dtype"] == "fp8" and d["config"]["workload"] == "decode_drift"
+    assert d["config"]["expert_outputs"] == "fp8+scales"
+    assert d["roofline"]["frac"] == pytest.approx(d["roofline"]["achieved"] / 8000.0, rel=1e-3)
+    r = _bench("--workload", "drift_decode", "--warmup", "1", "--skip-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    g = d["drift_gate"]
+    assert d["steps"] == d["config"]["calls"] and g["replanned_calls"][0] == 0
+    assert 0 < g["plan_us_kept"] and 0 < g["plan_us_replanned"]
+    assert g["header"]["replans"] == len(g["replanned_calls"])
