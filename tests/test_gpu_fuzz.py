@@ -11,6 +11,8 @@ Inputs come from ``workload``; expected values from the oracle only.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -31,7 +33,11 @@ def _gpu_required():
     torch.cuda.synchronize()
 
 
-def fuzz_cases(n: int = 240, seed: int = 4242):
+def fuzz_cases(n: int | None = None, seed: int | None = None):
+    """Seeded random shapes; MB_FUZZ_CASES and MB_FUZZ_SEED widen a run
+    (defaults 240 and 4242)."""
+    n = int(os.environ.get("MB_FUZZ_CASES", 240)) if n is None else n
+    seed = int(os.environ.get("MB_FUZZ_SEED", 4242)) if seed is None else seed
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
