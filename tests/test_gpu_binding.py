@@ -45,3 +45,16 @@ def test_short_gpu_tensors_are_refused():
     mb.plan(d, ids, ws, bufs)
     assert mb.plan_status(bufs)[0] == 0
     assert bufs._key is not None and bufs._key[1] == mb._dims_key(d)
+
+
+def test_smaller_buffer_at_the_same_address_is_checked_again():
+    """The checked-buffer cache keys on sizes as well as addresses: a view of
+    the same storage with too few elements is refused, not taken from the
+    cache."""
+    dev = torch.device("cuda:0")
+    d = mb.Dims.make(64, 2, 16, 4, 1, 128, dtype_in="bf16", dtype_out="bf16")
+    bufs = mb.PlanBuffers.allocate(d, dev)
+    bufs.c_struct(d)  # checked and cached
+    bufs.pos = bufs.pos.view(-1)[:10]  # same address, 10 of 128 elements
+    with pytest.raises(ValueError, match="pos holds 10 elements, 128 needed"):
+        bufs.c_struct(d)

@@ -239,10 +239,14 @@ class PlanBuffers:
     def c_struct(self, dims: Dims | None = None) -> _PlanBufsC:
         """The mb_plan_bufs of these tensors; with `dims`, checked against
         them first (once per set of pointers and sizes)."""
-        ptrs = tuple(getattr(self, n).data_ptr() for n, _ in _PlanBufsC._fields_)
+        ts = [getattr(self, n) for n, _ in _PlanBufsC._fields_]
+        ptrs = tuple(t.data_ptr() for t in ts)
         if dims is None:
             return self._c if self._key is not None and self._key[0] == ptrs else _PlanBufsC(*ptrs)
-        key = (ptrs, _dims_key(dims))
+        # the key holds the sizes too: a smaller tensor at the same address
+        # is checked again
+        key = (ptrs, _dims_key(dims), tuple(t.numel() for t in ts),
+               tuple(t.is_contiguous() for t in ts))
         if key != self._key:
             self.check(dims)
             self._c, self._key = _PlanBufsC(*ptrs), key
