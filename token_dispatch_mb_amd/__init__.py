@@ -371,7 +371,7 @@ def plan_status(bufs: PlanBuffers, stream=None):
 
     _check(bufs.status, "status", torch.int32, numel=4)
     out = (ctypes.c_int32 * 4)()
-    rc = _lib.mb_plan_status(ctypes.byref(bufs.c_struct()), _stream(stream), out)
+    rc = _lib.mb_plan_status(ctypes.byref(bufs.c_struct()), _stream(stream, bufs.status), out)
     if rc != OK:
         raise MoebalError("mb_plan_status", rc)
     return np.array(list(out), dtype=np.int32)
