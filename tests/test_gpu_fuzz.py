@@ -110,9 +110,11 @@ def test_random_drift_sequences_bit_exact():
     """40 seeded drift-gated sequences of 6-14 calls: random shapes,
     thresholds (including 0 and 1), windows, check intervals, popularity
     changes, rank speeds and the quota repair on some; every call's plan and
-    the whole drift state after it equal the oracle's."""
-    rng = np.random.default_rng(777)
-    for n in range(40):
+    the whole drift state after it equal the oracle's. MB_FUZZ_DRIFT and
+    MB_FUZZ_SEED widen a run."""
+    seed = int(os.environ.get("MB_FUZZ_SEED", 0))
+    rng = np.random.default_rng(777 + seed)
+    for n in range(int(os.environ.get("MB_FUZZ_DRIFT", 40))):
         P = int(rng.choice([1, 2, 5, 16, 31, 32, 33, 64]))
         eh = max(1, min(int(rng.choice([1, 2, 4, 8, 17, 40])), 1024 // P))
         E = P * eh
