@@ -49,7 +49,11 @@
  *    device (MB_ST_* bits). mb_dispatch and mb_combine read that word on the
  *    device and do nothing when a fatal bit (MB_ST_FATAL) is set, so a bad
  *    plan never writes out of bounds. When a fatal bit is set, the plan's
- *    pos and row_src contents are unspecified.
+ *    pos and row_src contents are unspecified. With MB_ST_BAD_ID or
+ *    MB_ST_DUP_ID there is no plan: counts, load_pre, load_post, slot_quota
+ *    and cu_seqlens are all 0, every rep_expert entry is -1, and status is
+ *    {flags, T, 0, 0}. With MB_ST_CAPACITY alone every output but pos and
+ *    row_src holds the plan that did not fit.
  *
  * Limits: 1 <= P <= 64, E % P == 0, E <= 1024, 1 <= K <= min(E, 32),
  * 0 <= R <= 16, N % P == 0, N*K < 2^31, P*cap < 2^31, row bytes a multiple

@@ -191,6 +191,29 @@ def test_bad_and_duplicate_ids():
     assert ref.status[0] == O.ST_DUP_ID
 
 
+def test_bad_ids_clear_the_previous_plan():
+    """A plan of bad or repeated ids into buffers that hold a valid plan:
+    counts, loads, quotas and cu_seqlens read 0 and every replica slot -1,
+    as in the oracle, not the previous call's values."""
+    wl = W.get_workload("tiny")
+    ids, _ = W.routing_for(wl)
+    dg = mb.Dims.for_workload(wl)
+    od = O.dims_for(wl)
+    gp = G.GpuPlan(dg)
+    good = gp.run(ids).fetch()
+    G.assert_plan_equal(good, O.plan(od, ids))
+    assert good["counts"].any() and (good["rep_expert"] >= 0).any()
+    for bad_val, flag in ((wl.n_experts, O.ST_BAD_ID), (-1, O.ST_BAD_ID), (None, O.ST_DUP_ID)):
+        gp.run(ids)
+        bad = ids.copy()
+        bad[37, 1] = bad[37, 0] if bad_val is None else bad_val
+        got = gp.run(bad).fetch()
+        ref = O.plan(od, bad)
+        assert ref.status[0] == flag
+        G.assert_plan_equal(got, ref)
+        assert not got["counts"].any() and (got["rep_expert"] == -1).all()
+
+
 @pytest.mark.parametrize("din,dout,H", [("bf16", "f32", 200), ("f32", "bf16", 200),
                                          ("fp8", "f32", 384), ("fp8", "bf16", 384)])
 def test_mixed_row_types(din, dout, H):

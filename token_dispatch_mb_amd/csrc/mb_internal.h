@@ -19,12 +19,14 @@ constexpr int kMaxExperts = 1024; // LDS: kWaves * E * 8 bytes of token masks
 constexpr int kMaxTopK = 32;
 constexpr int kMaxSlots = 16;
 
-// One entry per (source rank s, expert e), written by k_plan, read by
+// One entry per (source rank s, expert e), written by k_tables, read by
 // k_assign for every pair (s, e):
-//   x = local quota of s for e (0 when s holds no copy of e)
-//   y = first row of s's local pairs of e, absolute in the dispatch buffer
-//   z = (surplus pairs of e from ranks < s) - x, so that a surplus pair of
-//       stable rank rho has surplus index u = rho + z
+//   local_quota   = quota of s for e (0 when s holds no copy of e)
+//   local_base    = first row of s's local pairs of e, absolute in the
+//                   dispatch buffer
+//   surplus_shift = (surplus pairs of e from ranks < s) - local_quota, so
+//                   that a surplus pair of stable rank rho has surplus
+//                   index u = rho + surplus_shift
 struct alignas(16) PairEntry {
   int32_t local_quota;
   int32_t local_base;

@@ -41,6 +41,7 @@ struct PlanArgs {
   int delta_num, delta_den, window, check_every;
   int repair;                 // quota repair after placement
   const int32_t* counts;      // [P][E] pairs per (source rank, expert), from k_scan
+  int32_t* counts_out;        // the same buffer, cleared when the routing is invalid
   const int32_t* expert_total;
   const int32_t* blockflags;
   int32_t* load_pre;
@@ -785,8 +786,16 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     m.repM[i] = 0;
   }
   if (__syncthreads_or(fl)) {
+    // Routing decisions that name no expert or one twice define no plan:
+    // every count, load and quota is 0, every replica slot empty, and
+    // cu_seqlens all 0 (pos and row_src are left unspecified).
     const int bad = __syncthreads_or(fl & MB_ST_BAD_ID);
     const int dup = __syncthreads_or(fl & MB_ST_DUP_ID);
+    for (int i = tid; i < P * E; i += kPlanThreads) a.counts_out[i] = 0;
+    for (int r = tid; r < P; r += kPlanThreads) a.load_pre[r] = a.load_post[r] = 0;
+    for (int i = tid; i < P * R; i += kPlanThreads) a.rep_expert[i] = -1;
+    for (int i = tid; i < P * NS; i += kPlanThreads) a.slot_quota[i] = 0;
+    for (int i = tid; i < P * (NS + 1); i += kPlanThreads) a.cu_seqlens[i] = 0;
     if (tid == 0) {
       a.status[0] = (bad ? MB_ST_BAD_ID : 0) | (dup ? MB_ST_DUP_ID : 0);
       a.status[1] = m.misc[3];
@@ -898,6 +907,7 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.check_every = drift ? drift->check_every : 1;
   a.repair = repair;
   a.counts = o.counts;
+  a.counts_out = o.counts;
   a.expert_total = expert_total;
   a.blockflags = blockflags;
   a.load_pre = o.load_pre;
