@@ -207,6 +207,27 @@ size_t mb_plan_workspace_bytes(const mb_dims* dims);
 int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws_bytes,
             const mb_plan_bufs* out, hipStream_t stream);
 
+/* Largest workspace mb_plan_noalloc can use: 4 MiB per GPU. */
+#define MB_NOALLOC_WS_BYTES (4u << 20)
+
+/*
+ * mb_plan for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same plan as mb_plan, with the workspace taken from an array the
+ * library holds in device memory, one per GPU (MB_NOALLOC_WS_BYTES bytes,
+ * kept until the process ends). The call allocates and frees nothing.
+ *  ids_dev, out, stream  as in mb_plan; the GPU is the one `stream` runs on.
+ * Returns MB_ERR_WORKSPACE, enqueueing nothing, when these sizes need more
+ * than MB_NOALLOC_WS_BYTES (mb_plan_workspace_bytes(dims) tells), and
+ * MB_ERR_HIP if the array's device address cannot be obtained (the first
+ * call on each GPU looks it up). Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents: two calls whose work
+ * overlaps in time on one GPU (on different streams, or from different
+ * threads without ordering) race and may both produce wrong plans.
+ */
+int mb_plan_noalloc(const mb_dims* dims, const int32_t* ids_dev, const mb_plan_bufs* out,
+                    hipStream_t stream);
+
 /*
  * mb_plan with per-rank targets in place of the single water level [ViBE,
  * Variability-Informed Expert Placement]: rank r of speed s_r aims at

@@ -89,6 +89,8 @@ _lib.mb_plan_workspace_bytes.restype = ctypes.c_size_t
 _lib.mb_plan.argtypes = [ctypes.POINTER(Dims), _vp, _vp, ctypes.c_size_t,
                          ctypes.POINTER(_PlanBufsC), _vp]
 _lib.mb_plan.restype = ctypes.c_int
+_lib.mb_plan_noalloc.argtypes = [ctypes.POINTER(Dims), _vp, ctypes.POINTER(_PlanBufsC), _vp]
+_lib.mb_plan_noalloc.restype = ctypes.c_int
 _lib.mb_plan_weighted.argtypes = [ctypes.POINTER(Dims), _vp, _i32p, _vp, ctypes.c_size_t,
                                   ctypes.POINTER(_PlanBufsC), _vp]
 _lib.mb_plan_weighted.restype = ctypes.c_int
@@ -125,9 +127,10 @@ _lib.mb_plan_status.argtypes = [ctypes.POINTER(_PlanBufsC), _vp, _i32p]
 _lib.mb_plan_status.restype = ctypes.c_int
 
 EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan",
-           "mb_plan_weighted", "mb_drift_state_bytes", "mb_plan_drift", "mb_plan_ex",
+           "mb_plan_noalloc", "mb_plan_weighted", "mb_drift_state_bytes", "mb_plan_drift", "mb_plan_ex",
            "mb_dispatch", "mb_combine", "mb_combine_fp8", "mb_plan_status")
 ST_REPLANNED = 16
+NOALLOC_WS_BYTES = 4 << 20
 MAX_WINDOW = 4096
 MAX_SPEED = 1 << 20
 
@@ -298,6 +301,17 @@ def plan(dims: Dims, ids: torch.Tensor, ws: torch.Tensor, bufs: PlanBuffers, str
                                ctypes.byref(cb), st)
     if rc != OK:
         raise MoebalError("mb_plan_weighted", rc)
+
+
+def plan_noalloc(dims: Dims, ids: torch.Tensor, bufs: PlanBuffers, stream=None) -> None:
+    """mb_plan_noalloc: mb_plan with the library's own per-GPU workspace (no
+    workspace argument; calls on one GPU must not overlap in time)."""
+    _check(ids, "ids", torch.int32, numel=dims.n_tokens * dims.top_k)
+    cb = bufs.c_struct(dims)
+    rc = _lib.mb_plan_noalloc(ctypes.byref(dims), _ptr(ids), ctypes.byref(cb),
+                              _stream(stream, ids, bufs.status))
+    if rc != OK:
+        raise MoebalError("mb_plan_noalloc", rc)
 
 
 def dispatch(dims: Dims, bufs: PlanBuffers, x: torch.Tensor, buf: torch.Tensor,

@@ -2,6 +2,8 @@
 // The operations and conventions are documented in include/moebal.h.
 #include <string.h>
 
+#include <mutex>
+
 #include "mb_internal.h"
 
 namespace mb {
@@ -166,6 +168,54 @@ int mb_plan(const mb_dims* dims, const int32_t* ids_dev, void* ws_dev, size_t ws
   int32_t ones[kMaxRanks];
   for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
   return plan_impl(dims, ids_dev, ones, nullptr, nullptr, 0, ws_dev, ws_bytes, out, stream);
+}
+
+// ---- mb_plan_noalloc: mb_plan on a workspace the library holds ----------
+//
+// Every GPU the library runs on holds its own copy of `scratch`, at its own
+// address, until the process ends. In host code the array's name is only a
+// host-side stand-in: the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MB_NOALLOC_WS_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the GPU that `stream` belongs to.
+static int scratch_for(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return MB_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MB_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return MB_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MB_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MB_ERR_HIP;
+    if (e != hipSuccess || !p) return MB_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MB_OK;
+}
+
+int mb_plan_noalloc(const mb_dims* dims, const int32_t* ids_dev, const mb_plan_bufs* out,
+                    hipStream_t stream) {
+  const int rc = validate(dims);
+  if (rc != MB_OK) return rc;
+  const size_t need = ws_layout(*dims, geometry(*dims)).total;
+  if (need > MB_NOALLOC_WS_BYTES) return MB_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int src = scratch_for(stream, &ws);
+  if (src != MB_OK) return src;
+  int32_t ones[kMaxRanks];
+  for (int r = 0; r < kMaxRanks; ++r) ones[r] = 1;
+  return plan_impl(dims, ids_dev, ones, nullptr, nullptr, 0, ws, MB_NOALLOC_WS_BYTES, out,
+                   stream);
 }
 
 int mb_plan_weighted(const mb_dims* dims, const int32_t* ids_dev, const int32_t* rank_speed,
