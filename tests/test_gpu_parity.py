@@ -191,6 +191,23 @@ def test_bad_and_duplicate_ids():
     assert ref.status[0] == O.ST_DUP_ID
 
 
+def test_workspace_reused_across_sizes():
+    """One workspace for plans of different sizes in a row (one to 33 routing
+    blocks per source rank, several top-K, R = 0 to 3): every plan matches
+    the oracle, whatever the previous call left in the workspace."""
+    shapes = [(4, 8448, 16, 2, 1), (8, 300, 64, 8, 2), (64, 128, 256, 8, 1), (2, 256, 8, 3, 0),
+              (16, 1030, 96, 4, 3), (1, 700, 4, 1, 1), (32, 4096, 256, 8, 1)]
+    dev = G.dev()
+    dims = [mb.Dims.make(P * S, K, E, P, R, 64, cap=2 * S * K) for P, S, E, K, R in shapes]
+    ws = torch.empty(max(mb.workspace_bytes(d) for d in dims), dtype=torch.uint8, device=dev)
+    for (P, S, E, K, R), dg in zip(shapes, dims):
+        ids, _ = W.routing(P * S, E, K, W.NOISE_GUMBEL, 1.1, 1.0, 7000 + P * S)
+        od = O.make_dims(P * S, K, E, P, R, 64, cap=2 * S * K)
+        gp = G.GpuPlan(dg)
+        gp.ws = ws
+        G.assert_plan_equal(gp.run(ids).fetch(), O.plan(od, ids))
+
+
 def test_bad_ids_clear_the_previous_plan():
     """A plan of bad or repeated ids into buffers that hold a valid plan:
     counts, loads, quotas and cu_seqlens read 0 and every replica slot -1,
