@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MB_VERSION 1
+#define MB_VERSION 2
 
 /* Element types of rows. */
 enum mb_dtype {
@@ -103,6 +103,10 @@ enum mb_status_flag {
 /* status[0] bit of mb_plan_drift: this call ran the greedy placement
  * (informational, never fatal). */
 #define MB_ST_REPLANNED 16
+/* status[0] bit of mb_plan_drift, set with MB_ST_REPLANNED: the gate kept
+ * the placement, but its replay on this call's counts failed the load guard,
+ * so the greedy ran in the same call (informational). */
+#define MB_ST_GUARDED 32
 
 /* Largest reference window of mb_plan_drift, in calls. */
 #define MB_MAX_WINDOW 4096
@@ -114,6 +118,10 @@ typedef struct mb_drift_params {
   int32_t window;      /* reference = count vectors of up to `window` calls
                           since the last replan, in [1, MB_MAX_WINDOW] */
   int32_t check_every; /* calls between two checks (>= 1) */
+  int32_t tol_num;     /* load guard: a kept placement stands only if no   */
+  int32_t tol_den;     /*   rank needs more than cap rows and, when tol_den
+                          > 0, none ends above (1 + tol_num / tol_den) times
+                          its target; both >= 0 (0, 0: cap only) */
 } mb_drift_params;
 
 /* First bytes of a drift state buffer (device memory, caller-owned); the
@@ -128,7 +136,8 @@ typedef struct mb_drift_header {
   int64_t calls;      /* calls planned with this state */
   int64_t replans;    /* of which ran the greedy */
   double last_d;      /* distance found at the last check */
-  int64_t reserved[3];
+  int64_t guarded;    /* replans forced by the load guard */
+  int64_t reserved[2];
 } mb_drift_header;
 
 /* Problem sizes of one MoE layer call. */
@@ -265,9 +274,14 @@ size_t mb_drift_state_bytes(const mb_dims* dims);
  * counts, and status[0] gets MB_ST_REPLANNED. Otherwise the kept replicas,
  * in the order they were placed, each take min(target - host load,
  * remaining home quota) pairs while the expert's home rank is above its
- * target and the host below its own (none otherwise), the plan is
- * MB_ST_UNBALANCED if any rank stays above its target, and this call's
- * counts join the reference while it holds fewer than `window` vectors.
+ * target and the host below its own (none otherwise), and this call's counts
+ * join the reference while it holds fewer than `window` vectors. Load guard
+ * [ViBE, Incremental placement update: done once every GPU is within the
+ * tolerance epsilon]: when that replay leaves a rank with more than cap
+ * rows, or (tol_den > 0) with load * tol_den > target * (tol_den + tol_num),
+ * the greedy runs in the same call as on a replan and status[0] gets
+ * MB_ST_REPLANNED | MB_ST_GUARDED. A plan with a rank above its target is
+ * MB_ST_UNBALANCED either way.
  * d = 1 - r.c / (|r| |c|) over the expert counts c and the reference sum r,
  * with exact integer sums, then one division and two square roots in
  * double. A call with BAD_ID or DUP_ID leaves the state unchanged.

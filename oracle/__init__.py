@@ -28,6 +28,7 @@ ELT_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1}
 ST_BAD_ID, ST_DUP_ID, ST_UNBALANCED, ST_CAPACITY = 1, 2, 4, 8
 ST_FATAL = ST_BAD_ID | ST_DUP_ID | ST_CAPACITY
 ST_REPLANNED = 16
+ST_GUARDED = 32
 
 MOVE_FILL_HOST, MOVE_EXCESS_ONLY = 0, 1
 
@@ -59,14 +60,17 @@ class Report(ctypes.Structure):
 
 
 class DriftParams(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("delta_num", "delta_den", "window", "check_every")]
+    """Drift gate and load guard; tol_num = tol_den = 0 (the default) guards
+    the region size only."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("delta_num", "delta_den", "window", "check_every",
+                                             "tol_num", "tol_den")]
 
 
 class _DriftStateC(ctypes.Structure):
     _fields_ = [("have_plan", ctypes.c_int32), ("countdown", ctypes.c_int32),
                 ("nwin", ctypes.c_int32), ("n_moves", ctypes.c_int32),
                 ("calls", ctypes.c_int64), ("replans", ctypes.c_int64),
-                ("last_d", ctypes.c_double),
+                ("guarded", ctypes.c_int64), ("last_d", ctypes.c_double),
                 ("wsum", ctypes.POINTER(ctypes.c_int64)), ("rep", _i32p), ("order", _i32p)]
 
 
@@ -77,12 +81,13 @@ class DriftState:
         self.wsum = np.zeros(n_experts, np.int64)
         self.rep = np.full(n_ranks * slots_per_rank, -1, np.int32)
         self.order = np.full(n_ranks * slots_per_rank, -1, np.int32)
-        self.c = _DriftStateC(0, 0, 0, 0, 0, 0, 0.0,
+        self.c = _DriftStateC(0, 0, 0, 0, 0, 0, 0, 0.0,
                               self.wsum.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                               self.rep.ctypes.data_as(_i32p), self.order.ctypes.data_as(_i32p))
 
     def __getattr__(self, name):
-        if name in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans", "last_d"):
+        if name in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans", "guarded",
+                    "last_d"):
             return getattr(self.c, name)
         raise AttributeError(name)
 

@@ -530,12 +530,34 @@ static double cosine_distance(const int64_t* c, const int64_t* ws, int64_t E) {
   return 1.0 - (double)dot / (sqrt((double)n1) * sqrt((double)n2));
 }
 
+/* Load guard on a replayed placement ([ViBE] Incremental placement update:
+ * a placement is done once every GPU is within the tolerance epsilon of the
+ * balanced time; with time proportional to load over speed that is load_r
+ * <= (1 + epsilon) tau_r): the replay stands when no rank needs more than
+ * cap rows and, with tol_den > 0, load_r * tol_den <= tau_r * (tol_den +
+ * tol_num) for every rank, in exact integers. */
+static int replay_within_guard(const mbref_dims* dm, const int32_t* speed,
+                               const mbref_drift_params* prm, const mbref_plan_out* o) {
+  const int64_t P = dm->n_ranks, NK = (int64_t)dm->n_tokens * dm->top_k;
+  int64_t sum_s = 0;
+  for (int64_t r = 0; r < P; ++r) sum_s += speed ? speed[r] : 1;
+  for (int64_t r = 0; r < P; ++r) {
+    const int64_t load = o->load_post[r];
+    const int64_t tau = (NK * (speed ? speed[r] : 1) + sum_s - 1) / sum_s;
+    if (load > dm->cap) return 0;
+    if (prm->tol_den > 0 && load * prm->tol_den > tau * ((int64_t)prm->tol_den + prm->tol_num))
+      return 0;
+  }
+  return 1;
+}
+
 static int plan_drift_core(const mbref_dims* dm, const int32_t* ids, const int32_t* speed,
                            const mbref_drift_params* prm, mbref_drift_state* st, int repair,
                            mbref_plan_out* o, mbref_report* rep) {
   if (!dm || !o || !prm || !st || !valid_dims(dm)) return MBREF_ERR_INVALID_ARG;
   if (prm->delta_den < 1 || prm->delta_num < 0 || prm->delta_num > prm->delta_den ||
-      prm->window < 1 || prm->window > MBREF_MAX_WINDOW || prm->check_every < 1)
+      prm->window < 1 || prm->window > MBREF_MAX_WINDOW || prm->check_every < 1 ||
+      prm->tol_num < 0 || prm->tol_den < 0)
     return MBREF_ERR_INVALID_ARG;
   const int64_t N = dm->n_tokens, K = dm->top_k, E = dm->n_experts;
   const int64_t P = dm->n_ranks, R = dm->slots_per_rank;
@@ -556,13 +578,24 @@ static int plan_drift_core(const mbref_dims* dm, const int32_t* ids, const int32
   }
   for (int64_t i = 0; i < N * K; ++i) c[ids[i]] += 1;
   /* Replan on the first call, then check every check_every calls. */
-  int replan = !st->have_plan;
+  int replan = !st->have_plan, guarded = 0;
   if (!replan && --st->countdown == 0) {
     st->countdown = prm->check_every;
     st->last_d = cosine_distance(c, st->wsum, E);
     if (st->last_d > (double)prm->delta_num / (double)prm->delta_den) replan = 1;
   }
-  int rc;
+  int rc = MBREF_OK;
+  if (!replan) {
+    const keep_t keep = {st->rep, st->order, st->n_moves};
+    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, &keep, NULL, repair, o, rep);
+    if (rc == MBREF_OK && !replay_within_guard(dm, speed, prm, o)) {
+      replan = 1;
+      guarded = 1;
+    } else if (rc == MBREF_OK && st->nwin < prm->window) {
+      for (int64_t e = 0; e < E; ++e) st->wsum[e] += c[e];
+      st->nwin += 1;
+    }
+  }
   if (replan) {
     rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, NULL, order, repair, o, rep);
     if (rc == MBREF_OK) {
@@ -575,14 +608,8 @@ static int plan_drift_core(const mbref_dims* dm, const int32_t* ids, const int32
       for (int64_t e = 0; e < E; ++e) st->wsum[e] = c[e];
       st->nwin = 1;
       st->replans += 1;
-      o->status[0] |= MBREF_ST_REPLANNED;
-    }
-  } else {
-    const keep_t keep = {st->rep, st->order, st->n_moves};
-    rc = plan_core(dm, ids, speed, MBREF_MOVE_FILL_HOST, &keep, NULL, repair, o, rep);
-    if (rc == MBREF_OK && st->nwin < prm->window) {
-      for (int64_t e = 0; e < E; ++e) st->wsum[e] += c[e];
-      st->nwin += 1;
+      st->guarded += guarded;
+      o->status[0] |= MBREF_ST_REPLANNED | (guarded ? MBREF_ST_GUARDED : 0);
     }
   }
   if (rc == MBREF_OK) st->calls += 1;

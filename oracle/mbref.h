@@ -61,6 +61,10 @@ enum { MBREF_MOVE_FILL_HOST = 0, MBREF_MOVE_EXCESS_ONLY = 1 };
 /* status[0] bit of mbref_plan_drift: this call ran the greedy (no fatal
  * meaning). */
 #define MBREF_ST_REPLANNED 16
+/* status[0] bit of mbref_plan_drift, set with REPLANNED: the kept placement,
+ * replayed on this call's counts, missed the load tolerance or the region
+ * size, so the greedy ran in the same call. */
+#define MBREF_ST_GUARDED 32
 
 /* Largest reference window of mbref_plan_drift (calls). */
 #define MBREF_MAX_WINDOW 4096
@@ -68,9 +72,11 @@ enum { MBREF_MOVE_FILL_HOST = 0, MBREF_MOVE_EXCESS_ONLY = 1 };
 /* Drift gate: replan when d = 1 - cos(current counts, reference) exceeds
  * delta_num / delta_den, checked every check_every calls; the reference is
  * the sum of the count vectors of up to `window` calls since the last
- * replan. */
+ * replan. Load guard: a call that keeps the placement replans after all
+ * when the replay leaves a rank above cap rows or, with tol_den > 0, above
+ * (1 + tol_num / tol_den) times its target (tol_den = 0: cap only). */
 typedef struct mbref_drift_params {
-  int32_t delta_num, delta_den, window, check_every;
+  int32_t delta_num, delta_den, window, check_every, tol_num, tol_den;
 } mbref_drift_params;
 
 /* State carried between the calls of one layer; zero-filled (and arrays of
@@ -81,6 +87,7 @@ typedef struct mbref_drift_state {
   int32_t nwin;       /* count vectors in the reference */
   int32_t n_moves;    /* replicas of the kept placement */
   int64_t calls, replans;
+  int64_t guarded;    /* replans the load guard forced */
   double last_d;      /* distance at the last check */
   int64_t* wsum;      /* [E] sum of the reference's count vectors */
   int32_t* rep;       /* [P*R] kept replica experts */

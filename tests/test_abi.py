@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert mb.version() == 1
+    assert mb.version() == 2
     for code in (mb.OK, mb.ERR_INVALID_ARG, mb.ERR_WORKSPACE, mb.ERR_HIP, mb.ST_BAD_ID,
                  mb.ST_DUP_ID, mb.ST_UNBALANCED, mb.ST_CAPACITY, 12345):
         assert isinstance(mb.strerror(code), str) and mb.strerror(code)

@@ -519,7 +519,7 @@ def _gpu_drift_state(dg):
 
 def _assert_state_equal(state_d, st, E, label):
     h = mb.drift_header(state_d)
-    for key in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans"):
+    for key in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans", "guarded"):
         assert h[key] == getattr(st, key), (label, key, h[key], getattr(st, key))
     # the decision is taken in double on both sides from exact integer sums
     assert h["last_d"] == st.last_d, (label, "last_d", h["last_d"], st.last_d)
@@ -570,30 +570,35 @@ def test_drift_replay_needs_home_above_target_on_gpu():
 @pytest.mark.parametrize("H", [1, 10])
 def test_drift_decode_sequence(H):
     """The 60-pass drift workload through mb_plan_drift and the oracle in
-    lockstep: every call's plan bit-exact, the state (counters, reference,
-    distance) equal after every call; dispatch and combine on three kept
-    calls. Rows are 128 wide here (the plan does not depend on H)."""
+    lockstep, with its load guard (5/4 of the targets) and regions of
+    5/4 S K rows: every call's plan bit-exact, the state (counters,
+    reference, distance) equal after every call, no call fatal; dispatch and
+    combine on three kept calls. Rows are 128 wide here (the plan does not
+    depend on H)."""
     wl = W.get_workload("drift_decode")
-    num, den, win, _ = wl.drift
+    num, den, win, _, tn, td = wl.drift
     dg = mb.Dims.for_workload(wl)
     dg.hidden = 128
     od = O.dims_for(wl)
     od.hidden = 128
     state = _gpu_drift_state(dg)
     st = O.DriftState(wl.n_experts, wl.n_ranks, wl.slots_per_rank)
-    gprm, oprm = mb.DriftParams(num, den, win, H), O.DriftParams(num, den, win, H)
+    gprm, oprm = mb.DriftParams(num, den, win, H, tn, td), O.DriftParams(num, den, win, H, tn, td)
     gp = G.GpuPlan(dg)
-    replans = []
+    replans, guarded, rows_at = [], [], [7, 33, 59]
     for call in range(wl.calls):
         ids, w = W.routing_for(wl, call)
         got = gp.run(ids, drift=(gprm, state)).fetch()
         ref = O.plan(od, ids, drift=(oprm, st))
         G.assert_plan_equal(got, ref)
         _assert_state_equal(state, st, wl.n_experts, f"call {call}")
+        assert not ref.flags & O.ST_FATAL, call
         if ref.flags & O.ST_REPLANNED:
             replans.append(call)
-        if call in (7, 33, 59):
-            assert not ref.flags & O.ST_REPLANNED
+        if ref.flags & O.ST_GUARDED:
+            guarded.append(call)
+        if rows_at and call >= rows_at[0] and not ref.flags & O.ST_REPLANNED:
+            rows_at.pop(0)
             x, xs, _ = W.rows_fp8(wl.seed_for(call), W.TAG_X, 128, n=wl.n_tokens)
             ye = _y_exp_rows(wl.seed_for(call), od, od.n_ranks * od.cap)
             buf, bs, y = G.run_rows(dg, gp, x, xs, ye, w)
@@ -602,9 +607,46 @@ def test_drift_decode_sequence(H):
             assert np.array_equal(buf[used], ref_buf[used]) and np.array_equal(bs[used], ref_bs[used])
             y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, ye)
             G.assert_combine_close(y, y_ref, mag, "bf16")
-    G.log(f"drift_decode H={H}: replans at {replans}")
-    first = {1: [0, 25, 50], 10: [0, 30, 50]}[H]
-    assert replans == first
+    G.log(f"drift_decode H={H}: replans at {replans}, guarded {guarded}")
+    assert not rows_at
+    # the popularity shifts at 25 and 50 are caught in the call itself: by
+    # the check when one runs every call, else by the load guard
+    assert replans == [0, 25, 50]
+    assert guarded == ([] if H == 1 else [25, 50])
+
+
+@pytest.mark.parametrize("cap_q,tol", [(4, (0, 0)), (5, (1, 4)), (5, (3, 100))])
+def test_drift_decode_load_guard_regions(cap_q, tol):
+    """drift_decode in lockstep with the oracle at regions of cap_q/4 S K
+    rows (S K is the library's default) under the load guard alone (0, 0),
+    at 1/4 and at ViBE's 0.03: plans and state bit-exact every call; a call
+    is CAPACITY-fatal only where a fresh greedy plan of that call is too
+    (the guard falls back to that same greedy), so at 5/4 S K none is."""
+    wl = W.get_workload("drift_decode")
+    num, den, win, H = wl.drift[:4]
+    cap = wl.tokens_per_rank * wl.top_k * cap_q // 4
+    dg = mb.Dims.for_workload(wl, cap=cap)
+    dg.hidden = 128
+    od = O.dims_for(wl, cap=cap)
+    od.hidden = 128
+    state = _gpu_drift_state(dg)
+    st = O.DriftState(wl.n_experts, wl.n_ranks, wl.slots_per_rank)
+    gprm, oprm = mb.DriftParams(num, den, win, H, *tol), O.DriftParams(num, den, win, H, *tol)
+    gp = G.GpuPlan(dg)
+    fatal = []
+    for call in range(wl.calls):
+        ids, _ = W.routing_for(wl, call)
+        got = gp.run(ids, drift=(gprm, state)).fetch()
+        ref = O.plan(od, ids, drift=(oprm, st))
+        G.assert_plan_equal(got, ref)
+        _assert_state_equal(state, st, wl.n_experts, f"call {call}")
+        if ref.flags & O.ST_FATAL:
+            fatal.append(call)
+            assert ref.flags & O.ST_REPLANNED, call  # a kept replay never overflows
+            assert O.plan(od, ids).flags & O.ST_CAPACITY, call
+    G.log(f"drift_decode cap {cap} tol {tol}: fatal calls {fatal}, guarded {st.guarded}")
+    if cap_q == 5:
+        assert not fatal
 
 
 def _drift_cases():
@@ -871,8 +913,8 @@ def test_graph_capture_drift_state_advances():
     dg, od = mb.Dims.for_workload(wl), O.dims_for(wl)
     dg.hidden = od.hidden = 128
     d = G.dev()
-    num, den, win, _ = wl.drift
-    gprm, oprm = mb.DriftParams(num, den, win, 2), O.DriftParams(num, den, win, 2)
+    num, den, win, _, tn, td = wl.drift
+    gprm, oprm = mb.DriftParams(num, den, win, 2, tn, td), O.DriftParams(num, den, win, 2, tn, td)
     ids_s = torch.from_numpy(W.routing_for(wl, 0)[0]).to(d)
     state = mb.alloc_drift_state(dg, d)
     st = O.DriftState(wl.n_experts, wl.n_ranks, wl.slots_per_rank)

@@ -89,6 +89,15 @@ MUTANTS = [
      "(double)y_scale[p * (H / 128) + i / 128];", "(double)y_scale[p * (H / 128) + i / 256];"),
     ("fp8 decode without the subnormal range",
      "    v = ldexp((double)m, -9);", "    v = ldexp(1.0 + m / 8.0, -7);"),
+    ("load guard ignores the region size",
+     "    if (load > dm->cap) return 0;\n", ""),
+    ("load guard tolerance exclusive",
+     "if (prm->tol_den > 0 && load * prm->tol_den > tau", "if (prm->tol_den > 0 && load * prm->tol_den >= tau"),
+    ("load guard against the largest target",
+     "const int64_t tau = (NK * (speed ? speed[r] : 1) + sum_s - 1) / sum_s;",
+     "const int64_t tau = (NK * (speed ? speed[P - 1] : 1) + sum_s - 1) / sum_s;"),
+    ("load guard flags the call but keeps the replay",
+     "      replan = 1;\n      guarded = 1;", "      guarded = 1;"),
     ("duplicate ids not flagged",
      "if (ids[t * K + k2] == e) flags |= MBREF_ST_DUP_ID;", "if (0) flags |= MBREF_ST_DUP_ID;"),
 ]

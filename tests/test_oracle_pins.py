@@ -279,6 +279,95 @@ def test_drift_replay_needs_home_above_target():
     assert np.array_equal(p1.slot_quota, [[4, 0], [2, 0], [6, 0]])
 
 
+@pytest.mark.parametrize("cap,tol,kept", [(12, (0, 0), True), (5, (0, 0), False),
+                                           (12, (1, 2), True), (12, (1, 3), False)])
+def test_drift_load_guard_hand_example(cap, tol, kept):
+    """The load guard on the example above (T = 4; call 1 replays to loads
+    [4, 2, 6]). Rank 2 ends at 6 rows: within a region of 12, not of 5; with
+    tolerance 1/2 the limit is 4 * 3/2 = 6 (6 * 2 <= 4 * 3, kept at the
+    boundary), with 1/3 it is 16/3 (6 * 3 > 4 * 4, guarded). Guarded, the
+    greedy runs on c = [4, 2, 6]: rank 2 (x = +2) gives its home expert 2 to
+    rank 1 (x = -2, the only rank below T) with min(4 - 2, 6) = 2 pairs ->
+    loads [4, 4, 4], replica slots [-1, 2, -1]; the reference restarts at
+    [4, 2, 6] and the state counts a second replan, one of them guarded."""
+    d = O.make_dims(12, 1, 3, 3, 1, 4, cap=cap)
+    st = O.DriftState(3, 3, 1)
+    prm = O.DriftParams(1, 1, 4, 1, *tol)
+    c0 = np.array([0] * 6 + [1] * 3 + [2] * 3, np.int32).reshape(-1, 1)
+    assert O.plan(d, c0, drift=(prm, st)).flags == O.ST_REPLANNED
+    c1 = np.array([0] * 4 + [1] * 2 + [2] * 6, np.int32).reshape(-1, 1)
+    p1 = O.plan(d, c1, drift=(prm, st))
+    if kept:
+        assert p1.flags == O.ST_UNBALANCED
+        assert np.array_equal(p1.load_post, [4, 2, 6])
+        assert st.replans == 1 and st.guarded == 0 and st.nwin == 2
+        assert np.array_equal(st.wsum, [10, 5, 9])
+    else:
+        assert p1.flags == O.ST_REPLANNED | O.ST_GUARDED
+        assert np.array_equal(p1.load_post, [4, 4, 4])
+        assert np.array_equal(p1.rep_expert.ravel(), [-1, 2, -1])
+        assert np.array_equal(p1.slot_quota, [[4, 0], [2, 2], [4, 0]])
+        assert st.replans == 2 and st.guarded == 1 and st.nwin == 1
+        assert np.array_equal(st.wsum, [4, 2, 6])
+        assert np.array_equal(st.rep, [-1, 2, -1]) and np.array_equal(st.order, [1, -1, -1])
+        assert st.countdown == 1 and st.n_moves == 1
+    C.check_layout(p1, c1, 3, 3, 1, cap)
+
+
+def test_drift_load_guard_uses_each_ranks_own_target():
+    """With speeds [1, 1, 2] the targets are ceil(12 s_r / 4) = [3, 3, 6].
+    Call 0 (c = [9, 2, 1]): rank 0 gives expert 0 to rank 2 (x = -5) with
+    min(6 - 1, 9) = 5, then to rank 1 (x = -1) with min(3 - 2, 4) = 1 ->
+    loads [3, 3, 6]; kept slots in order: 2, 1.
+    Call 1 (c = [5, 5, 2]): the slot on rank 2 takes min(6 - 2, 5) = 4
+    (home 0 at 5 > 3, host at 2 < 6), the slot on rank 1 nothing (home now
+    at 1) -> loads [1, 5, 6]. Rank 1 is 5/3 of its own target of 3 (and
+    below the largest, 6): tolerance 1/4 guards it (5 * 4 > 3 * 5) and the
+    greedy reaches [3, 3, 6] (expert 0 to rank 2 with 4 pairs, then rank 1,
+    x = +2, gives expert 1 to rank 0, x = -2, with 2); without a tolerance
+    the replay is kept, UNBALANCED."""
+    d = O.make_dims(12, 1, 3, 3, 1, 4, cap=12)
+    sp = np.array([1, 1, 2], np.int32)
+    c0 = np.array([0] * 9 + [1] * 2 + [2], np.int32).reshape(-1, 1)
+    c1 = np.array([0] * 5 + [1] * 5 + [2] * 2, np.int32).reshape(-1, 1)
+    for tol in ((1, 4), (0, 0)):
+        st = O.DriftState(3, 3, 1)
+        prm = O.DriftParams(1, 1, 4, 1, *tol)
+        p0 = O.plan(d, c0, speeds=sp, drift=(prm, st))
+        assert p0.flags == O.ST_REPLANNED and np.array_equal(p0.load_post, [3, 3, 6])
+        assert np.array_equal(st.order, [2, 1, -1])
+        p1 = O.plan(d, c1, speeds=sp, drift=(prm, st))
+        if tol[1]:
+            assert p1.flags == O.ST_REPLANNED | O.ST_GUARDED
+            assert np.array_equal(p1.load_post, [3, 3, 6])
+            assert np.array_equal(p1.rep_expert.ravel(), [1, -1, 0])
+        else:
+            assert p1.flags == O.ST_UNBALANCED
+            assert np.array_equal(p1.load_post, [1, 5, 6])
+
+
+def test_drift_load_guard_adds_no_fatal_call():
+    """drift_decode over its 60 passes with regions of S*K rows: a guarded
+    call runs the same greedy as a fresh plan of that call, so the calls the
+    gate leaves CAPACITY-fatal are among those a fresh greedy leaves fatal;
+    with regions 5/4 S K and tolerance 1/4 no call is fatal. Checked on the
+    first 30 passes (one popularity shift)."""
+    wl = W.get_workload("drift_decode")
+    for cap, tol in ((wl.tokens_per_rank * wl.top_k, (0, 0)),
+                     (wl.tokens_per_rank * wl.top_k * 5 // 4, (1, 4))):
+        d = O.dims_for(wl, cap=cap)
+        st = O.DriftState(wl.n_experts, wl.n_ranks, wl.slots_per_rank)
+        prm = O.DriftParams(*wl.drift[:4], *tol)
+        for call in range(30):
+            ids, _ = W.routing_for(wl, call)
+            p = O.plan(d, ids, drift=(prm, st))
+            if p.flags & O.ST_FATAL:
+                assert tol == (0, 0) and O.plan(d, ids).flags & O.ST_CAPACITY, call
+            assert p.status[2] <= cap or p.flags & O.ST_REPLANNED, call
+            if tol[1] and not p.flags & O.ST_FATAL:
+                assert p.status[2] * 4 <= 5 * p.status[1] or p.flags & O.ST_GUARDED, call
+
+
 @pytest.mark.parametrize("H", [1, 3, 4])
 def test_drift_replans_every_check_when_counts_are_orthogonal(H):
     """Each call sends every token to one expert, a different one each call:
@@ -319,7 +408,7 @@ def test_drift_rejects_bad_params_and_keeps_state_on_bad_ids():
     d = O.make_dims(8, 1, 4, 2, 1, 4, cap=8)
     ids = np.zeros((8, 1), np.int32)
     for prm in ((1, 0, 2, 1), (-1, 2, 2, 1), (3, 2, 2, 1), (1, 2, 0, 1), (1, 2, 2, 0),
-                (1, 2, 4097, 1)):
+                (1, 2, 4097, 1), (1, 2, 2, 1, -1, 4), (1, 2, 2, 1, 1, -4)):
         st = O.DriftState(4, 2, 1)
         assert O.plan_drift_rc(d, ids, O.DriftParams(*prm), st) == O.ERR_INVALID_ARG, prm
     st = O.DriftState(4, 2, 1)

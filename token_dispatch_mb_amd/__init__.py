@@ -98,8 +98,12 @@ _lib.mb_plan_weighted.restype = ctypes.c_int
 
 class DriftParams(ctypes.Structure):
     """mb_drift_params: replan when d > delta_num / delta_den, checked every
-    check_every calls, reference of up to `window` calls."""
-    _fields_ = [(n, ctypes.c_int32) for n in ("delta_num", "delta_den", "window", "check_every")]
+    check_every calls, reference of up to `window` calls; a kept placement
+    replayed above cap or (tol_den > 0) above (1 + tol_num / tol_den) times a
+    target replans in the same call. tol_num = tol_den = 0 (the default)
+    guards cap only."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("delta_num", "delta_den", "window", "check_every",
+                                             "tol_num", "tol_den")]
 
 
 class _PlanOptionsC(ctypes.Structure):
@@ -130,6 +134,7 @@ EXPORTS = ("mb_version", "mb_strerror", "mb_plan_workspace_bytes", "mb_plan",
            "mb_plan_noalloc", "mb_plan_weighted", "mb_drift_state_bytes", "mb_plan_drift", "mb_plan_ex",
            "mb_dispatch", "mb_combine", "mb_combine_fp8", "mb_plan_status")
 ST_REPLANNED = 16
+ST_GUARDED = 32
 NOALLOC_WS_BYTES = 4 << 20
 MAX_WINDOW = 4096
 MAX_SPEED = 1 << 20
@@ -361,7 +366,8 @@ def drift_header(state: torch.Tensor) -> dict:
     i64 = np.frombuffer(b[16:32], np.int64)
     return {"have_plan": int(i32[0]), "countdown": int(i32[1]), "nwin": int(i32[2]),
             "n_moves": int(i32[3]), "calls": int(i64[0]), "replans": int(i64[1]),
-            "last_d": float(np.frombuffer(b[32:40], np.float64)[0])}
+            "last_d": float(np.frombuffer(b[32:40], np.float64)[0]),
+            "guarded": int(np.frombuffer(b[40:48], np.int64)[0])}
 
 
 def combine_fp8(dims: Dims, bufs: PlanBuffers, y_exp: torch.Tensor, y_scale: torch.Tensor,

@@ -239,7 +239,8 @@ int mb_plan_ex(const mb_dims* dims, const int32_t* ids_dev, const mb_plan_option
   if (prm) {
     if (!aligned16(opt->drift_state)) return MB_ERR_INVALID_ARG;
     if (prm->delta_den < 1 || prm->delta_num < 0 || prm->delta_num > prm->delta_den ||
-        prm->window < 1 || prm->window > MB_MAX_WINDOW || prm->check_every < 1)
+        prm->window < 1 || prm->window > MB_MAX_WINDOW || prm->check_every < 1 ||
+        prm->tol_num < 0 || prm->tol_den < 0)
       return MB_ERR_INVALID_ARG;
   }
   int32_t ones[kMaxRanks];

@@ -39,6 +39,7 @@ struct PlanArgs {
   // drift-gated replanning: state buffer (nullptr: run the greedy every call)
   uint8_t* drift_state;
   int delta_num, delta_den, window, check_every;
+  int tol_num, tol_den;       // load guard on a replayed placement
   int repair;                 // quota repair after placement
   const int32_t* counts;      // [P][E] pairs per (source rank, expert), from k_scan
   int32_t* counts_out;        // the same buffer, cleared when the routing is invalid
@@ -73,7 +74,7 @@ struct PlanSmem {
   int32_t* loadv;   // [64] load after planning
   int32_t* lpre;    // [64] load before planning
   int32_t* tau;     // [64] target of each rank
-  int32_t* misc;    // [8] moves, unbalanced, max load, largest target,
+  int32_t* misc;    // [8] moves, unbalanced, guard replan, largest target,
                     //     replan, checked, next countdown, window size
 };
 
@@ -474,6 +475,37 @@ __device__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
   }
 }
 
+// Wave 0, after replay_kept: the load guard (ViBE, Incremental placement
+// update: a placement is done once every GPU is within the tolerance epsilon
+// of the balanced time, i.e. load_r <= (1 + epsilon) tau_r when time is load
+// over speed). The replay stands when no rank needs more than cap rows and,
+// with tol_den > 0, load * tol_den <= tau * (tol_den + tol_num) on every rank
+// (exact in 64-bit integers). Otherwise the placement state is reset for
+// the greedy, which then runs in this call as on a replan. Returns whether
+// it must run.
+__device__ bool guard_rejects(const PlanArgs& a, PlanSmem& m) {
+  const int lane = threadIdx.x;
+  bool over = false;
+  if (lane < a.P) {
+    const long long load = m.loadv[lane], tau = m.tau[lane];
+    over = load > a.cap ||
+           (a.tol_den > 0 && load * a.tol_den > tau * ((long long)a.tol_den + a.tol_num));
+  }
+  if (ballot64(over) == 0) return false;
+  for (int e = lane; e < a.E; e += 64) m.qh[e] = m.c[e];
+  for (int i = lane; i < a.P * a.R; i += 64) {
+    m.repE[i] = -1;
+    m.repM[i] = 0;
+  }
+  if (lane == 0) {
+    m.misc[2] = 1;
+    m.misc[4] = 1;
+    m.misc[6] = a.check_every;
+  }
+  wave_lds_sync();
+  return true;
+}
+
 // Wave 0, after the placement: ISER-MoE HALO-Q stage 4, quota repair. A
 // circle-method tournament (n = P rounded up to even players, n - 1 rounds;
 // player 0 stays at position 0, the others rotate one position per round;
@@ -723,6 +755,7 @@ __device__ void drift_update(const PlanArgs& a, PlanSmem& m) {
     if (replan) h.n_moves = moves;
     h.calls += 1;
     h.replans += replan;
+    h.guarded += m.misc[2];
     h.last_d = m.dmisc[0];
     *v.hdr = h;
   }
@@ -780,7 +813,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     }
   }
   if (tid < 64) m.tau[tid] = tid < P ? tau_v : 0;
-  if (tid == 0) m.misc[3] = a.tau_max;
+  if (tid == 0) {
+    m.misc[2] = 0;
+    m.misc[3] = a.tau_max;
+  }
   for (int i = tid; i < P * R; i += kPlanThreads) {
     m.repE[i] = -1;
     m.repM[i] = 0;
@@ -808,14 +844,19 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   const bool drift = a.drift_state != nullptr;
   if (tid < 64) {
     if (drift) drift_decide(a, m);
-    if (drift && !m.misc[4])
+    bool greedy = true;
+    if (drift && !m.misc[4]) {
       replay_kept(a, m);
-    else if ((long long)a.N * a.K >= kPackedPairsLimit || Eh > 32)
-      greedy_lds(a, m);
-    else if (P <= 32)
-      greedy_regs_for<32>(a, m);
-    else
-      greedy_regs_for<64>(a, m);
+      greedy = guard_rejects(a, m);
+    }
+    if (greedy) {
+      if ((long long)a.N * a.K >= kPackedPairsLimit || Eh > 32)
+        greedy_lds(a, m);
+      else if (P <= 32)
+        greedy_regs_for<32>(a, m);
+      else
+        greedy_regs_for<64>(a, m);
+    }
     if (a.repair && R > 0) quota_repair(a, m);
   }
   __syncthreads();
@@ -866,7 +907,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
     const int max_load = wave_max_i32(mymax);
     if (tid == 0) {
       a.status[0] = (m.misc[1] ? MB_ST_UNBALANCED : 0) | (max_load > a.cap ? MB_ST_CAPACITY : 0) |
-                    (drift && m.misc[4] ? MB_ST_REPLANNED : 0);
+                    (drift && m.misc[4] ? MB_ST_REPLANNED : 0) |
+                    (drift && m.misc[2] ? MB_ST_GUARDED : 0);
       a.status[1] = m.misc[3];
       a.status[2] = max_load;
       a.status[3] = m.misc[0];
@@ -905,6 +947,8 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.delta_den = drift ? drift->delta_den : 1;
   a.window = drift ? drift->window : 1;
   a.check_every = drift ? drift->check_every : 1;
+  a.tol_num = drift ? drift->tol_num : 0;
+  a.tol_den = drift ? drift->tol_den : 0;
   a.repair = repair;
   a.counts = o.counts;
   a.counts_out = o.counts;
