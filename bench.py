@@ -11,19 +11,23 @@ Expert outputs are the dispatched rows (identity experts), written once
 before timing into a buffer of their own.
 
 A workload of several calls (the 61 layer calls of decode_drift) steps
-through its calls, one per step (the default step count is the number of
-calls), so plan times cover every call. A workload whose row buffers are
+through its calls, one per step (by default five passes over them), so plan
+times cover every call five times. A workload whose row buffers are
 smaller than the last-level cache runs on several buffer sets in turn (at
 least 1 GiB in all), so no step reads what a recent step left in cache.
 
 A workload planned with drift-gated replanning (drift_decode) steps through
 its sequence of calls, one call per step, from a fresh drift state when the
-timed steps begin; the line then also reports which calls replanned, their
-plan time against the kept calls' and against replanning every call, and
-the rank imbalance each way.
+timed steps begin; the line then also reports, per gate setting (none, the
+workload's, a check every call, ViBE's tolerance 0.03, the region-size guard
+alone), plan times over five fresh passes, replans, replica weight copies at
+W = 3 H I b bytes each, and the rank imbalance.
 
 Prints one JSON line. `value` is dispatch + combine algorithmic bytes per
-step divided by the whole step time (plan included). `roofline` refers to the
+step divided by the whole step time (plan included), from HIP events around
+the timed steps; the steps are queued behind 30 ms of unrelated GPU work
+(`backlog_ms`, inside the wall-clock bracket) so that the host's launch rate
+does not idle the GPU between short steps. `roofline` refers to the
 kernel with the larger share of the step (HIP events on the launch stream);
 `cpu_baseline` times the CPU oracle (single thread) on half of the
 tokens of the same workload.
@@ -88,35 +92,124 @@ def measured_traffic(kernel: str, workload: str):
     return float(m.group(1)) if m else None
 
 
-def _drift_report(steps, plan_ms, plan_call, bufs, drift, mean_load, mb, torch, np):
-    """Untimed replays of the timed sequence from a fresh state: which calls
-    replanned and the imbalance after each call, then every call planned
-    without the gate (its plan time by HIP events, and its imbalance)."""
-    drift[1].zero_()
-    replanned, ir_gated = [], []
-    for i in range(steps):
-        plan_call(i)
-        st = mb.plan_status(bufs)
-        replanned.append(bool(st[0] & mb.ST_REPLANNED))
-        ir_gated.append(float(st[2]) / mean_load)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    ir_always = []
-    for i in range(steps):
-        ev[i][0].record()
-        plan_call(i, gated=False)
-        ev[i][1].record()
-        ir_always.append(float(mb.plan_status(bufs)[2]) / mean_load)
-    always_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    rp = np.array(replanned)
+# Intermediate width I of one expert for the replica weight bytes W = 3 H I b
+# (ISER-MoE, Key Formula: gate, up and down projections), the MoonEP
+# benchmark's H' = 2048; b = 1 byte (fp8 weights, as the rows).
+WEIGHT_I = 2048
+WEIGHT_B = 1
+
+
+def _backlog(torch, dev, ms: float) -> None:
+    """Queue about `ms` of GPU work (fills of a 2 GiB buffer, their rate
+    measured once) on the current stream, so that the host can queue the
+    work after it before the GPU reaches it: event pairs around that work
+    then time the GPU alone, not the host's launch rate."""
+    st = _backlog.__dict__
+    if "buf" not in st:
+        st["buf"] = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st["buf"].fill_(0)
+        a.record()
+        for _ in range(4):
+            st["buf"].fill_(0)
+        b.record()
+        torch.cuda.synchronize()
+        st["fill_ms"] = a.elapsed_time(b) / 4
+    for _ in range(max(1, int(ms / st["fill_ms"]) + 1)):
+        st["buf"].fill_(0)
+
+
+def _drift_report(wl, dims, ids_all, ws, bufs, speeds, repair, mb, torch, np, reps=5):
+    """Untimed against the step, timed per plan: the sequence of calls planned
+    from a fresh state `reps` times under each gate setting (and with no
+    gate: the greedy every call), one HIP event pair around each plan, the
+    plans queued back to back. Per setting: plan µs (mean, p50, p99, and the
+    replanned and kept calls' means), replans and guard replans per
+    sequence, replica slots whose expert changed from the previous call
+    (each a weight copy of W bytes) and calls that kept every slot, the rank
+    imbalance max load / mean load after each call, and fatal calls. Each
+    setting runs twice: once to time the host's queueing, then behind a
+    backlog of GPU work longer than that, so the plans run back to back."""
+    dev = bufs.status.device
+    T, PR = wl.calls, bufs.rep_expert.numel()
+    w_bytes = 3 * wl.hidden * WEIGHT_I * WEIGHT_B
+    mean_load = wl.n_tokens * wl.top_k / wl.n_ranks
+    g = tuple(wl.drift)
+    settings = [("every_call", None), ("gate", g), ("gate_check_every_1", g[:3] + (1,) + g[4:]),
+                ("gate_tol_0.03", g[:4] + (3, 100)), ("gate_cap_only", g[:4] + (0, 0))]
+    rows = {}
+    for name, prm in settings:
+        drift = None
+        if prm is not None:
+            drift = (mb.DriftParams(*prm), mb.alloc_drift_state(dims, dev))
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps * T)]
+        rep_d = torch.empty((reps * T, PR), dtype=torch.int32, device=dev)
+        st_d = torch.empty((reps * T, 4), dtype=torch.int32, device=dev)
+
+        def run():
+            for r in range(reps):
+                if drift is not None:
+                    drift[1].zero_()
+                for c in range(T):
+                    i = r * T + c
+                    ev[i][0].record()
+                    mb.plan(dims, ids_all[c], ws, bufs, speeds=speeds, drift=drift, repair=repair)
+                    ev[i][1].record()
+                    rep_d[i].copy_(bufs.rep_expert.view(-1))
+                    st_d[i].copy_(bufs.status)
+
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        run()
+        host_ms = (time.perf_counter() - h0) * 1e3
+        torch.cuda.synchronize()
+        _backlog(torch, dev, 2 * host_ms + 5)
+        run()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+        reps_h = rep_d.cpu().numpy().reshape(reps, T, PR)
+        st = st_d.cpu().numpy().reshape(reps, T, 4)
+        flags = st[..., 0]
+        replanned = np.ones_like(flags, bool) if drift is None else (flags & mb.ST_REPLANNED) != 0
+        guarded = (flags & mb.ST_GUARDED) != 0
+        # a slot whose expert differs from the previous call's needs that
+        # expert's weights copied in (an emptied slot needs nothing)
+        changed = ((reps_h[:, 1:] != reps_h[:, :-1]) & (reps_h[:, 1:] >= 0)).sum(axis=2)
+        ir = st[..., 2] / mean_load
+        rp = replanned.ravel()
+        row = {
+            "params": None if prm is None else dict(zip(
+                ("delta_num", "delta_den", "window", "check_every", "tol_num", "tol_den"), prm)),
+            "plan_us": {"mean": round(float(us.mean()), 2), "p50": round(float(np.median(us)), 2),
+                        "p99": round(float(np.percentile(us, 99)), 2),
+                        "replanned_mean": round(float(us[rp].mean()), 2) if rp.any() else None,
+                        "kept_mean": round(float(us[~rp].mean()), 2) if (~rp).any() else None},
+            "replans": int(replanned[0].sum()),
+            "guard_replans": int(guarded[0].sum()),
+            "replanned_calls": [int(c) for c in np.flatnonzero(replanned[0])],
+            "replica_changes": int(changed[0].sum()),
+            "calls_keeping_every_slot": int((changed[0] == 0).sum()),
+            "replica_weight_bytes": int(changed[0].sum()) * w_bytes,
+            "ir_after_mean": round(float(ir[0].mean()), 5),
+            "ir_after_max": round(float(ir[0].max()), 5),
+            "unbalanced_calls": int(((flags[0] & mb.ST_UNBALANCED) != 0).sum()),
+            "fatal_calls": int(((flags[0] & mb.ST_FATAL) != 0).sum()),
+            "same_every_rep": bool((st == st[:1]).all() and (reps_h == reps_h[:1]).all()),
+        }
+        if name == "gate":
+            row["changes_per_call"] = [0] + [int(v) for v in changed[0]]
+            row["header"] = mb.drift_header(drift[1])
+        rows[name] = row
+        log(f"drift {name}: plan p50 {row['plan_us']['p50']} us, {row['replans']} replans "
+            f"({row['guard_replans']} guarded), {row['replica_changes']} replica changes, "
+            f"IR mean {row['ir_after_mean']}, fatal {row['fatal_calls']}")
+    every = rows["every_call"]["replica_changes"]
     return {
-        "replanned_calls": [i for i in range(steps) if replanned[i]],
-        "plan_us_replanned": round(float(plan_ms[rp].mean()) * 1e3, 2) if rp.any() else None,
-        "plan_us_kept": round(float(plan_ms[~rp].mean()) * 1e3, 2) if (~rp).any() else None,
-        "plan_us_every_call_replanned": round(float(always_ms.mean()) * 1e3, 2),
-        "ir_after_mean_gated": round(float(np.mean(ir_gated)), 5),
-        "ir_after_max_gated": round(float(np.max(ir_gated)), 5),
-        "ir_after_mean_every_call_replanned": round(float(np.mean(ir_always)), 5),
-        "header": mb.drift_header(drift[1]),
+        "calls": T, "reps": reps, "plans_timed_per_setting": reps * T,
+        "weight_bytes_per_replica": w_bytes,
+        "weight_model": f"W = 3*H*I*b, H={wl.hidden}, I={WEIGHT_I}, b={WEIGHT_B}",
+        "replica_weight_bytes_avoided_by_gate": (every - rows["gate"]["replica_changes"]) * w_bytes,
+        "settings": rows,
     }
 
 
@@ -216,6 +309,111 @@ def cpu_baseline(wl, fraction: int = 2) -> dict:
     }
 
 
+CEILING_LIB = os.path.join(ROOT, "token_dispatch_mb_amd", "libmoebal_ceiling.so")
+
+
+def _ceiling_lib():
+    import ctypes
+
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(CEILING_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.mbc_fill.argtypes = [vp, i64, vp]
+    L.mbc_copy.argtypes = [vp, vp, i64, vp]
+    L.mbc_read.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
+    L.mbc_scatter_write.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+    L.mbc_row_write.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+    for f in (L.mbc_fill, L.mbc_copy, L.mbc_read, L.mbc_scatter_write, L.mbc_row_write):
+        f.restype = ctypes.c_int
+    return L
+
+
+def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
+    """k_dispatch against reference kernels of the same traffic on this GPU
+    (libmoebal_ceiling): the dispatch's writes alone at its own rows, in its
+    own wave shape and one row per wave; a contiguous fill of the same write
+    bytes; a contiguous read of its read bytes; a contiguous copy. Each
+    kernel `reps` times, HIP events around each launch on the launch stream,
+    the median kept; inputs resident and the plan made before."""
+    import ctypes
+
+    L = _ceiling_lib()
+    ids, _ = W.routing_for(wl)
+    x, xs = W.token_rows(wl)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+    x_d = torch.from_numpy(x).view(tdt[wl.dtype_in]).to(dev)
+    xs_d = torch.from_numpy(xs).to(dev) if xs is not None else None
+    del x
+    bufs = mb.PlanBuffers.allocate(dims, dev)
+    ws = mb.alloc_workspace(dims, dev)
+    mb.plan(dims, torch.from_numpy(ids).to(dev), ws, bufs, speeds=W.rank_speeds(wl))
+    status = mb.plan_status(bufs)
+    if status[0] & mb.ST_FATAL:
+        raise RuntimeError(f"plan failed: {status.tolist()}")
+    row_bytes = x_d[0].numel() * x_d.element_size()
+    N, K = wl.n_tokens, wl.top_k
+    buf = torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_in], device=dev)
+    bs = (torch.empty((dims.rows, wl.hidden // 128), dtype=torch.float32, device=dev)
+          if wl.dtype_in == "fp8" else None)
+    write_b, read_b = N * K * row_bytes, N * row_bytes
+    assert write_b <= buf.numel() * buf.element_size() and read_b == x_d.numel() * x_d.element_size()
+    half = write_b // 32 * 16  # the copy reads and writes this many bytes
+    src = torch.empty(half, dtype=torch.uint8, device=dev)
+    src.fill_(0x3c)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    key = (ctypes.c_uint32 * 4)(0xDEADBEEF, 0x0BADF00D, 0x12345678, 0x9ABCDEF1)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def check(rc, name):
+        if rc != 0:
+            raise RuntimeError(f"{name} returned {rc}")
+
+    cases = {
+        "k_dispatch": (lambda: mb.dispatch(dims, bufs, x_d, buf, xs_d, bs),
+                       read_b + write_b + N * K * 4),
+        "k_scatter_write": (lambda: check(L.mbc_scatter_write(ptr(bufs.pos), ptr(buf), N, K,
+                                                              row_bytes, dims.rows, sh),
+                                          "mbc_scatter_write"), write_b + N * K * 4),
+        "k_row_write": (lambda: check(L.mbc_row_write(ptr(bufs.pos), ptr(buf), N, K, row_bytes,
+                                                      dims.rows, sh), "mbc_row_write"),
+                        write_b + N * K * 4),
+        "k_fill": (lambda: check(L.mbc_fill(ptr(buf), write_b, sh), "mbc_fill"), write_b),
+        "k_read": (lambda: check(L.mbc_read(ptr(x_d), read_b, key, ptr(sink), sh), "mbc_read"),
+                   read_b),
+        "k_copy": (lambda: check(L.mbc_copy(ptr(src), ptr(buf), half, sh), "mbc_copy"), 2 * half),
+    }
+    out = {}
+    for name, (fn, nbytes) in cases.items():
+        fn()  # warm
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)[reps // 2]
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "bytes": int(nbytes), "gbps": round(gbps, 1),
+                     "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        log(f"ceiling {name}: {us:.1f} us, {gbps:.0f} GB/s")
+    if int(sink.abs().sum()) != 0:
+        raise RuntimeError("mbc_read found its key in the rows")
+    d_us = out["k_dispatch"]["us"]
+    best_w = min(out["k_scatter_write"]["us"], out["k_row_write"]["us"])
+    return {
+        "workload": wl.name, "reps": reps, "row_bytes": row_bytes,
+        "kernels": out,
+        "dispatch_time_over_its_writes_alone": round(d_us / best_w, 4),
+        "dispatch_gbps_over_write_only_scatter_gbps": round(
+            out["k_dispatch"]["gbps"] / max(out["k_scatter_write"]["gbps"],
+                                            out["k_row_write"]["gbps"]), 4),
+        "write_only_scatter_over_fill": round(out["k_fill"]["us"] / best_w, 4),
+    }
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -230,7 +428,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; a drift-gated workload: its call count)")
+                    help="timed steps (default 20; a workload of several calls: 5 passes over "
+                         "them; a drift-gated workload: one pass, its call count)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--combine-fp8", action="store_true",
@@ -243,6 +442,12 @@ def main() -> int:
                     help="plan with the quota repair after placement (mb_plan_ex)")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="leave out the CPU oracle leg (for profiler runs)")
+    ap.add_argument("--no-backlog", action="store_true",
+                    help="start the timed steps on an idle GPU (no queued work ahead of them)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only time k_dispatch beside the reference kernels that bound it "
+                         "(its writes alone, a fill, a read, a copy) and print that report")
+    ap.add_argument("--reps", type=int, default=9, help="launches per kernel with --ceiling")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's device copy of MIB MiB three times (the known-size "
                          "reference for the HBM byte counters) and exit")
@@ -275,8 +480,12 @@ def main() -> int:
     wl = W.get_workload(args.workload)
     dims = mb.Dims.for_workload(wl)
     log(f"workload {wl.name}: {wl.note}")
+    if args.ceiling:
+        print(json.dumps({"ceiling": ceiling_report(wl, dims, mb, W, torch, np, dev, args.reps)}),
+              flush=True)
+        return 0
     if args.steps is None:
-        args.steps = wl.calls if wl.calls > 1 else 20
+        args.steps = 20 if wl.calls == 1 else wl.calls if wl.drift else 5 * wl.calls
 
     ids, w = W.routing_for(wl)
     x, xs = W.token_rows(wl)
@@ -329,14 +538,9 @@ def main() -> int:
         drift = (mb.DriftParams(*wl.drift), mb.alloc_drift_state(dims, dev))
         log(f"drift gate {wl.drift}")
 
-    def plan_call(i, gated=True):
-        if drift is None:
-            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, repair=args.repair)
-        elif gated:
-            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, drift=drift,
-                    repair=args.repair)
-        else:
-            mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, repair=args.repair)
+    def plan_call(i):
+        mb.plan(dims, ids_all[i % wl.calls], ws, bufs, speeds=speeds, drift=drift,
+                repair=args.repair)
 
     wir_equal = None
     if speeds is not None:
@@ -385,14 +589,22 @@ def main() -> int:
 
     for i in range(args.warmup):
         step(i)
+    _backlog(torch, dev, 0.0)  # its buffer and fill rate, before timing
     if drift is not None:
         drift[1].zero_()  # the timed steps run the sequence from its first call
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The timed steps queue behind about backlog_ms of unrelated GPU work
+    # (fills of a scratch buffer, before the first step's event), so the host
+    # starts that far ahead: a step shorter than its launches' host time
+    # (decode) is then timed on the GPU, not at the host's launch rate.
+    backlog_ms = 0.0 if args.no_backlog else 30.0
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
+    if backlog_ms:
+        _backlog(torch, dev, backlog_ms)
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
@@ -429,8 +641,9 @@ def main() -> int:
 
     drift_report = None
     if drift is not None:
-        drift_report = _drift_report(args.steps, plan_ms, plan_call, bufs, drift, mean_load, mb,
-                                     torch, np)
+        drift_report = _drift_report(wl, dims, ids_all, ws, bufs, speeds, args.repair, mb, torch,
+                                     np)
+        drift[1].zero_()
 
     graph_report = None
     if args.graph:
@@ -489,6 +702,10 @@ def main() -> int:
                     "p99": round(float(np.percentile(plan_ms, 99)) * 1e3, 2)},
         "dispatch_us": round(disp_ms.mean() * 1e3, 2),
         "combine_us": round(comb_ms.mean() * 1e3, 2),
+        "dispatch_us_p50_p99": [round(float(np.median(disp_ms)) * 1e3, 2),
+                                round(float(np.percentile(disp_ms, 99)) * 1e3, 2)],
+        "combine_us_p50_p99": [round(float(np.median(comb_ms)) * 1e3, 2),
+                               round(float(np.percentile(comb_ms, 99)) * 1e3, 2)],
         "dispatch_gbps": round(d_gbps, 2),
         "combine_gbps": round(c_gbps, 2),
         "algorithmic_bytes": {"dispatch": ab["dispatch"], "combine": ab["combine"]},
@@ -504,6 +721,7 @@ def main() -> int:
             graph_report, value=round((ab["dispatch"] + ab["combine"]) /
                                       (graph_report["ms_per_step"] * 1e-3) / 1e9, 2)),
         "wall_s_timed": round(t_wall, 4),
+        "backlog_ms": backlog_ms,
         "roofline": {
             "kernel": dominant,
             "bound": "hbm",

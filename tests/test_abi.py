@@ -28,6 +28,18 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_ceiling_library_exports_its_header():
+    """libmoebal_ceiling.so (reference kernels for bench.py --ceiling)
+    exports every symbol include/moebal_ceiling.h declares."""
+    text = open(os.path.join(ROOT, "include", "moebal_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(mbc_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["mbc_copy", "mbc_fill", "mbc_read", "mbc_row_write", "mbc_scatter_write"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "token_dispatch_mb_amd", "libmoebal_ceiling.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+
+
 def test_version_and_strerror():
     assert mb.version() == 2
     for code in (mb.OK, mb.ERR_INVALID_ARG, mb.ERR_WORKSPACE, mb.ERR_HIP, mb.ST_BAD_ID,

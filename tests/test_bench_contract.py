@@ -89,6 +89,57 @@ def test_fp8_and_drift_reports():
     assert r.returncode == 0, r.stderr[-2000:]
     d = json.loads(r.stdout.strip().splitlines()[-1])
     g = d["drift_gate"]
-    assert d["steps"] == d["config"]["calls"] and g["replanned_calls"][0] == 0
-    assert 0 < g["plan_us_kept"] and 0 < g["plan_us_replanned"]
-    assert g["header"]["replans"] == len(g["replanned_calls"])
+    assert d["steps"] == d["config"]["calls"] == g["calls"]
+    s = g["settings"]
+    gate = s["gate"]
+    assert gate["replanned_calls"][0] == 0 and gate["same_every_rep"]
+    assert 0 < gate["plan_us"]["kept_mean"] and 0 < gate["plan_us"]["replanned_mean"]
+    assert gate["header"]["replans"] == gate["replans"] == len(gate["replanned_calls"])
+    assert gate["header"]["guarded"] == gate["guard_replans"]
+    assert len(gate["changes_per_call"]) == g["calls"]
+    assert s["every_call"]["replans"] == g["calls"] and s["every_call"]["params"] is None
+    for row in s.values():
+        assert row["fatal_calls"] == 0
+    assert g["replica_weight_bytes_avoided_by_gate"] == (
+        s["every_call"]["replica_changes"] - gate["replica_changes"]) * g["weight_bytes_per_replica"]
+
+
+@pytest.mark.gpu
+def test_ceiling_report():
+    """bench.py --ceiling: k_dispatch beside its reference kernels, each
+    timed; the write-only scatter writes what its header says where pos says."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    r = _bench("--workload", "mixtral", "--ceiling", "--reps", "3")
+    assert r.returncode == 0, r.stderr[-2000:]
+    c = json.loads(r.stdout.strip().splitlines()[-1])["ceiling"]
+    assert set(c["kernels"]) == {"k_dispatch", "k_scatter_write", "k_row_write", "k_fill",
+                                 "k_read", "k_copy"}
+    for k in c["kernels"].values():
+        assert k["us"] > 0 and 0 < k["frac_of_peak"] < 1.2
+    import ctypes
+
+    import bench
+
+    L = bench._ceiling_lib()
+    dev = torch.device("cuda:0")
+    N, K, rows, rb = 300, 4, 1500, 2064  # rows of 129 lanes: a ragged second span
+    pos = torch.randperm(rows, device=dev)[: N * K].to(torch.int32)
+    pos[5] = -1  # skipped
+    pos[7] = rows  # skipped
+    for fn in (L.mbc_scatter_write, L.mbc_row_write):
+        buf = torch.full((rows, rb // 4), -1, dtype=torch.int32, device=dev)
+        rc = fn(ctypes.c_void_p(pos.data_ptr()), ctypes.c_void_p(buf.data_ptr()), N, K, rb, rows,
+                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0
+        torch.cuda.synchronize()
+        b = buf.view(rows, rb // 16, 4).cpu()
+        p = pos.cpu()
+        hit = torch.zeros(rows, dtype=torch.bool)
+        for j in range(N * K):
+            r = int(p[j])
+            if 0 <= r < rows:
+                hit[r] = True
+                assert bool((b[r, :, 0] == j // K).all())
+                assert bool((b[r, :, 1] == torch.arange(rb // 16)).all())
+        assert bool((b[~hit] == -1).all())
