@@ -11,8 +11,9 @@ Expert outputs are the dispatched rows (identity experts), written once
 before timing into a buffer of their own.
 
 A workload of several calls (the 61 layer calls of decode_drift) steps
-through its calls, one per step (by default five passes over them), so plan
-times cover every call five times. A workload whose row buffers are
+through its calls, one per step (by default one pass), so plan times cover
+every call; the line also gives the plan's p50/p99 over five passes of its
+calls planned back to back (`plan_us_passes`). A workload whose row buffers are
 smaller than the last-level cache runs on several buffer sets in turn (at
 least 1 GiB in all), so no step reads what a recent step left in cache.
 
@@ -47,7 +48,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dispatch+combine GB/s (% of HBM peak) and mb_plan µs per MoE layer call"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_k_dispatch_k_combine_dsv3_prefill.md")
+# committed counter summaries, one per workload: pmc_k_dispatch_k_combine_<workload>.md
+PROFILE_PMC = os.path.join(ROOT, "profiles", "pmc_k_dispatch_k_combine_{}.md")
 ROW_KERNEL_SOURCE = os.path.join(ROOT, "token_dispatch_mb_amd", "csrc", "rows.hip")
 
 
@@ -76,12 +78,13 @@ def source_hash() -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if absent, for another workload, or taken on different
-    kernel source."""
-    if not os.path.exists(PROFILE_PMC):
+    """HBM bytes per launch of `kernel` from the workload's committed
+    rocprofv3 counter summary, or None if absent or taken on different kernel
+    source."""
+    path = PROFILE_PMC.format(workload)
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_PMC).read()
+    text = open(path).read()
     m = re.search(r"^source_sha256_16:\s*(\w+)", text, re.M)
     if not m or m.group(1) != source_hash():
         return None
@@ -119,6 +122,43 @@ def _backlog(torch, dev, ms: float) -> None:
         st["buf"].fill_(0)
 
 
+def _time_plans(dims, ids_all, ws, bufs, speeds, repair, drift, reps, mb, torch, np):
+    """The calls of ids_all planned `reps` times in turn (a drift state, if
+    any, zero-filled before each pass), one HIP event pair around each plan,
+    run twice: once to time the host's queueing, then behind a backlog of GPU
+    work longer than that, so the plans run back to back on the GPU. Returns
+    the µs of each plan [reps * calls] and each plan's replica slots and
+    status word [reps, calls, ...]."""
+    dev = bufs.status.device
+    T, PR = ids_all.shape[0], bufs.rep_expert.numel()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps * T)]
+    rep_d = torch.empty((reps * T, PR), dtype=torch.int32, device=dev)
+    st_d = torch.empty((reps * T, 4), dtype=torch.int32, device=dev)
+
+    def run():
+        for r in range(reps):
+            if drift is not None:
+                drift[1].zero_()
+            for c in range(T):
+                i = r * T + c
+                ev[i][0].record()
+                mb.plan(dims, ids_all[c], ws, bufs, speeds=speeds, drift=drift, repair=repair)
+                ev[i][1].record()
+                rep_d[i].copy_(bufs.rep_expert.view(-1))
+                st_d[i].copy_(bufs.status)
+
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    run()
+    host_ms = (time.perf_counter() - h0) * 1e3
+    torch.cuda.synchronize()
+    _backlog(torch, dev, 2 * host_ms + 5)
+    run()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    return us, rep_d.cpu().numpy().reshape(reps, T, PR), st_d.cpu().numpy().reshape(reps, T, 4)
+
+
 def _drift_report(wl, dims, ids_all, ws, bufs, speeds, repair, mb, torch, np, reps=5):
     """Untimed against the step, timed per plan: the sequence of calls planned
     from a fresh state `reps` times under each gate setting (and with no
@@ -127,11 +167,10 @@ def _drift_report(wl, dims, ids_all, ws, bufs, speeds, repair, mb, torch, np, re
     replanned and kept calls' means), replans and guard replans per
     sequence, replica slots whose expert changed from the previous call
     (each a weight copy of W bytes) and calls that kept every slot, the rank
-    imbalance max load / mean load after each call, and fatal calls. Each
-    setting runs twice: once to time the host's queueing, then behind a
-    backlog of GPU work longer than that, so the plans run back to back."""
+    imbalance max load / mean load after each call, and fatal calls (plans
+    timed by _time_plans)."""
     dev = bufs.status.device
-    T, PR = wl.calls, bufs.rep_expert.numel()
+    T = wl.calls
     w_bytes = 3 * wl.hidden * WEIGHT_I * WEIGHT_B
     mean_load = wl.n_tokens * wl.top_k / wl.n_ranks
     g = tuple(wl.drift)
@@ -142,33 +181,8 @@ def _drift_report(wl, dims, ids_all, ws, bufs, speeds, repair, mb, torch, np, re
         drift = None
         if prm is not None:
             drift = (mb.DriftParams(*prm), mb.alloc_drift_state(dims, dev))
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps * T)]
-        rep_d = torch.empty((reps * T, PR), dtype=torch.int32, device=dev)
-        st_d = torch.empty((reps * T, 4), dtype=torch.int32, device=dev)
-
-        def run():
-            for r in range(reps):
-                if drift is not None:
-                    drift[1].zero_()
-                for c in range(T):
-                    i = r * T + c
-                    ev[i][0].record()
-                    mb.plan(dims, ids_all[c], ws, bufs, speeds=speeds, drift=drift, repair=repair)
-                    ev[i][1].record()
-                    rep_d[i].copy_(bufs.rep_expert.view(-1))
-                    st_d[i].copy_(bufs.status)
-
-        torch.cuda.synchronize()
-        h0 = time.perf_counter()
-        run()
-        host_ms = (time.perf_counter() - h0) * 1e3
-        torch.cuda.synchronize()
-        _backlog(torch, dev, 2 * host_ms + 5)
-        run()
-        torch.cuda.synchronize()
-        us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
-        reps_h = rep_d.cpu().numpy().reshape(reps, T, PR)
-        st = st_d.cpu().numpy().reshape(reps, T, 4)
+        us, reps_h, st = _time_plans(dims, ids_all, ws, bufs, speeds, repair, drift, reps, mb, torch,
+                                     np)
         flags = st[..., 0]
         replanned = np.ones_like(flags, bool) if drift is None else (flags & mb.ST_REPLANNED) != 0
         guarded = (flags & mb.ST_GUARDED) != 0
@@ -428,8 +442,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; a workload of several calls: 5 passes over "
-                         "them; a drift-gated workload: one pass, its call count)")
+                    help="timed steps (default 20; a workload of several calls: one pass over "
+                         "them, its call count)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--combine-fp8", action="store_true",
@@ -485,7 +499,7 @@ def main() -> int:
               flush=True)
         return 0
     if args.steps is None:
-        args.steps = 20 if wl.calls == 1 else wl.calls if wl.drift else 5 * wl.calls
+        args.steps = 20 if wl.calls == 1 else wl.calls
 
     ids, w = W.routing_for(wl)
     x, xs = W.token_rows(wl)
@@ -639,6 +653,17 @@ def main() -> int:
         err = (y_last[samp].float() - x_d[samp].float() * w_d[samp].sum(1, keepdim=True)).abs().max()
         log(f"identity-expert check: max |y - x * sum(w)| = {float(err):.3e}")
 
+    plan_passes = None
+    if wl.calls > 1 and drift is None:
+        us, _, _ = _time_plans(dims, ids_all, ws, bufs, speeds, args.repair, None, 5, mb, torch, np)
+        plan_passes = {"passes": 5, "calls": wl.calls, "mean": round(float(us.mean()), 2),
+                       "p50": round(float(np.median(us)), 2),
+                       "p99": round(float(np.percentile(us, 99)), 2)}
+        log(f"plan over 5 passes of {wl.calls} calls: p50 {plan_passes['p50']} us, "
+            f"p99 {plan_passes['p99']} us")
+        mb.plan(dims, ids_all[(args.steps - 1) % wl.calls], ws, bufs, speeds=speeds,
+                repair=args.repair)
+
     drift_report = None
     if drift is not None:
         drift_report = _drift_report(wl, dims, ids_all, ws, bufs, speeds, args.repair, mb, torch,
@@ -700,6 +725,7 @@ def main() -> int:
         "dispatch_combine_gbps": round(bytes_step / ((disp_ms.mean() + comb_ms.mean()) * 1e-3) / 1e9, 2),
         "plan_us": {"mean": round(plan_ms.mean() * 1e3, 2), "p50": round(float(np.median(plan_ms)) * 1e3, 2),
                     "p99": round(float(np.percentile(plan_ms, 99)) * 1e3, 2)},
+        "plan_us_passes": plan_passes,
         "dispatch_us": round(disp_ms.mean() * 1e3, 2),
         "combine_us": round(comb_ms.mean() * 1e3, 2),
         "dispatch_us_p50_p99": [round(float(np.median(disp_ms)) * 1e3, 2),
