@@ -308,6 +308,29 @@ def test_plan_around_the_packed_key_limit(N, K, E, P, R, kind):
     assert ref.status[0] == 0 and ref.status[3] > 0
 
 
+@pytest.mark.parametrize("din,H,K", [
+    ("bf16", 1024, 2), ("bf16", 1024, 3), ("bf16", 2048, 16), ("f32", 512, 8), ("fp8", 2048, 4),
+    ("fp8", 4096, 8),                       # rows of whole 2 KiB spans: k_dispatch_span
+    ("bf16", 1024, 1), ("bf16", 1536, 8), ("bf16", 1024, 17), ("fp8", 1152, 5),  # k_dispatch
+])
+def test_dispatch_kernels_by_row_shape(din, H, K):
+    """Rows made of whole 2 KiB spans with 2 <= K <= 16 go through the
+    span kernel (one workgroup of K waves per span, staged in LDS), the rest
+    through the one-wave-per-KiB kernel; both bit-exact against the oracle
+    on a ragged token count, fp8 scale rows included, padding rows left
+    untouched; and with a bad id neither writes anything."""
+    P, eh, S, R = 4, 8, 77, 2
+    E = P * eh
+    ids, _ = W.routing(P * S, E, K, W.NOISE_GUMBEL, 1.1, 1.0, 5300 + H + K)
+    _edge(P * S, K, E, P, R, H, ids, cap=2 * S * K, din=din, dout="bf16", seed=H + K,
+          label=f"dispatch {din} H{H} K{K}")
+    bad = ids.copy()
+    bad[S + 3, 0] = E
+    ref = _edge(P * S, K, E, P, R, H, bad, cap=2 * S * K, din=din, dout="bf16", seed=H,
+                label=f"dispatch {din} H{H} K{K} bad id")
+    assert ref.status[0] & O.ST_BAD_ID
+
+
 def test_fp8_rows_and_scales_small():
     ids, _ = W.routing(512, 32, 4, W.NOISE_GUMBEL, 1.1, 1.0, 21)
     _edge(512, 4, 32, 8, 1, 256, ids, din="fp8", dout="bf16", label="fp8")

@@ -2,8 +2,9 @@
 //
 // The kernels are HBM-bound byte movers: one wave64 per part of a token's
 // row, a token's parts on consecutive waves; dispatch moves 1 KiB parts in
-// 16-byte lane chunks (global_load/store_dwordx4), the combines 512-byte
-// parts in 8-byte lane chunks. The part size and the cache hint of each
+// 16-byte lane chunks (global_load/store_dwordx4), or, for rows of whole
+// 2 KiB spans, one span per workgroup of K waves staged once in LDS; the
+// combines move 512-byte parts in 8-byte lane chunks. The part size and the cache hint of each
 // access (temporal or nontemporal) are the ones measured fastest on MI355X
 // for that kernel's traffic mix; see the comment at each kernel.
 //
@@ -91,6 +92,49 @@ __global__ __launch_bounds__(kRowThreads) void k_dispatch(
         const int p = pt[k];
         if ((unsigned)p < (unsigned)rows) bs[(size_t)p * nsc + c] = xs[(size_t)t * nsc + c];
       }
+    }
+  }
+}
+
+// Dispatch of rows made of whole 2 KiB spans (2 <= K <= 16): a workgroup
+// of K waves per (token, span); the span's 128 lane chunks are loaded once
+// into LDS, then wave k writes the whole span to row pos[t][k] (two 1 KiB
+// stores per lane, 2 KiB contiguous per wave). On MI355X this beat the
+// one-wave-per-chunk kernel by 2 % at 131072 tokens x 8 x 14336 B (3.08 vs
+// 3.16 ms): the destination rows receive 2 KiB runs instead of 1 KiB ones
+// (write-only, those runs alone measured 5.80 against 5.56 TB/s), while the
+// load is shared by the K waves. Spans of 1, 3 and 4 KiB were 22, 7 and 11 %
+// slower than 2 KiB ones; on fp8 rows of 7168 B (3.5 spans) this kernel lost.
+// For fp8 rows the first span's waves also copy the token's scale row to
+// their destination, 16-byte units when the scale arrays allow (vec4).
+constexpr int kSpanChunks = 128;  // 16-byte lane chunks per 2 KiB span
+
+template <int KT>
+__global__ __launch_bounds__(1024) void k_dispatch_span(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ status, u32x4* __restrict__ buf, int K_, int rb16, int spans,
+    int rows, const float* __restrict__ xs, float* __restrict__ bs, int nsc, int vec4) {
+  __shared__ u32x4 span[kSpanChunks];
+  const int K = KT ? KT : K_;
+  const int lane = threadIdx.x & 63, k = threadIdx.x >> 6;
+  const int t = blockIdx.x / spans, h = blockIdx.x - t * spans;
+  if (status[0] & MB_ST_FATAL) return;  // the same word for every thread
+  const int base = h * kSpanChunks;
+  const int p = pos[(size_t)t * K + k];
+  if (threadIdx.x < kSpanChunks) span[threadIdx.x] = x[(size_t)t * rb16 + base + threadIdx.x];
+  __syncthreads();
+  if ((unsigned)p >= (unsigned)rows) return;
+  u32x4* dst = buf + (size_t)p * rb16 + base;
+  dst[lane] = span[lane];
+  dst[64 + lane] = span[64 + lane];
+  if (h == 0 && nsc > 0) {
+    if (vec4) {
+      const int cu = nsc >> 2;
+      const u32x4* src = reinterpret_cast<const u32x4*>(xs) + (size_t)t * cu;
+      u32x4* d4 = reinterpret_cast<u32x4*>(bs) + (size_t)p * cu;
+      for (int u = lane; u < cu; u += 64) d4[u] = src[u];
+    } else {
+      for (int u = lane; u < nsc; u += 64) bs[(size_t)p * nsc + u] = xs[(size_t)t * nsc + u];
     }
   }
 }
@@ -293,6 +337,14 @@ hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* 
   const int64_t waves = (int64_t)d.n_tokens * wpt;
   const dim3 grid((unsigned)((waves + kWavesPerRowBlock - 1) / kWavesPerRowBlock));
   const int vec4 = nsc % 4 == 0 && ((uintptr_t)x_scale & 15u) == 0 && ((uintptr_t)buf_scale & 15u) == 0;
+  if (rb16 % kSpanChunks == 0 && d.top_k >= 2 && d.top_k <= 16) {
+    const int spans = rb16 / kSpanChunks;
+    const dim3 sgrid((unsigned)((int64_t)d.n_tokens * spans));
+    MB_DISPATCH_TOPK(d.top_k, k_dispatch_span, sgrid, dim3(64 * d.top_k), 0, st,
+                     static_cast<const u32x4*>(x), o.pos, o.status, static_cast<u32x4*>(buf),
+                     d.top_k, rb16, spans, rows, x_scale, buf_scale, nsc, vec4);
+    return hipGetLastError();
+  }
   MB_DISPATCH_TOPK(d.top_k, k_dispatch, grid, dim3(kRowThreads), 0, st,
                    static_cast<const u32x4*>(x), o.pos, o.status, static_cast<u32x4*>(buf),
                    d.n_tokens, d.top_k, rb16, wpt, rows, x_scale, buf_scale, nsc, vec4);
