@@ -9,10 +9,11 @@
  * pos gives. These kernels take that traffic apart: a contiguous fill and
  * copy of the same byte count (what HBM streams), a contiguous read (the
  * read side alone), and the dispatch's own writes with no reads — the same
- * pos, the same rows, the same 16-byte lane stores in the same wave and
- * workgroup shape as k_dispatch, or one destination row per wave in 2 KiB
- * runs. Comparing k_dispatch with them says how much of its time the
- * scattered writes alone cost.
+ * pos, the same rows, the same 16-byte lane stores, in the two shapes of
+ * libmoebal's dispatch kernels: one wave per 1 KiB of a row (k_dispatch),
+ * or a workgroup of K waves per 2 KiB span, one destination row per wave
+ * (k_dispatch_span). Comparing the dispatch with them says how much of its
+ * time the scattered writes alone cost.
  *
  * All entry points enqueue one kernel on `stream` and return 0, or -1 for
  * invalid arguments (nothing enqueued), or the HIP error code of the launch.
@@ -49,9 +50,9 @@ int mbc_read(const void* src, int64_t bytes, const uint32_t key[4], void* sink,
 int mbc_scatter_write(const int32_t* pos, void* buf, int32_t n_tokens, int32_t top_k,
                       int32_t row_bytes, int32_t rows, hipStream_t stream);
 
-/* The same writes, one destination row per wave: a workgroup of top_k
- * waves covers 2 KiB of one token's row, wave k writing that span of row
- * pos[t * top_k + k] contiguously. top_k in [1, 16]. */
+/* The same writes in k_dispatch_span's shape, one destination row per wave:
+ * a workgroup of top_k waves covers 2 KiB of one token's row, wave k writing
+ * that span of row pos[t * top_k + k] contiguously. top_k in [1, 16]. */
 int mbc_row_write(const int32_t* pos, void* buf, int32_t n_tokens, int32_t top_k,
                   int32_t row_bytes, int32_t rows, hipStream_t stream);
 

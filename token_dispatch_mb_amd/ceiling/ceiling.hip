@@ -2,11 +2,12 @@
 // (the MoonEP dispatch, "What MoonEP enforces and how": each token row read
 // once and written to its K rows of the expert-grouped buffer).
 //
-// k_dispatch moves N row reads and N*K row writes, the writes scattered over
-// the buffer by pos. Against it: a contiguous fill and copy (HBM streaming),
-// a contiguous read, and the dispatch's own writes with the reads taken out —
-// in k_dispatch's own shape (one 1 KiB lane span per wave, four waves per
-// workgroup, K stores per lane) and with one destination row per wave.
+// The dispatch moves N row reads and N*K row writes, the writes scattered
+// over the buffer by pos. Against it: a contiguous fill and copy (HBM
+// streaming), a contiguous read, and the dispatch's own writes with the reads
+// taken out — in k_dispatch's shape (one 1 KiB lane span per wave, four waves
+// per workgroup, K stores per lane) and in k_dispatch_span's (a workgroup of
+// K waves per 2 KiB span, one destination row per wave).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
