@@ -84,8 +84,7 @@ def test_fp8_and_drift_reports():
     d = json.loads(r.stdout.strip().splitlines()[-1])
     assert d["dtype"] == "fp8" and d["config"]["workload"] == "decode_drift"
     assert d["config"]["expert_outputs"] == "fp8+scales"
-    pp = d["plan_us_passes"]
-    assert pp["passes"] == 5 and pp["calls"] == 61 and 0 < pp["p50"] <= pp["p99"]
+    assert 0 < d["plan_us"]["p50"] <= d["plan_us"]["p99"]
     assert d["roofline"]["frac"] == pytest.approx(d["roofline"]["achieved"] / 8000.0, rel=1e-3)
     r = _bench("--workload", "drift_decode", "--warmup", "1", "--skip-cpu-baseline")
     assert r.returncode == 0, r.stderr[-2000:]
