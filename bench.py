@@ -338,18 +338,21 @@ def _ceiling_lib():
     L.mbc_read.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
     L.mbc_scatter_write.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     L.mbc_row_write.argtypes = [vp, vp, i32, i32, i32, i32, vp]
-    for f in (L.mbc_fill, L.mbc_copy, L.mbc_read, L.mbc_scatter_write, L.mbc_row_write):
+    L.mbc_gather_xor.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    for f in (L.mbc_fill, L.mbc_copy, L.mbc_read, L.mbc_scatter_write, L.mbc_row_write,
+              L.mbc_gather_xor):
         f.restype = ctypes.c_int
     return L
 
 
 def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
-    """k_dispatch against reference kernels of the same traffic on this GPU
-    (libmoebal_ceiling): the dispatch's writes alone at its own rows, in its
-    own wave shape and one row per wave; a contiguous fill of the same write
-    bytes; a contiguous read of its read bytes; a contiguous copy. Each
-    kernel `reps` times, HIP events around each launch on the launch stream,
-    the median kept; inputs resident and the plan made before."""
+    """The dispatch and the combine against reference kernels of the same
+    traffic on this GPU (libmoebal_ceiling): the dispatch's writes alone at
+    its own rows, one KiB per wave and one row per wave; a contiguous fill of
+    the same write bytes; a contiguous read of its read bytes; a contiguous
+    copy; the combine's gathers and writes with an XOR for its arithmetic.
+    Each kernel `reps` times, HIP events around each launch on the launch
+    stream, the median kept; inputs resident and the plan made before."""
     import ctypes
 
     L = _ceiling_lib()
@@ -370,6 +373,14 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
     buf = torch.empty((dims.rows, wl.hidden), dtype=tdt[wl.dtype_in], device=dev)
     bs = (torch.empty((dims.rows, wl.hidden // 128), dtype=torch.float32, device=dev)
           if wl.dtype_in == "fp8" else None)
+    _, w = W.routing_for(wl)
+    w_d = torch.from_numpy(w).to(dev)
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16}[wl.dtype_out]
+    out_row = wl.hidden * (4 if wl.dtype_out == "f32" else 2)
+    # expert outputs: the dispatch buffer itself when the row types agree
+    ye = buf if wl.dtype_in == wl.dtype_out else torch.zeros((dims.rows, wl.hidden), dtype=odt,
+                                                              device=dev)
+    y = torch.empty((N, wl.hidden), dtype=odt, device=dev)
     write_b, read_b = N * K * row_bytes, N * row_bytes
     assert write_b <= buf.numel() * buf.element_size() and read_b == x_d.numel() * x_d.element_size()
     half = write_b // 32 * 16  # the copy reads and writes this many bytes
@@ -398,6 +409,11 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
         "k_read": (lambda: check(L.mbc_read(ptr(x_d), read_b, key, ptr(sink), sh), "mbc_read"),
                    read_b),
         "k_copy": (lambda: check(L.mbc_copy(ptr(src), ptr(buf), half, sh), "mbc_copy"), 2 * half),
+        "k_combine": (lambda: mb.combine(dims, bufs, ye, w_d, y),
+                      N * K * out_row + N * K * 8 + N * out_row),
+        "k_gather_xor": (lambda: check(L.mbc_gather_xor(ptr(bufs.pos), ptr(ye), ptr(y), N, K, out_row,
+                                                        dims.rows, sh), "mbc_gather_xor"),
+                         N * K * out_row + N * K * 4 + N * out_row),
     }
     out = {}
     for name, (fn, nbytes) in cases.items():
@@ -425,6 +441,8 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
             out["k_dispatch"]["gbps"] / max(out["k_scatter_write"]["gbps"],
                                             out["k_row_write"]["gbps"]), 4),
         "write_only_scatter_over_fill": round(out["k_fill"]["us"] / best_w, 4),
+        "combine_gbps_over_gather_xor_gbps": round(out["k_combine"]["gbps"] /
+                                                   out["k_gather_xor"]["gbps"], 4),
     }
 
 

@@ -13,7 +13,10 @@
  * libmoebal's dispatch kernels: one wave per 1 KiB of a row (k_dispatch),
  * or a workgroup of K waves per 2 KiB span, one destination row per wave
  * (k_dispatch_span). Comparing the dispatch with them says how much of its
- * time the scattered writes alone cost.
+ * time the scattered writes alone cost. For the combine (K expert-output
+ * rows gathered per token, weighted and summed, one row written) one kernel
+ * moves the same bytes in k_combine's shape with an XOR in place of the
+ * fp32 arithmetic.
  *
  * All entry points enqueue one kernel on `stream` and return 0, or -1 for
  * invalid arguments (nothing enqueued), or the HIP error code of the launch.
@@ -55,6 +58,15 @@ int mbc_scatter_write(const int32_t* pos, void* buf, int32_t n_tokens, int32_t t
  * that span of row pos[t * top_k + k] contiguously. top_k in [1, 16]. */
 int mbc_row_write(const int32_t* pos, void* buf, int32_t n_tokens, int32_t top_k,
                   int32_t row_bytes, int32_t rows, hipStream_t stream);
+
+/* The combine's traffic alone: for token t < n_tokens, y row t (row_bytes)
+ * = XOR over k < top_k of y_exp row pos[t * top_k + k] (rows of row_bytes,
+ * `rows` rows; entries outside [0, rows) are skipped), in k_combine's shape:
+ * one wave per 512 bytes of an output row (8-byte lane chunks), 16 waves per
+ * workgroup, a lane's top_k loads issued before their use, loads and stores
+ * nontemporal. top_k in [1, 32]. */
+int mbc_gather_xor(const int32_t* pos, const void* y_exp, void* y, int32_t n_tokens,
+                   int32_t top_k, int32_t row_bytes, int32_t rows, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,8 @@ def test_ceiling_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "moebal_ceiling.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(mbc_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["mbc_copy", "mbc_fill", "mbc_read", "mbc_row_write", "mbc_scatter_write"]
+    assert names == ["mbc_copy", "mbc_fill", "mbc_gather_xor", "mbc_read", "mbc_row_write",
+                     "mbc_scatter_write"]
     lib = ctypes.CDLL(os.path.join(ROOT, "token_dispatch_mb_amd", "libmoebal_ceiling.so"))
     for n in names:
         assert hasattr(lib, n), n

@@ -115,7 +115,7 @@ def test_ceiling_report():
     assert r.returncode == 0, r.stderr[-2000:]
     c = json.loads(r.stdout.strip().splitlines()[-1])["ceiling"]
     assert set(c["kernels"]) == {"k_dispatch", "k_scatter_write", "k_row_write", "k_fill",
-                                 "k_read", "k_copy"}
+                                 "k_read", "k_copy", "k_combine", "k_gather_xor"}
     for k in c["kernels"].values():
         assert k["us"] > 0 and 0 < k["frac_of_peak"] < 1.2
     import ctypes
@@ -144,3 +144,17 @@ def test_ceiling_report():
                 assert bool((b[r, :, 0] == j // K).all())
                 assert bool((b[r, :, 1] == torch.arange(rb // 16)).all())
         assert bool((b[~hit] == -1).all())
+    # the gather: y row t = XOR of the rows pos[t][k] (skipped entries add nothing)
+    ye = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows, rb // 4), dtype=torch.int32, device=dev)
+    y = torch.full((N, rb // 4), 7, dtype=torch.int32, device=dev)
+    rc = L.mbc_gather_xor(ctypes.c_void_p(pos.data_ptr()), ctypes.c_void_p(ye.data_ptr()),
+                          ctypes.c_void_p(y.data_ptr()), N, K, rb, rows,
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    p = pos.view(N, K).long()
+    ok = (p >= 0) & (p < rows)
+    g = ye[p.clamp(0, rows - 1)] * ok.unsqueeze(-1)
+    exp = g[:, 0]
+    for k in range(1, K):
+        exp = exp ^ g[:, k]
+    assert torch.equal(y, exp)

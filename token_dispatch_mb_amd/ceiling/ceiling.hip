@@ -7,7 +7,8 @@
 // streaming), a contiguous read, and the dispatch's own writes with the reads
 // taken out — in k_dispatch's shape (one 1 KiB lane span per wave, four waves
 // per workgroup, K stores per lane) and in k_dispatch_span's (a workgroup of
-// K waves per 2 KiB span, one destination row per wave).
+// K waves per 2 KiB span, one destination row per wave). And the combine's
+// traffic without its arithmetic: K gathered row loads per lane, one store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,6 +17,7 @@
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -83,6 +85,46 @@ __global__ __launch_bounds__(1024) void k_row_write(const int32_t* __restrict__ 
     const int i = (s * 2 + c) * 64 + lane;
     if (i < rb16) buf[(size_t)p * rb16 + i] = u32x4{(unsigned)t, (unsigned)i, 3u, 4u};
   }
+}
+
+// The combine's traffic without its arithmetic, in k_combine's shape: one
+// wave per 512 B of an output row (8-byte lane chunks), 16 waves per
+// workgroup, a lane's K row loads issued before use (nontemporal), their XOR
+// stored once (nontemporal).
+constexpr int kGatherThreads = 1024;
+constexpr int kGatherWaves = kGatherThreads / 64;
+
+template <int KT>
+__global__ __launch_bounds__(kGatherThreads) void k_gather_xor(const int32_t* __restrict__ pos,
+                                                               const u32x2* __restrict__ ye,
+                                                               u32x2* __restrict__ y, int N, int K_,
+                                                               int rc, int wpt, int rows) {
+  const int K = KT ? KT : K_;
+  const int lane = threadIdx.x & 63;
+  const int gw = uniform(blockIdx.x * kGatherWaves + (threadIdx.x >> 6));
+  const int t = gw / wpt, part = gw - t * wpt;
+  if (t >= N) return;
+  const int ci = part * 64 + lane;
+  if (ci >= rc) return;
+  const int32_t* pt = pos + (size_t)t * K;
+  u32x2 acc = u32x2{0u, 0u};
+  if constexpr (KT > 0) {
+    u32x2 v[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      const int p = pt[k];
+      const bool ok = (unsigned)p < (unsigned)rows;
+      v[k] = ok ? __builtin_nontemporal_load(ye + (size_t)p * rc + ci) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) acc ^= v[k];
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const int p = pt[k];
+      if ((unsigned)p < (unsigned)rows) acc ^= __builtin_nontemporal_load(ye + (size_t)p * rc + ci);
+    }
+  }
+  __builtin_nontemporal_store(acc, y + (size_t)t * rc + ci);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -161,6 +203,24 @@ int mbc_row_write(const int32_t* pos, void* buf, int32_t N, int32_t K, int32_t r
   if (blocks == 0) return 0;
   hipLaunchKernelGGL(k_row_write, dim3((unsigned)blocks), dim3(64 * K), 0, st, pos,
                      static_cast<u32x4*>(buf), N, K, rb16, spans, rows);
+  return hipGetLastError();
+}
+
+int mbc_gather_xor(const int32_t* pos, const void* y_exp, void* y, int32_t N, int32_t K,
+                   int32_t row_bytes, int32_t rows, hipStream_t st) {
+  if (!rows_ok(pos, y_exp, N, K, row_bytes, rows, 32) || !y || !aligned16(y)) return -1;
+  const int rc = row_bytes / 8, wpt = (rc + 63) / 64;
+  const int64_t waves = (int64_t)N * wpt, blocks = (waves + kGatherWaves - 1) / kGatherWaves;
+  if (waves > 0x7fffffff) return -1;
+  if (blocks == 0) return 0;
+  const dim3 g((unsigned)blocks), b(kGatherThreads);
+  const auto* src = static_cast<const u32x2*>(y_exp);
+  auto* out = static_cast<u32x2*>(y);
+  switch (K) {
+    case 8: hipLaunchKernelGGL(k_gather_xor<8>, g, b, 0, st, pos, src, out, N, K, rc, wpt, rows); break;
+    case 2: hipLaunchKernelGGL(k_gather_xor<2>, g, b, 0, st, pos, src, out, N, K, rc, wpt, rows); break;
+    default: hipLaunchKernelGGL(k_gather_xor<0>, g, b, 0, st, pos, src, out, N, K, rc, wpt, rows); break;
+  }
   return hipGetLastError();
 }
 
