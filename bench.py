@@ -352,7 +352,12 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
     the same write bytes; a contiguous read of its read bytes; a contiguous
     copy; the combine's gathers and writes with an XOR for its arithmetic.
     Each kernel `reps` times, HIP events around each launch on the launch
-    stream, the median kept; inputs resident and the plan made before."""
+    stream, the median kept; inputs resident and the plan made before. Every
+    timed launch follows an untimed read of 512 MiB of a buffer of its own
+    (torch's max reduction, so that profiles tell it from these kernels),
+    which leaves nothing of the kernels' data in the 256 MB last-level cache
+    (back to back, the combine measured 8 % slower: its previous launch's
+    output lines were still cached)."""
     import ctypes
 
     L = _ceiling_lib()
@@ -387,6 +392,7 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
     src = torch.empty(half, dtype=torch.uint8, device=dev)
     src.fill_(0x3c)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    evict_buf = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
     key = (ctypes.c_uint32 * 4)(0xDEADBEEF, 0x0BADF00D, 0x12345678, 0x9ABCDEF1)
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -415,11 +421,15 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
                                                         dims.rows, sh), "mbc_gather_xor"),
                          N * K * out_row + N * K * 4 + N * out_row),
     }
+    def evict():
+        evict_buf.max()
+
     out = {}
     for name, (fn, nbytes) in cases.items():
         fn()  # warm
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for e in ev:
+            evict()
             e[0].record()
             fn()
             e[1].record()

@@ -110,14 +110,16 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_xor(const int32_t* __
   u32x2 acc = u32x2{0u, 0u};
   if constexpr (KT > 0) {
     u32x2 v[KT];
+    bool ok[KT];
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
+    for (int k = 0; k < KT; ++k) {  // as k_combine: every load issued, at row 0 when skipped
       const int p = pt[k];
-      const bool ok = (unsigned)p < (unsigned)rows;
-      v[k] = ok ? __builtin_nontemporal_load(ye + (size_t)p * rc + ci) : u32x2{0u, 0u};
+      ok[k] = (unsigned)p < (unsigned)rows;
+      v[k] = __builtin_nontemporal_load(ye + (ok[k] ? (size_t)p : 0) * rc + ci);
     }
 #pragma unroll
-    for (int k = 0; k < KT; ++k) acc ^= v[k];
+    for (int k = 0; k < KT; ++k)
+      if (ok[k]) acc ^= v[k];
   } else {
     for (int k = 0; k < K; ++k) {
       const int p = pt[k];
