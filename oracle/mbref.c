@@ -58,9 +58,10 @@
  * placements of the tiny workload, hand-derived worked examples, the E1
  * table of [ISER], numpy for dispatch and combine, and planted mistakes that
  * must fail them. Parity unpinned: the exact choices of the greedy, the
- * drift gate and the quota repair follow the readings above, which no page
- * illustrates with a worked example of its own; they are pinned only by the
- * hand-derived examples, the invariants and the exhaustive bound.
+ * drift gate with its load guard and the quota repair follow the readings
+ * above, which no page illustrates with a worked example of its own; they
+ * are pinned only by the hand-derived examples, the invariants and the
+ * exhaustive bound.
  */
 #include "mbref.h"
 
