@@ -387,6 +387,8 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
                                                               device=dev)
     y = torch.empty((N, wl.hidden), dtype=odt, device=dev)
     write_b, read_b = N * K * row_bytes, N * row_bytes
+    # fp8 rows: the dispatch also reads each scale row once and writes it K times
+    scale_b = N * (1 + K) * (wl.hidden // 128) * 4 if wl.dtype_in == "fp8" else 0
     assert write_b <= buf.numel() * buf.element_size() and read_b == x_d.numel() * x_d.element_size()
     half = write_b // 32 * 16  # the copy reads and writes this many bytes
     src = torch.empty(half, dtype=torch.uint8, device=dev)
@@ -404,7 +406,7 @@ def ceiling_report(wl, dims, mb, W, torch, np, dev, reps: int) -> dict:
 
     cases = {
         "k_dispatch": (lambda: mb.dispatch(dims, bufs, x_d, buf, xs_d, bs),
-                       read_b + write_b + N * K * 4),
+                       read_b + write_b + N * K * 4 + scale_b),
         "k_scatter_write": (lambda: check(L.mbc_scatter_write(ptr(bufs.pos), ptr(buf), N, K,
                                                               row_bytes, dims.rows, sh),
                                           "mbc_scatter_write"), write_b + N * K * 4),
