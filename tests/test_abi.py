@@ -41,6 +41,41 @@ def test_ceiling_library_exports_its_header():
         assert hasattr(lib, n), n
 
 
+def test_ceiling_library_refuses_bad_arguments_on_the_host():
+    """Invalid sizes, alignments and top-K values return -1 before anything
+    is launched (so this needs no GPU)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "token_dispatch_mb_amd", "libmoebal_ceiling.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mbc_fill.argtypes = [vp, i64, vp]
+    lib.mbc_copy.argtypes = [vp, vp, i64, vp]
+    lib.mbc_read.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_uint32), vp, vp]
+    for f in (lib.mbc_scatter_write, lib.mbc_row_write):
+        f.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+    lib.mbc_gather_xor.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    a, b = vp(1 << 20), vp((1 << 20) + 8)  # 16-byte aligned / misaligned (never dereferenced)
+    key = (ctypes.c_uint32 * 4)(1, 2, 3, 4)
+    assert lib.mbc_fill(None, 16, None) == -1
+    assert lib.mbc_fill(b, 16, None) == -1
+    assert lib.mbc_fill(a, 24, None) == -1
+    assert lib.mbc_fill(a, -16, None) == -1
+    assert lib.mbc_copy(a, b, 16, None) == -1
+    assert lib.mbc_read(a, 16, None, a, None) == -1
+    assert lib.mbc_read(a, 16, key, b, None) == -1
+    for K in (0, 33, -1):
+        assert lib.mbc_scatter_write(a, a, 8, K, 1024, 64, None) == -1
+        assert lib.mbc_gather_xor(a, a, a, 8, K, 1024, 64, None) == -1
+    assert lib.mbc_row_write(a, a, 8, 17, 1024, 64, None) == -1
+    for rb in (0, 8, 1000):
+        assert lib.mbc_scatter_write(a, a, 8, 8, rb, 64, None) == -1
+        assert lib.mbc_row_write(a, a, 8, 8, rb, 64, None) == -1
+    assert lib.mbc_scatter_write(a, b, 8, 8, 1024, 64, None) == -1
+    assert lib.mbc_scatter_write(a, a, -1, 8, 1024, 64, None) == -1
+    assert lib.mbc_gather_xor(a, a, b, 8, 8, 1024, 64, None) == -1
+    # nothing to do: no launch, success
+    assert lib.mbc_fill(a, 0, None) == 0
+    assert lib.mbc_scatter_write(a, a, 0, 8, 1024, 64, None) == 0
+
+
 def test_version_and_strerror():
     assert mb.version() == 2
     for code in (mb.OK, mb.ERR_INVALID_ARG, mb.ERR_WORKSPACE, mb.ERR_HIP, mb.ST_BAD_ID,
