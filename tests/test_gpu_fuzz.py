@@ -61,7 +61,7 @@ def fuzz_cases(n: int | None = None, seed: int | None = None):
 
 
 def test_random_shapes_plan_bit_exact():
-    n_rows = 0
+    n_rows = n_span = 0
     for (i, P, eh, K, R, S, noise, zipf, beta, cap_kind, speeds) in fuzz_cases():
         E, N = P * eh, P * S
         cap = {"tight": S * K, "double": 2 * S * K, "quad": 4 * S * K,
@@ -79,16 +79,25 @@ def test_random_shapes_plan_bit_exact():
         ref = O.plan(od, ids, speeds=sp)
         G.assert_plan_equal(got, ref)
         if i % 4 == 0 and not ref.status[0] & O.ST_FATAL:
-            x = W.rows_f32(60000 + i, W.TAG_X, H, n=N)
-            ye = W.rows_f32(60000 + i, W.TAG_YEXP, H, n=P * cap)
-            buf, _, y = G.run_rows(dg, gp, x, None, ye, w)
-            ref_buf, _, _ = O.dispatch(od, ref, x, None)
+            # every other dispatched case moves rows of one 2 KiB span (512
+            # f32), the span kernel's shape when 2 <= K <= 16; the rest rows
+            # of 64 bytes (one wave per row chunk)
+            dr, orr, Hr = dg, od, H
+            if (i // 4) % 2 and 2 <= K <= 16 and P * cap * 2048 <= 1 << 28:
+                Hr = 512
+                dr = mb.Dims.make(N, K, E, P, R, Hr, cap=cap, dtype_in="f32", dtype_out="f32")
+                orr = O.make_dims(N, K, E, P, R, Hr, cap=cap, dtype_in="f32", dtype_out="f32")
+                n_span += 1
+            x = W.rows_f32(60000 + i, W.TAG_X, Hr, n=N)
+            ye = W.rows_f32(60000 + i, W.TAG_YEXP, Hr, n=P * cap)
+            buf, _, y = G.run_rows(dr, gp, x, None, ye, w)
+            ref_buf, _, _ = O.dispatch(orr, ref, x, None)
             used = ref.row_src >= 0
             assert np.array_equal(buf[used], ref_buf[used]), label
-            y_ref, mag, _ = O.combine(od, ref.pos, ref.status, w, ye)
+            y_ref, mag, _ = O.combine(orr, ref.pos, ref.status, w, ye)
             G.assert_combine_close(y, y_ref, mag, "f32")
             n_rows += 1
-    assert n_rows > 20
+    assert n_rows > 20 and n_span > 5
 
 
 def test_random_shapes_with_quota_repair_bit_exact():
