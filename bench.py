@@ -102,24 +102,26 @@ WEIGHT_I = 2048
 WEIGHT_B = 1
 
 
+_BACKLOG = {}  # the backlog's scratch buffer and its measured fill time
+
+
 def _backlog(torch, dev, ms: float) -> None:
     """Queue about `ms` of GPU work (fills of a 2 GiB buffer, their rate
     measured once) on the current stream, so that the host can queue the
     work after it before the GPU reaches it: event pairs around that work
     then time the GPU alone, not the host's launch rate."""
-    st = _backlog.__dict__
-    if "buf" not in st:
-        st["buf"] = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    if "buf" not in _BACKLOG:
+        _BACKLOG["buf"] = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st["buf"].fill_(0)
+        _BACKLOG["buf"].fill_(0)
         a.record()
         for _ in range(4):
-            st["buf"].fill_(0)
+            _BACKLOG["buf"].fill_(0)
         b.record()
         torch.cuda.synchronize()
-        st["fill_ms"] = a.elapsed_time(b) / 4
-    for _ in range(max(1, int(ms / st["fill_ms"]) + 1)):
-        st["buf"].fill_(0)
+        _BACKLOG["fill_ms"] = a.elapsed_time(b) / 4
+    for _ in range(max(1, int(ms / _BACKLOG["fill_ms"]) + 1)):
+        _BACKLOG["buf"].fill_(0)
 
 
 def _time_plans(dims, ids_all, ws, bufs, speeds, repair, drift, reps, mb, torch, np):
