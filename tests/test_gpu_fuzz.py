@@ -117,12 +117,14 @@ def test_random_shapes_with_quota_repair_bit_exact():
 
 def test_random_drift_sequences_bit_exact():
     """40 seeded drift-gated sequences of 6-14 calls: random shapes,
-    thresholds (including 0 and 1), windows, check intervals, popularity
-    changes, rank speeds and the quota repair on some; every call's plan and
-    the whole drift state after it equal the oracle's. MB_FUZZ_DRIFT and
-    MB_FUZZ_SEED widen a run."""
+    thresholds (including 0 and 1), windows, check intervals, load-guard
+    tolerances (cap only, 0, 1/20, 1/4), popularity changes, rank speeds and
+    the quota repair on some; every call's plan and the whole drift state
+    after it equal the oracle's. MB_FUZZ_DRIFT and MB_FUZZ_SEED widen a run."""
     seed = int(os.environ.get("MB_FUZZ_SEED", 0))
     rng = np.random.default_rng(777 + seed)
+    trng = np.random.default_rng(991 + seed)  # tolerances, drawn apart so the shapes stay put
+    n_guarded = 0
     for n in range(int(os.environ.get("MB_FUZZ_DRIFT", 40))):
         P = int(rng.choice([1, 2, 5, 16, 31, 32, 33, 64]))
         eh = max(1, min(int(rng.choice([1, 2, 4, 8, 17, 40])), 1024 // P))
@@ -138,15 +140,17 @@ def test_random_drift_sequences_bit_exact():
         speeds = rng.integers(1, 5, P).tolist() if rng.random() < 0.3 else None
         repair = bool(rng.random() < 0.25)
         calls = int(rng.integers(6, 15))
+        tn, td = [(0, 0), (0, 1), (1, 20), (1, 4)][int(trng.integers(0, 4))]
         label = (f"drift fuzz {n}: P={P} Eh={eh} K={K} R={R} S={S} delta={num}/{den} "
-                 f"window={window} every={every} change={change} speeds={speeds} repair={repair}")
+                 f"window={window} every={every} tol={tn}/{td} change={change} speeds={speeds} "
+                 f"repair={repair}")
         G.log(label)
         dg = mb.Dims.make(N, K, E, P, R, 16, cap=cap, dtype_in="f32", dtype_out="f32")
         od = O.make_dims(N, K, E, P, R, 16, cap=cap, dtype_in="f32", dtype_out="f32")
         state = mb.alloc_drift_state(dg, G.dev())
         st = O.DriftState(E, P, R)
-        gprm = mb.DriftParams(num, den, window, every)
-        oprm = O.DriftParams(num, den, window, every)
+        gprm = mb.DriftParams(num, den, window, every, tn, td)
+        oprm = O.DriftParams(num, den, window, every, tn, td)
         gp = G.GpuPlan(dg)
         for call in range(calls):
             ids, _ = W.routing(N, E, K, W.NOISE_GUMBEL, 1.1, 1.0, 70000 + 100 * n + call,
@@ -155,8 +159,11 @@ def test_random_drift_sequences_bit_exact():
             ref = O.plan(od, ids, speeds=speeds, drift=(oprm, st), repair=repair)
             G.assert_plan_equal(got, ref)
             h = mb.drift_header(state)
-            for key in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans"):
+            for key in ("have_plan", "countdown", "nwin", "n_moves", "calls", "replans", "guarded"):
                 assert h[key] == getattr(st, key), (label, call, key, h[key], getattr(st, key))
             assert h["last_d"] == st.last_d, (label, call, "last_d")
             wsum = state[64:64 + 8 * E].cpu().numpy().view(np.int64)
             assert np.array_equal(wsum, st.wsum), (label, call, "reference")
+        n_guarded += st.guarded
+    if int(os.environ.get("MB_FUZZ_DRIFT", 40)) >= 40:
+        assert n_guarded > 0  # the guard's replan branch ran
