@@ -136,11 +136,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // slot free) holds it, and the destination of a move is the open rank with
 // the smallest x whatever expert the busiest rank gives. A step is then two
 // independent wave reductions over x (largest; smallest among open ranks)
-// plus reads of the busiest rank's heaviest expert, which each rank lane
+// plus a read of the busiest rank's heaviest expert, which each rank lane
 // keeps up to date in registers.
 //
 // EHM >= Eh: registers per lane for the home quotas of its rank; kLanes =
-// 32 when P <= 32 (shorter reductions), else 64.
+// 32 when P <= 32 (shorter reductions), else 64; kOneSlot: R == 1.
 //
 // Packed keys make every choice one max or min: a rank lane enters the
 // busiest-rank reduction with x*64 + (63 - lane) and, when open, the
@@ -148,17 +148,47 @@ __device__ __forceinline__ void wave_lds_sync() {
 // q*32 + (31 - j), so the extreme key also names the lowest rank or expert
 // index among equal values. The keys are exact while |x| and q stay below
 // 2^25, which N*K < 2^25 guarantees (loads, targets and quotas are at most
-// N*K); larger plans take greedy_lds. A move changes two lanes (the donor's
-// load and one quota key, the destination's load and slot count); every
-// lane applies it through selects (the donor's quota key, with more than 8
-// per lane, addressed by the uniform expert index). Each move is recorded
-// in the registers of lane (move mod 64) and written to LDS 64 moves at a
-// time.
+// N*K); larger plans take greedy_lds.
+//
+// A single wave issues about one instruction per SIMD turn, so the move is
+// written for few instructions. Both reduction results are keys, which give
+// the two lanes' x back (x*64 = key with the low six bits cleared): the move
+// writes the donor's and the destination's new x, slot count and quota key
+// into those lanes alone (v_writelane), and is recorded the same way in
+// lane (move mod 64). With at most 8 home experts a lane keeps its keys in
+// descending order, so its heaviest is the first register and the donor's
+// lowered key sinks back into place in one compare-exchange pass (lanes
+// other than the donor are already in order); with more, the heaviest is a
+// max over the registers and the lowered key is written at the uniform
+// expert index.
 constexpr long long kPackedPairsLimit = 1LL << 25;
 
-template <int EHM, int kLanes>
-__device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
+// Descending order of n registers: k[from] sinks past its smaller
+// neighbours (compare-exchange; indices fixed at compile time, so the array
+// stays in registers).
+template <int n, int from>
+__device__ __forceinline__ void sink_pass(int (&k)[n]) {
+  if constexpr (from + 1 < n) {
+    const int hi = max(k[from], k[from + 1]), lo = min(k[from], k[from + 1]);
+    k[from] = hi;
+    k[from + 1] = lo;
+    sink_pass<n, from + 1>(k);
+  }
+}
+
+// Insertion sort, descending: elements i, i-1, ..., 0 sink in turn.
+template <int n, int i>
+__device__ __forceinline__ void sort_desc(int (&k)[n]) {
+  if constexpr (i >= 0) {
+    sink_pass<n, i>(k);
+    sort_desc<n, i - 1>(k);
+  }
+}
+
+template <int EHM, int kLanes, bool kOneSlot>
+__device__ __forceinline__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
   static_assert(EHM <= 32, "five index bits per quota key");
+  constexpr bool kSorted = EHM <= 8;
   const int lane = threadIdx.x;
   const int P = a.P, R = a.R, Eh = a.Eh;
   const bool rank_lane = lane < P;
@@ -172,72 +202,86 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     load += q;
     kq[j] = real ? q * 32 + (31 - j) : -1;
   }
+  if constexpr (kSorted) sort_desc<EHM, EHM - 2>(kq);
   const int lpre = load;
-  // The lane keeps x*64 itself: both reduction keys are then one add away,
-  // and a move adds or subtracts mv*64. A lane without a rank sits far
-  // below every key (never the busiest) with no free slot (never open).
+  // The lane keeps x*64 itself, so both reduction keys are one add away.
+  // A lane without a rank sits far below every key (never the busiest)
+  // with no free slot (never open).
   int kx = rank_lane ? (load - tau) * 64 : -(1 << 30);
+  const int c63 = 63 - lane;
+  // Free slots: with one slot per rank a mask that the open key passes
+  // through (all ones while the slot is free), else the slot count.
+  int om = rank_lane ? -1 : 0x7fffffff;
   int used = rank_lane ? 0 : R;
-  int moves = 0, unbalanced = 0;
-  int rec_e = 0, rec_m = 0, rec_i = 0;  // the move recorded in this lane
-
-  for (;;) {
-    // Heaviest remaining home expert of each rank (max3 chain).
+  auto open_key = [&]() -> int {
+    const int kn = kx + lane;  // x*64 + lane: negative exactly when x < 0
+    if constexpr (kOneSlot) return (int)max((unsigned)(kn & om), 0x7fffffffu);
+    return used < R && kn < 0 ? kn : INT32_MAX;
+  };
+  auto heaviest = [&]() -> int {
+    if constexpr (kSorted) return kq[0];
     int bk = kq[0];
 #pragma unroll
     for (int j = 1; j + 1 < EHM; j += 2) bk = max(bk, max(kq[j], kq[j + 1]));
-    bk = max(bk, kq[EHM - 1]);
-
-    const int kn = kx + lane;  // x*64 + lane: negative exactly when x < 0
-    int kmax, kmin;
-    wave_max_min_i32<kLanes>(kx + (63 - lane), used < R && kn < 0 ? kn : INT32_MAX, kmax, kmin);
-    __asm__ volatile("" : "+v"(bk));  // keep the tournament beside the reductions
-    if (kmax < 64) break;             // largest x <= 0: every rank at or below target
-    if (kmin == INT32_MAX) {          // no open rank
-      unbalanced = 1;
-      break;
-    }
+    return max(bk, kq[EHM - 1]);
+  };
+  int moves = 0;
+  int rec_e = 0, rec_m = 0, rec_i = 0;  // the moves recorded in this lane
+  int kmax, kmin;
+  wave_max_min_i32<kLanes>(kx + c63, open_key(), kmax, kmin);
+  int bk = heaviest();
+  // Go on while the largest x is positive (kmax >= 64) and a rank is open
+  // (kmin < 0; INT32_MAX when none is).
+  while (((63 - kmax) & kmin) < 0) {
     const int rs = 63 - (kmax & 63);
     const int d = kmin & 63;
     const int kd = __builtin_amdgcn_readlane(bk, rs);
-    const int slot = __builtin_amdgcn_readlane(used, d);  // slots fill in index order
+    const int slot = kOneSlot ? 0 : __builtin_amdgcn_readlane(used, d);  // slots fill in order
     const int mv = min(-(kmin >> 6), kd >> 5);
     const int jb = 31 - (kd & 31);
     const int mi = moves & 63;
-    if (lane == mi) {
-      rec_e = rs * Eh + jb;
-      rec_m = mv;
-      rec_i = d * R + slot;
-    }
-    // Every lane applies the move; it changes only the lanes d and rs.
-    const bool at_d = lane == d, at_rs = lane == rs;
-    kx += (at_d ? mv * 64 : 0) - (at_rs ? mv * 64 : 0);
-    used += at_d ? 1 : 0;
-    if constexpr (EHM <= 8) {
-      if (at_rs) {
-#pragma unroll
-        for (int j = 0; j < EHM; ++j) kq[j] -= j == jb ? mv * 32 : 0;
-      }
+    rec_e = writelane_i32(rs * Eh + jb, mi, rec_e);
+    rec_m = writelane_i32(mv, mi, rec_m);
+    rec_i = writelane_i32(d * R + slot, mi, rec_i);
+    kx = writelane_i32((kmin & ~63) + mv * 64, d, kx);
+    kx = writelane_i32((kmax & ~63) - mv * 64, rs, kx);
+    if constexpr (kOneSlot)
+      om = writelane_i32(0x7fffffff, d, om);
+    else
+      used = writelane_i32(slot + 1, d, used);
+    if constexpr (kSorted) {
+      kq[0] = writelane_i32(kd - mv * 32, rs, kq[0]);
+      sink_pass<EHM, 0>(kq);
     } else {
-      kq[jb] -= at_rs ? mv * 32 : 0;  // uniform index: relative register addressing
+      kq[jb] = writelane_i32(kd - mv * 32, rs, kq[jb]);  // uniform index: relative addressing
     }
     ++moves;
-    if ((moves & 63) == 0) {
+    if (!kOneSlot && (moves & 63) == 0) {
       m.repE[rec_i] = rec_e;
       m.repM[rec_i] = rec_m;
       m.order[moves - 64 + lane] = rec_i;
     }
+    wave_max_min_i32<kLanes>(kx + c63, open_key(), kmax, kmin);
+    bk = heaviest();
   }
+  const int unbalanced = kmax >= 64;  // a rank above target and none open
   load = rank_lane ? (kx >> 6) + tau : 0;
-  if (lane < (moves & 63)) {
+  // one slot per rank: at most P <= 64 moves, all still in registers
+  const int done = kOneSlot ? 0 : moves & ~63;
+  if (lane < moves - done) {
     m.repE[rec_i] = rec_e;
     m.repM[rec_i] = rec_m;
-    m.order[(moves & ~63) + lane] = rec_i;
+    m.order[done + lane] = rec_i;
   }
   if (rank_lane) {
 #pragma unroll
-    for (int j = 0; j < EHM; ++j)
-      if (j < Eh) m.qh[lane * Eh + j] = kq[j] >> 5;
+    for (int j = 0; j < EHM; ++j) {
+      if constexpr (kSorted) {
+        if (kq[j] >= 0) m.qh[lane * Eh + (31 - (kq[j] & 31))] = kq[j] >> 5;
+      } else {
+        if (j < Eh) m.qh[lane * Eh + j] = kq[j] >> 5;
+      }
+    }
     m.loadv[lane] = load;
     m.lpre[lane] = lpre;
   }
@@ -247,22 +291,32 @@ __device__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
   }
 }
 
-template <int kLanes>
-__device__ void greedy_regs_for(const PlanArgs& a, PlanSmem& m) {
+template <int kLanes, bool kOneSlot>
+__device__ __forceinline__ void greedy_regs_for(const PlanArgs& a, PlanSmem& m) {
   if (a.Eh <= 4)
-    greedy_regs<4, kLanes>(a, m);
+    greedy_regs<4, kLanes, kOneSlot>(a, m);
   else if (a.Eh <= 8)
-    greedy_regs<8, kLanes>(a, m);
+    greedy_regs<8, kLanes, kOneSlot>(a, m);
   else if (a.Eh <= 16)
-    greedy_regs<16, kLanes>(a, m);
+    greedy_regs<16, kLanes, kOneSlot>(a, m);
+  else if (a.Eh <= 24)
+    greedy_regs<24, kLanes, kOneSlot>(a, m);
   else
-    greedy_regs<32, kLanes>(a, m);
+    greedy_regs<32, kLanes, kOneSlot>(a, m);
+}
+
+template <int kLanes>
+__device__ __forceinline__ void greedy_regs_lanes(const PlanArgs& a, PlanSmem& m) {
+  if (a.R == 1)
+    greedy_regs_for<kLanes, true>(a, m);
+  else
+    greedy_regs_for<kLanes, false>(a, m);
 }
 
 // The same greedy for ranks with more home experts than fit in registers:
 // home quotas stay in LDS and the heaviest expert of the busiest rank is a
 // wave reduction per step.
-__device__ void greedy_lds(const PlanArgs& a, PlanSmem& m) {
+__device__ __forceinline__ void greedy_lds(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
   const int P = a.P, R = a.R, Eh = a.Eh;
   const bool rank_lane = lane < P;
@@ -341,7 +395,7 @@ __device__ inline DriftView drift_view(const PlanArgs& a) {
 
 // d = 1 - c.r / (|c| |r|) from exact integer sums (ViBE summary, Drift-Aware
 // Recalibration); the window's sum r has the direction of its mean.
-__device__ double cosine_distance(u128 dot, u128 n1, u128 n2) {
+__device__ __forceinline__ double cosine_distance(u128 dot, u128 n1, u128 n2) {
 #pragma clang fp contract(off)
   if (n1 == 0 || n2 == 0) return n1 == n2 ? 0.0 : 1.0;
   return 1.0 - (double)dot / (__builtin_sqrt((double)n1) * __builtin_sqrt((double)n2));
@@ -350,7 +404,7 @@ __device__ double cosine_distance(u128 dot, u128 n1, u128 n2) {
 // Wave 0: whether this call runs the greedy. The first call does; after
 // that a check every check_every calls compares the counts with the
 // reference and replans when d exceeds delta_num / delta_den.
-__device__ void drift_decide(const PlanArgs& a, PlanSmem& m) {
+__device__ __forceinline__ void drift_decide(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
   const DriftView v = drift_view(a);
   const int have = v.hdr->have_plan;
@@ -403,7 +457,7 @@ __device__ void drift_decide(const PlanArgs& a, PlanSmem& m) {
 // one move per lane, each lane also holding its move's expert's remaining
 // home quota, then stepped through in order (a move lowers the quota on
 // every lane of the same expert).
-__device__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
+__device__ __forceinline__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
   const int P = a.P, R = a.R, Eh = a.Eh;
   const DriftView v = drift_view(a);
@@ -483,7 +537,7 @@ __device__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
 // (exact in 64-bit integers). Otherwise the placement state is reset for
 // the greedy, which then runs in this call as on a replan. Returns whether
 // it must run.
-__device__ bool guard_rejects(const PlanArgs& a, PlanSmem& m) {
+__device__ __forceinline__ bool guard_rejects(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
   bool over = false;
   if (lane < a.P) {
@@ -521,7 +575,7 @@ __device__ bool guard_rejects(const PlanArgs& a, PlanSmem& m) {
 // holds in common, and its two quota cells; the entries of a pair read each
 // other's x from LDS for the pair's totals and running sums. Different
 // entries have different cells, so the entries of a round act at once.
-__device__ void quota_repair(const PlanArgs& a, PlanSmem& m) {
+__device__ __forceinline__ void quota_repair(const PlanArgs& a, PlanSmem& m) {
   const int lane = threadIdx.x;
   const int P = a.P, R = a.R, Eh = a.Eh, E = a.E, PR = P * R;
   // Per slot: home of its expert, own demands of its holder and of that
@@ -733,7 +787,7 @@ __device__ void quota_repair(const PlanArgs& a, PlanSmem& m) {
 }
 
 // All threads, after the placement: the state for the layer's next call.
-__device__ void drift_update(const PlanArgs& a, PlanSmem& m) {
+__device__ __forceinline__ void drift_update(const PlanArgs& a, PlanSmem& m) {
   const int tid = threadIdx.x;
   const DriftView v = drift_view(a);
   const int replan = m.misc[4], moves = m.misc[0], nwin = m.misc[7];
@@ -853,9 +907,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       if ((long long)a.N * a.K >= kPackedPairsLimit || Eh > 32)
         greedy_lds(a, m);
       else if (P <= 32)
-        greedy_regs_for<32>(a, m);
+        greedy_regs_lanes<32>(a, m);
       else
-        greedy_regs_for<64>(a, m);
+        greedy_regs_lanes<64>(a, m);
     }
     if (a.repair && R > 0) quota_repair(a, m);
   }

@@ -14,6 +14,11 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
+// v_writelane_b32: `old` with lane `lane` replaced by `value` (lane and value
+// wave-uniform). This clang has no builtin for it, so the declaration names
+// the LLVM intrinsic.
+__device__ int writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
 // OR over the workgroup of per-thread status bits (the low 8 bits): one
 // ballot per bit in each wave, a word per wave in `wfl`, and one barrier,
 // which also orders the workgroup's earlier LDS writes as __syncthreads()
