@@ -308,6 +308,35 @@ def test_plan_around_the_packed_key_limit(N, K, E, P, R, kind):
     assert ref.status[0] == 0 and ref.status[3] > 0
 
 
+@pytest.mark.parametrize("P,eh,R", [
+    # home experts per rank: 4 | 8 | 16 | 24 | 32 quota registers per lane (the first two kept in
+    # order); 32-lane (P <= 32) and 64-lane reductions; one slot per rank and several
+    (16, 4, 1), (16, 4, 2), (64, 4, 1), (64, 4, 3),
+    (32, 8, 1), (32, 8, 2), (40, 6, 1), (40, 6, 2),
+    (20, 12, 1), (20, 12, 3), (48, 16, 1), (48, 16, 2),
+    (16, 24, 1), (16, 24, 2), (40, 20, 1), (40, 20, 4),
+    (32, 32, 1), (32, 32, 2), (33, 31, 1), (33, 31, 3),
+])
+def test_register_greedy_variants(P, eh, R):
+    """Every register-greedy variant, bit-exact: once with equal speeds and
+    once with rank speeds alternating 8 and 1, whose fast ranks fill all
+    their slots (more than 64 moves when the P/2 fast ranks hold more than 64
+    slots, so the move records leave registers mid-loop)."""
+    E, S, K = P * eh, 96, 8
+    N = P * S
+    dg = mb.Dims.make(N, K, E, P, R, 16, cap=4 * S * K, dtype_in="f32", dtype_out="f32")
+    od = O.make_dims(N, K, E, P, R, 16, cap=4 * S * K, dtype_in="f32", dtype_out="f32")
+    for speeds in (None, [8 if r % 2 == 0 else 1 for r in range(P)]):
+        G.log(f"case greedy variant P={P} Eh={eh} R={R} speeds={'8/1' if speeds else None}")
+        ids, _ = W.routing(N, E, K, W.NOISE_GUMBEL, 1.0, 0.3, 61000 + P * 100 + eh)
+        got = G.GpuPlan(dg).run(ids, speeds=speeds).fetch()
+        ref = O.plan(od, ids, speeds=speeds)
+        G.assert_plan_equal(got, ref)
+        assert ref.status[3] > 0
+        if speeds and (P // 2) * R > 64:
+            assert ref.status[3] > 64, "the mid-loop record flush did not run"
+
+
 @pytest.mark.parametrize("din,H,K", [
     ("bf16", 1024, 2), ("bf16", 1024, 3), ("bf16", 2048, 16), ("f32", 512, 8), ("fp8", 2048, 4),
     ("fp8", 4096, 8),                       # rows of whole 2 KiB spans: k_dispatch_span
