@@ -507,9 +507,12 @@ __device__ __forceinline__ void replay_kept(const PlanArgs& a, PlanSmem& m) {
       // no move unless the home is above target and the host below (q is
       // 0 in lanes without a move)
       const int mv = min(min(max(-xd, 0), qe), xh > 0 ? INT32_MAX : 0);
-      mine = lane == j ? mv : mine;
+      mine = writelane_i32(mv, j, mine);
       q -= (ok && e == se) ? mv : 0;
-      x += (lane == sd ? mv : 0) - (lane == sh ? mv : 0);
+      // the two changed lanes written alone (a host is never its expert's
+      // home; were it, the second write restores the lane)
+      x = writelane_i32(xh - mv, sh, x);
+      x = writelane_i32((sd & 63) == sh ? xd : xd + mv, sd & 63, x);
     }
     if (ok) {
       m.repM[slot] = mine;
