@@ -154,8 +154,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // written for few instructions. Both reduction results are keys, which give
 // the two lanes' x back (x*64 = key with the low six bits cleared): the move
 // writes the donor's and the destination's new x, slot count and quota key
-// into those lanes alone (v_writelane), and is recorded the same way in
-// lane (move mod 64). With at most 8 home experts a lane keeps its keys in
+// into those lanes alone (v_writelane), and is recorded the same way: in
+// the destination's lane with one slot per rank, else in lane (move mod 64). With at most 8 home experts a lane keeps its keys in
 // descending order, so its heaviest is the first register and the donor's
 // lowered key sinks back into place in one compare-exchange pass (lanes
 // other than the donor are already in order); with more, the heaviest is a
@@ -226,7 +226,7 @@ __device__ __forceinline__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     return max(bk, kq[EHM - 1]);
   };
   int moves = 0;
-  int rec_e = 0, rec_m = 0, rec_i = 0;  // the moves recorded in this lane
+  int rec_e = 0, rec_m = 0, rec_i = kOneSlot ? -1 : 0;  // the moves recorded in this lane
   int kmax, kmin;
   wave_max_min_i32<kLanes>(kx + c63, open_key(), kmax, kmin);
   int bk = heaviest();
@@ -239,10 +239,18 @@ __device__ __forceinline__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
     const int slot = kOneSlot ? 0 : __builtin_amdgcn_readlane(used, d);  // slots fill in order
     const int mv = min(-(kmin >> 6), kd >> 5);
     const int jb = 31 - (kd & 31);
-    const int mi = moves & 63;
-    rec_e = writelane_i32(rs * Eh + jb, mi, rec_e);
-    rec_m = writelane_i32(mv, mi, rec_m);
-    rec_i = writelane_i32(d * R + slot, mi, rec_i);
+    if constexpr (kOneSlot) {
+      // one replica per rank: the record sits in the destination's lane,
+      // rec_i holding the move's place in the placement order
+      rec_e = writelane_i32(rs * Eh + jb, d, rec_e);
+      rec_m = writelane_i32(mv, d, rec_m);
+      rec_i = writelane_i32(moves, d, rec_i);
+    } else {
+      const int mi = moves & 63;
+      rec_e = writelane_i32(rs * Eh + jb, mi, rec_e);
+      rec_m = writelane_i32(mv, mi, rec_m);
+      rec_i = writelane_i32(d * R + slot, mi, rec_i);
+    }
     kx = writelane_i32((kmin & ~63) + mv * 64, d, kx);
     kx = writelane_i32((kmax & ~63) - mv * 64, rs, kx);
     if constexpr (kOneSlot)
@@ -266,12 +274,19 @@ __device__ __forceinline__ void greedy_regs(const PlanArgs& a, PlanSmem& m) {
   }
   const int unbalanced = kmax >= 64;  // a rank above target and none open
   load = rank_lane ? (kx >> 6) + tau : 0;
-  // one slot per rank: at most P <= 64 moves, all still in registers
-  const int done = kOneSlot ? 0 : moves & ~63;
-  if (lane < moves - done) {
-    m.repE[rec_i] = rec_e;
-    m.repM[rec_i] = rec_m;
-    m.order[done + lane] = rec_i;
+  if constexpr (kOneSlot) {
+    if (rec_i >= 0) {  // this rank received move rec_i into its one slot
+      m.repE[lane] = rec_e;
+      m.repM[lane] = rec_m;
+      m.order[rec_i] = lane;
+    }
+  } else {
+    const int done = moves & ~63;
+    if (lane < moves - done) {
+      m.repE[rec_i] = rec_e;
+      m.repM[rec_i] = rec_m;
+      m.order[done + lane] = rec_i;
+    }
   }
   if (rank_lane) {
 #pragma unroll
