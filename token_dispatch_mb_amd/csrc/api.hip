@@ -142,21 +142,28 @@ static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t*
   // tables -> per-pair rows, all on `stream`, no host synchronisation.
   // With one routing block per source rank, the block counts are d[s][e]
   // and every block offset is 0: k_count writes d itself, the scan is
-  // skipped and k_plan sums c_e.
+  // skipped and k_plan sums c_e. With a few blocks per source and a small
+  // table of block counts, the scan is skipped too: k_plan sums the table
+  // into d[s][e] and c_e, and each k_assign block sums its source's earlier
+  // blocks.
   const bool one_block = g.nbps == 1;
+  const bool small = small_block_table(*dims, g);
+  const bool scan = !one_block && !small;
   if (launch_count(*dims, g, ids_dev, one_block ? out->counts : blockcnt, blockflags, brank,
                    stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (!one_block &&
+  if (scan &&
       launch_scan(*dims, g, blockcnt, blockoff, out->counts, expert_total, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_plan(*dims, g, *out, rank_speed, drift, drift_state, repair, blockflags,
-                  one_block ? nullptr : expert_total, stream) != hipSuccess)
+                  scan ? expert_total : nullptr, small ? blockcnt : nullptr,
+                  stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_assign(*dims, g, ids_dev, brank, one_block ? nullptr : blockoff, pair_tab, host_list,
-                    host_range, *out, stream) != hipSuccess)
+  if (launch_assign(*dims, g, ids_dev, brank, scan ? blockoff : nullptr,
+                    small ? blockcnt : nullptr, pair_tab, host_list, host_range, *out,
+                    stream) != hipSuccess)
     return MB_ERR_HIP;
   return MB_OK;
 }

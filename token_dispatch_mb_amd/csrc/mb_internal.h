@@ -18,6 +18,10 @@ constexpr int kMaxRanks = 64;     // one wave lane per logical rank in k_plan
 constexpr int kMaxExperts = 1024; // LDS: kWaves * E * 8 bytes of token masks
 constexpr int kMaxTopK = 32;
 constexpr int kMaxSlots = 16;
+// Block-count tables k_plan and k_assign sum directly instead of running
+// k_scan: at most this many routing blocks per source and block counts.
+constexpr int kSmallTableBlocks = 4;
+constexpr int kSmallTableCounts = 4096;
 
 // One entry per (source rank s, expert e), written by k_tables, read by
 // k_assign for every pair (s, e):
@@ -75,10 +79,20 @@ hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* block
 // rank_speed: P host values (all 1 for the single water level);
 // drift/drift_state: drift-gated replanning, or both nullptr; repair: the
 // quota repair after placement.
+// c_e comes from expert_total (k_scan ran), else from the block counts
+// `blockcnt` (a small table: k_plan also writes d[s][e]), else from d[s][e]
+// itself (one routing block per source).
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
                        void* drift_state, int repair, const int32_t* blockflags,
-                       const int32_t* expert_total, hipStream_t st);
+                       const int32_t* expert_total, const int32_t* blockcnt, hipStream_t st);
+
+// Whether the block counts are few enough for k_plan and k_assign to sum
+// them directly, so that k_scan is skipped.
+inline bool small_block_table(const mb_dims& d, const Geometry& g) {
+  return g.nbps > 1 && g.nbps <= kSmallTableBlocks &&
+         (long long)g.nblk * d.n_experts <= kSmallTableCounts;
+}
 
 // Bytes of a drift state buffer: header, int64 reference [E], kept replicas
 // and their placement order [P*R] each.
@@ -86,10 +100,12 @@ size_t drift_state_bytes(const mb_dims& d);
 hipError_t launch_tables(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                          PairEntry* pair_tab, HostEntry* host_list, int2* host_range,
                          hipStream_t st);
+// A block's offsets come from blockoff (k_scan ran), else from summing the
+// earlier blocks of its source in blockcnt (small table), else are 0.
 hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids,
-                         const uint8_t* brank, const int32_t* blockoff, const PairEntry* pair_tab,
-                         const HostEntry* host_list, const int2* host_range,
-                         const mb_plan_bufs& o, hipStream_t st);
+                         const uint8_t* brank, const int32_t* blockoff, const int32_t* blockcnt,
+                         const PairEntry* pair_tab, const HostEntry* host_list,
+                         const int2* host_range, const mb_plan_bufs& o, hipStream_t st);
 hipError_t launch_dispatch(const mb_dims& d, const mb_plan_bufs& o, const void* x,
                            const float* x_scale, void* buf, float* buf_scale, hipStream_t st);
 hipError_t launch_combine(const mb_dims& d, const mb_plan_bufs& o, const void* y_exp,

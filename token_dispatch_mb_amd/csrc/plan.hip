@@ -1,7 +1,8 @@
 // plan.hip — the single-workgroup replica planner of libmoebal.
 //
 // One workgroup of 256 threads (the per-rank targets come from the host):
-//  1. routed pairs per expert c_e (summed over sources by k_scan, or here);
+//  1. routed pairs per expert c_e (summed over sources by k_scan, or here
+//     from d[s][e] or from a small table of block counts);
 //  2. wave 0 runs the greedy with lane r = logical rank r (P <= 64): the
 //     rank farthest above its target tau_r gives a replica of its heaviest
 //     home expert to the rank farthest below its own target that has a free
@@ -44,6 +45,8 @@ struct PlanArgs {
   const int32_t* counts;      // [P][E] pairs per (source rank, expert), from k_scan
   int32_t* counts_out;        // the same buffer, cleared when the routing is invalid
   const int32_t* expert_total;
+  const int32_t* blockcnt;    // small table of block counts [nblk][E] (k_scan skipped)
+  int nbps;                   // routing blocks per source rank
   const int32_t* blockflags;
   int32_t* load_pre;
   int32_t* load_post;
@@ -840,8 +843,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
   PlanSmem m = carve(smem, E, P, R, NS);
 
   // The targets, the status bits of the routing decisions and c_e (summed
-  // over sources by k_scan, or here from d[s][e] when k_scan did not run)
-  // are loaded before any of them is used, so their latencies overlap.
+  // over sources by k_scan, or here when k_scan did not run: from d[s][e],
+  // or from the block counts) are loaded before any of them is used, so
+  // their latencies overlap.
   static_assert(kMaxExperts <= 4 * kPlanThreads, "c_e takes one batch of loads");
   const int tau_v = a.tau[tid & (kMaxRanks - 1)];
   int f[4], cv[4];
@@ -865,6 +869,22 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       const int e = u * kPlanThreads + tid;
       if (e < E) m.c[e] = m.qh[e] = cv[u];
     }
+  } else if (a.blockcnt) {
+    // A small table of block counts: d[s][e] is the sum of the source's
+    // blocks (a plan output, here in place of k_scan's), c_e their sum over
+    // sources, accumulated in LDS.
+    for (int e = tid; e < E; e += kPlanThreads) m.c[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < P * E; i += kPlanThreads) {
+      const int s = i / E, e = i - s * E;
+      const int32_t* col = a.blockcnt + (size_t)s * a.nbps * E + e;
+      int d = 0;
+      for (int j = 0; j < a.nbps; ++j) d += col[(size_t)j * E];
+      a.counts_out[i] = d;
+      atomicAdd(&m.c[e], d);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kPlanThreads) m.qh[e] = m.c[e];
   } else {
     // Every source's count of the thread's expert in flight at once; the
     // address advances in a vector register (kept there by the empty asm),
@@ -993,7 +1013,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
                        void* drift_state, int repair, const int32_t* blockflags,
-                       const int32_t* expert_total, hipStream_t st) {
+                       const int32_t* expert_total, const int32_t* blockcnt, hipStream_t st) {
   PlanArgs a;
   a.N = d.n_tokens;
   a.K = d.top_k;
@@ -1025,6 +1045,8 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.counts = o.counts;
   a.counts_out = o.counts;
   a.expert_total = expert_total;
+  a.blockcnt = blockcnt;
+  a.nbps = g.nbps;
   a.blockflags = blockflags;
   a.load_pre = o.load_pre;
   a.load_post = o.load_post;

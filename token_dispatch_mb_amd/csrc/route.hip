@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
     const PairEntry* __restrict__ pair_tab, const HostEntry* __restrict__ host_list,
     const int2* __restrict__ host_range, const int32_t* __restrict__ status,
     const int32_t* __restrict__ load_post, int32_t* __restrict__ pos,
-    int32_t* __restrict__ row_src) {
+    int32_t* __restrict__ row_src, const int32_t* __restrict__ blockcnt) {
   // LDS: offsets [E4] | pairs [E] | ranges [E4] | hosts [nhost]
   extern __shared__ int4 lds[];
   __shared__ int32_t lp_s[kMaxRanks];
@@ -216,7 +216,15 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   }
   if (has_tokens) {
     for (int i = tl; i < E; i += kTokensPerBlock) {
-      boff[i] = blockoff ? blockoff[(size_t)b * E + i] : 0;  // null: one block per source
+      // from k_scan; else the sum of the source's earlier blocks (j of
+      // them, a small table); with one block per source, 0
+      int o = 0;
+      if (blockoff) {
+        o = blockoff[(size_t)b * E + i];
+      } else if (blockcnt) {
+        for (int jj = 0; jj < j; ++jj) o += blockcnt[(size_t)(b - j + jj) * E + i];
+      }
+      boff[i] = o;
       ptab[i] = pair_tab[(size_t)s * E + i];
       hrange[i] = host_range[i];
     }
@@ -409,9 +417,9 @@ hipError_t launch_tables(const mb_dims& d, const Geometry& g, const mb_plan_bufs
 }
 
 hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids,
-                         const uint8_t* brank, const int32_t* blockoff, const PairEntry* pair_tab,
-                         const HostEntry* host_list, const int2* host_range,
-                         const mb_plan_bufs& o, hipStream_t st) {
+                         const uint8_t* brank, const int32_t* blockoff, const int32_t* blockcnt,
+                         const PairEntry* pair_tab, const HostEntry* host_list,
+                         const int2* host_range, const mb_plan_bufs& o, hipStream_t st) {
   const int64_t rows = (int64_t)d.n_ranks * d.cap;
   int grid = g.nblk;
   const int64_t pad_blocks = (rows + kTokensPerBlock - 1) / kTokensPerBlock;
@@ -430,12 +438,12 @@ hipError_t launch_assign(const mb_dims& d, const Geometry& g, const int32_t* ids
       hipLaunchKernelGGL((k_assign<KT, true>), dim3(grid), dim3(kTokensPerBlock), shmem, st, \
                          ids, brank, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps, g.nblk,   \
                          d.cap, nhost, blockoff, pair_tab, host_list, host_range, o.status,  \
-                         o.load_post, o.pos, o.row_src);                                     \
+                         o.load_post, o.pos, o.row_src, blockcnt);                           \
     else                                                                                     \
       hipLaunchKernelGGL((k_assign<KT, false>), dim3(grid), dim3(kTokensPerBlock), shmem,    \
                          st, ids, brank, d.top_k, d.n_experts, g.S, d.n_ranks, g.nbps,       \
                          g.nblk, d.cap, nhost, blockoff, pair_tab, host_list, host_range,    \
-                         o.status, o.load_post, o.pos, o.row_src);                           \
+                         o.status, o.load_post, o.pos, o.row_src, blockcnt);                 \
   } while (0)
   switch (d.top_k) {
     case 1: MB_A(1); break;
