@@ -149,6 +149,7 @@ static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t*
   const bool one_block = g.nbps == 1;
   const bool small = small_block_table(*dims, g);
   const bool scan = !one_block && !small;
+  const bool tables_in_plan = dims->n_experts <= kPlanTableExperts;
   if (launch_count(*dims, g, ids_dev, one_block ? out->counts : blockcnt, blockflags, brank,
                    stream) != hipSuccess)
     return MB_ERR_HIP;
@@ -157,9 +158,11 @@ static int plan_impl(const mb_dims* dims, const int32_t* ids_dev, const int32_t*
     return MB_ERR_HIP;
   if (launch_plan(*dims, g, *out, rank_speed, drift, drift_state, repair, blockflags,
                   scan ? expert_total : nullptr, small ? blockcnt : nullptr,
-                  stream) != hipSuccess)
+                  tables_in_plan ? pair_tab : nullptr, tables_in_plan ? host_list : nullptr,
+                  tables_in_plan ? host_range : nullptr, stream) != hipSuccess)
     return MB_ERR_HIP;
-  if (launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
+  if (!tables_in_plan &&
+      launch_tables(*dims, g, *out, pair_tab, host_list, host_range, stream) != hipSuccess)
     return MB_ERR_HIP;
   if (launch_assign(*dims, g, ids_dev, brank, scan ? blockoff : nullptr,
                     small ? blockcnt : nullptr, pair_tab, host_list, host_range, *out,

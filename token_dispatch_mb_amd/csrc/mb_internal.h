@@ -22,6 +22,9 @@ constexpr int kMaxSlots = 16;
 // k_scan: at most this many routing blocks per source and block counts.
 constexpr int kSmallTableBlocks = 4;
 constexpr int kSmallTableCounts = 4096;
+// Experts few enough for k_plan's four waves to build k_assign's lookup
+// tables (one wave per expert, at most four in turn) instead of k_tables.
+constexpr int kPlanTableExperts = 16;
 
 // One entry per (source rank s, expert e), written by k_tables, read by
 // k_assign for every pair (s, e):
@@ -81,11 +84,14 @@ hipError_t launch_scan(const mb_dims& d, const Geometry& g, const int32_t* block
 // quota repair after placement.
 // c_e comes from expert_total (k_scan ran), else from the block counts
 // `blockcnt` (a small table: k_plan also writes d[s][e]), else from d[s][e]
-// itself (one routing block per source).
+// itself (one routing block per source). With pair_tab, host_list and
+// host_range non-null k_plan also builds k_assign's lookup tables (few
+// experts; k_tables is then not launched).
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
                        void* drift_state, int repair, const int32_t* blockflags,
-                       const int32_t* expert_total, const int32_t* blockcnt, hipStream_t st);
+                       const int32_t* expert_total, const int32_t* blockcnt, PairEntry* pair_tab,
+                       HostEntry* host_list, int2* host_range, hipStream_t st);
 
 // Whether the block counts are few enough for k_plan and k_assign to sum
 // them directly, so that k_scan is skipped.

@@ -28,6 +28,7 @@
 // Informed Expert Placement (token target per GPU in proportion to its
 // speed, experts to the GPU farthest below its target).
 #include "mb_internal.h"
+#include "tables.h"
 #include "wave.h"
 
 namespace mb {
@@ -54,6 +55,10 @@ struct PlanArgs {
   int32_t* slot_quota;
   int32_t* cu_seqlens;
   int32_t* status;
+  // k_assign's lookup tables, built here when non-null (few experts)
+  PairEntry* pair_tab;
+  HostEntry* host_list;
+  int2* host_range;
 };
 
 constexpr int kPlanThreads = 256;
@@ -1006,6 +1011,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
       a.status[3] = m.misc[0];
     }
   }
+  if (a.pair_tab) {
+    // With few experts k_assign's lookup tables are built here, one wave
+    // per expert in turn, from the plan outputs this workgroup has just
+    // stored (nothing is needed under CAPACITY: k_assign then stores no row).
+    const int ln = tid & 63;
+    const int ml = wave_max_i32(ln < P ? m.loadv[ln] : 0);
+    __syncthreads();
+    if (ml <= a.cap)
+      for (int e = tid >> 6; e < E; e += kPlanThreads / 64)
+        tables_for_expert(e, E, P, R, Eh, NS, a.cap, a.counts, a.rep_expert, a.slot_quota,
+                          a.cu_seqlens, a.pair_tab, a.host_list, a.host_range);
+  }
 }
 
 }  // namespace
@@ -1013,7 +1030,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(PlanArgs a) {
 hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& o,
                        const int32_t* rank_speed, const mb_drift_params* drift,
                        void* drift_state, int repair, const int32_t* blockflags,
-                       const int32_t* expert_total, const int32_t* blockcnt, hipStream_t st) {
+                       const int32_t* expert_total, const int32_t* blockcnt, PairEntry* pair_tab,
+                       HostEntry* host_list, int2* host_range, hipStream_t st) {
   PlanArgs a;
   a.N = d.n_tokens;
   a.K = d.top_k;
@@ -1054,6 +1072,9 @@ hipError_t launch_plan(const mb_dims& d, const Geometry& g, const mb_plan_bufs& 
   a.slot_quota = o.slot_quota;
   a.cu_seqlens = o.cu_seqlens;
   a.status = o.status;
+  a.pair_tab = pair_tab;
+  a.host_list = host_list;
+  a.host_range = host_range;
   const size_t shmem = plan_smem_bytes(a.E, a.P, a.R, a.NS);
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), shmem, st, a);
   return hipGetLastError();

@@ -20,6 +20,7 @@
 // routing); MoonEP, "What MoonEP enforces and how" (fixed per-rank regions
 // indexed by cu_seqlens).
 #include "mb_internal.h"
+#include "tables.h"
 #include "wave.h"
 
 namespace mb {
@@ -329,10 +330,7 @@ __global__ __launch_bounds__(kTokensPerBlock) void k_assign(
   }
 }
 
-// Lookup tables of k_assign, one wave per expert e, lane = source rank s:
-//   pass 1 keeps min(d[s][e], quota of s) pairs on each holder s; the
-//   remaining (surplus) pairs, in token order, fill the holders' spare quota
-//   in ascending rank order. Prefix sums over s are wave scans.
+// Lookup tables of k_assign, one wave per expert (tables.h).
 __global__ __launch_bounds__(256) void k_tables(
     int E, int P, int R, int Eh, int NS, int cap, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ rep_expert, const int32_t* __restrict__ slot_quota,
@@ -342,48 +340,8 @@ __global__ __launch_bounds__(256) void k_tables(
   if (status[0] & MB_ST_FATAL) return;
   const int e = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (e >= E) return;
-  const int s = threadIdx.x & 63;
-  const bool valid = s < P;
-  const int home = e / Eh;
-  int d = 0, slot = -1, lq = 0, rowbase = 0, reps_below = 0;
-  if (valid) {
-    d = counts[(size_t)s * E + e];
-    for (int q = 0; q < R; ++q) {
-      const int re = rep_expert[s * R + q];
-      reps_below += (unsigned)re < (unsigned)e ? 1 : 0;
-      if (s != home && re == e) slot = Eh + q;
-    }
-    if (s == home) slot = e - s * Eh;
-    if (slot >= 0) {
-      lq = slot_quota[s * NS + slot];
-      rowbase = s * cap + cu_seqlens[s * (NS + 1) + slot];
-    }
-  }
-  const int lt = min(d, lq);
-  const int sur = d - lt, sp = lq - lt;
-  const int sur_before = wave_inclusive_sum(sur) - sur;
-  const int sp_before = wave_inclusive_sum(sp) - sp;
-  if (valid) {
-    PairEntry pe;
-    pe.local_quota = lq;
-    pe.local_base = slot >= 0 ? rowbase + min(max(sur_before - sp_before, 0), sp) : 0;
-    pe.surplus_shift = sur_before - lq;
-    pe.pad = 0;
-    pair_tab[(size_t)s * E + e] = pe;
-  }
-  // The host list in expert order, 1 + (replicas of e) entries for e: its
-  // entries start after those of the experts below it.
-  const int off = e + __builtin_amdgcn_readlane(wave_inclusive_sum(reps_below), 63);
-  const uint64_t hb = ballot64(valid && sp > 0);
-  if (valid && sp > 0) {
-    HostEntry h;
-    h.end = sp_before + sp;
-    h.base = rowbase - sp_before;
-    h.rank = s;
-    h.lt = lt;
-    host_list[off + lanes_below(hb)] = h;
-  }
-  if (s == 0) host_range[e] = make_int2(off, __popcll(hb));
+  tables_for_expert(e, E, P, R, Eh, NS, cap, counts, rep_expert, slot_quota, cu_seqlens,
+                    pair_tab, host_list, host_range);
 }
 
 }  // namespace
