@@ -163,12 +163,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // the two lanes' x back (x*64 = key with the low six bits cleared): the move
 // writes the donor's and the destination's new x, slot count and quota key
 // into those lanes alone (v_writelane), and is recorded the same way: in
-// the destination's lane with one slot per rank, else in lane (move mod 64). With at most 8 home experts a lane keeps its keys in
-// descending order, so its heaviest is the first register and the donor's
-// lowered key sinks back into place in one compare-exchange pass (lanes
-// other than the donor are already in order); with more, the heaviest is a
-// max over the registers and the lowered key is written at the uniform
-// expert index.
+// the destination's lane with one slot per rank, else in lane (move mod
+// 64). With at most 8 home experts a lane keeps its keys in descending
+// order, so its heaviest is the first register and the donor's lowered key
+// sinks back into place in one compare-exchange pass (lanes other than the
+// donor are already in order); with more, the heaviest is a max over the
+// registers and the lowered key is written at the uniform expert index.
 constexpr long long kPackedPairsLimit = 1LL << 25;
 
 // Descending order of n registers: k[from] sinks past its smaller
